@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-rank ZeRO stage-1/2 fused shard step on one MI355X.
+
+A step is one pass of the whole path over one rank's shard: fold the N resident
+gradient replicas in ring (slot) order, average and unscale, flag overflow and
+form the squared norm, Adam/AdamW on fp32 master / m / v, bf16 write into this
+rank's slot of the gathered parameter buffer, then the 16-byte stats read-back
+and the commit rule. The default workload is the GPT-2-small shard (rank 0 of
+N=8, 15,554,976 elements, bf16 replicas, AdamW); inputs are synthetic, seeded,
+and resident in HBM before the timed region starts.
+
+Prints one JSON line. ``roofline`` is for the dominant kernel (the fused step
+kernel): algorithmic bytes per launch, S * (N * 2 + 26), over its mean duration
+measured with HIP events recorded around that kernel on its own stream.
+``cpu_baseline`` is the CPU oracle timed on this host on the same shard.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "fused shard step: elements/s and achieved HBM GB/s (% of MI355X peak)"
+KERNEL_SRC = os.path.join(ROOT, "zero_partitioned_optimizer_amd", "csrc", "step_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the step kernel from the committed rocprofv3 counter
+    runs, or None if there are none for this workload or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_sha") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, host_reps, p0_host, S, seconds: float):
+    """The oracle, as it stands, on this host: repeated steps over the shard."""
+    import numpy as np
+
+    import oracle
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    p = p0_host.copy()
+    m = np.zeros(S, np.float32)
+    v = np.zeros(S, np.float32)
+    slot = np.zeros(S, np.uint16)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.step(host_reps, p, m, v, slot, loss_scale=w.loss_scale, t=n + 1, nthreads=nthreads,
+                    **w.hyper())
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n * S / el, "unit": "elements/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{w.name} rank-0 shard, S={S} elements, N={w.N} replicas, {n} oracle "
+                      f"steps in {el:.1f} s, OpenMP threads={nthreads}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="gpt2s",
+                    choices=["tiny", "gpt2s", "llama7b", "ragged", "llama70b"])
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--bucket-elems", type=int, default=0,
+                    help="launch over the layout's bucket table cut at this size (0: whole shard)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's share of the step; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported: run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import zero_partitioned_optimizer_amd as Z
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    w = W.get(args.config)
+    gdt = Z.ZERO_BF16 if w.grad_dtype == "bf16" else Z.ZERO_F32
+    h = Z.zero_layout_build(list(w.numels), w.N, w.A, w.B)
+    try:
+        S = Z.zero_layout_info_get(h).shard_S
+        covered = [(s[2], s[3]) for s in Z.zero_layout_segments(h, args.rank)]
+        buckets_t, nb = None, 0
+        if args.bucket_elems:
+            raw, nb = Z.zero_layout_buckets_raw(h, args.rank, args.bucket_elems)
+            buckets_t = torch.frombuffer(bytearray(bytes(raw)[: 16 * nb]), dtype=torch.uint8).to(dev)
+    finally:
+        Z.zero_layout_free(h)
+    log(f"workload {w.name}: S={S} N={w.N} grad={w.grad_dtype} buckets={nb}")
+
+    tdt = torch.int16 if w.grad_dtype == "bf16" else torch.float32
+    reps = []
+    for j in range(w.N):
+        buf = torch.empty(S, dtype=torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32,
+                          device=dev)
+        W.device_fill_replica(buf, w, covered, args.rank, 0, j)
+        reps.append(buf.view(tdt))
+    p0 = torch.empty(S, dtype=torch.float32, device=dev)
+    W.device_fill_params(p0, w, covered, args.rank)
+    step = Z.ShardStep(S, w.N, gdt, p0, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                       weight_decay=w.wd, loss_scale=w.loss_scale, dynamic=w.dynamic_loss_scale,
+                       buckets=buckets_t, n_buckets=nb)
+    torch.cuda.synchronize()
+    log("inputs resident; warmup", args.warmup)
+
+    for _ in range(args.warmup):
+        step.step(reps)
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    skipped = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        st, verdict = step.step(reps, events=ev[k])
+        skipped += verdict == Z.ZERO_SKIP
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kms = [a.elapsed_time(b) for a, b in ev]
+    log(f"timed {K} steps in {elapsed:.4f} s; kernel mean {statistics.mean(kms) * 1e3:.1f} us, "
+        f"median {statistics.median(kms) * 1e3:.1f} us, skipped {skipped}")
+
+    bpe = w.N * w.grad_bytes + 26
+    kernel_s = statistics.mean(kms) / 1e3
+    achieved = S * bpe / kernel_s / 1e9
+    traffic = measured_traffic(w.name)
+    out = {
+        "metric": METRIC,
+        "value": S * K / elapsed,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} shard, rank {args.rank} of N={w.N}", "shard_elems": S,
+                   "n_replicas": w.N, "grad_dtype": w.grad_dtype, "state_dtype": "f32",
+                   "bytes_per_elem": bpe, "bucket_elems": args.bucket_elems},
+        "step_gbps": S * bpe / (elapsed / K) / 1e9,
+        "kernel_us_mean": kernel_s * 1e6,
+        "kernel_us_median": statistics.median(kms) * 1e3,
+        "kernel_us_min": min(kms) * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "cpu_baseline": None,
+        "skipped_steps": skipped,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        host_reps = []
+        for r in reps:
+            x = r.cpu()
+            host_reps.append(x.numpy().view(np.uint16) if w.grad_dtype == "bf16" else x.numpy())
+        out["cpu_baseline"] = cpu_baseline(w, host_reps, p0.cpu().numpy(), S, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,218 @@
+"""Host-side tests of libzero (no GPU needed): the library loads and exports every
+function include/zero.h declares; its layout, segments, buckets and memory
+accounting equal the oracle's exactly; argument checks reject bad calls before
+touching the GPU; the host commit rule follows the skip rule."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def Z():
+    import zero_partitioned_optimizer_amd as Z
+    Z.lib()
+    return Z
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "zero.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(Z):
+    names = declared_functions()
+    assert len(names) >= 15
+    L = ctypes.CDLL(os.path.join(ROOT, "zero_partitioned_optimizer_amd", "libzero.so"))
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert Z.zero_version().startswith("libzero")
+
+
+def lib_layout(Z, numels, N, A, B):
+    h = Z.zero_layout_build(list(numels), N, A, B)
+    try:
+        info = Z.zero_layout_info_get(h)
+        offs = Z.zero_layout_offsets(h)
+        return h, info, offs
+    except Exception:
+        Z.zero_layout_free(h)
+        raise
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_layout_equals_oracle_random(Z, seed):
+    rng = np.random.default_rng(seed)
+    T = int(rng.integers(0, 40))
+    numels = [int(x) for x in rng.integers(0, 3000, size=T)]
+    N = int(rng.integers(1, 17))
+    A = int(rng.choice([1, 2, 8, 256]))
+    B = int(rng.choice([1, 8, 16]))
+    ref = oracle.Layout(numels, N=N, A=A, B=B)
+    h, info, offs = lib_layout(Z, numels, N, A, B)
+    try:
+        assert offs == ref.offsets.tolist()
+        assert (info.used_L, info.shard_S, info.padded_L) == (ref.L, ref.S, ref.L_pad)
+        assert info.psi == sum(numels) and info.world_N == N and info.n_tensors == T
+        for r in range(N):
+            assert [list(s) for s in Z.zero_layout_segments(h, r)] == ref.segments(r).tolist()
+            for be in (1, 7, 64, 1000):
+                assert [list(b) for b in Z.zero_layout_buckets(h, r, be)] == ref.buckets(r, be).tolist()
+        for stage in range(4):
+            assert Z.zero_layout_mem_values(h, stage) == ref.mem_values(stage).tolist()
+            assert Z.zero_layout_mem_bytes(h, stage) == ref.mem_bytes(stage).tolist()
+    finally:
+        Z.zero_layout_free(h)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2s", "llama7b", "ragged", "llama70b"])
+def test_layout_equals_oracle_workloads(Z, name):
+    w = W.get(name)
+    ref = oracle.Layout(w.numels, N=w.N, A=w.A, B=w.B)
+    h, info, offs = lib_layout(Z, w.numels, w.N, w.A, w.B)
+    try:
+        assert offs == ref.offsets.tolist()
+        assert (info.used_L, info.shard_S, info.padded_L) == (ref.L, ref.S, ref.L_pad)
+        ranks = range(w.N) if name in ("tiny",) else (0, w.N // 2, w.N - 1)
+        for r in ranks:
+            assert [list(s) for s in Z.zero_layout_segments(h, r)] == ref.segments(r).tolist()
+        if ref.S <= 2_000_000:
+            for r in ranks:
+                assert ([list(b) for b in Z.zero_layout_buckets(h, r, 4096)] ==
+                        ref.buckets(r, 4096).tolist())
+        for stage in range(4):
+            assert Z.zero_layout_mem_values(h, stage) == ref.mem_values(stage).tolist()
+    finally:
+        Z.zero_layout_free(h)
+
+
+def test_bucket_struct_is_16_bytes_and_matches(Z):
+    h = Z.zero_layout_build([3, 200, 300], 4, 256, 8)
+    try:
+        raw, n = Z.zero_layout_buckets_raw(h, 1, 64)
+        arr = np.frombuffer(bytes(raw)[: 16 * n], dtype=np.dtype([("off", "<i8"), ("len", "<i4"),
+                                                                   ("t", "<i4")]))
+        assert [tuple(int(v) for v in x) for x in arr] == [tuple(b) for b in Z.zero_layout_buckets(h, 1, 64)]
+    finally:
+        Z.zero_layout_free(h)
+
+
+def test_layout_errors(Z):
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_layout_build([1, 2], 0)
+    assert e.value.status == -1
+    with pytest.raises(Z.ZeroError):
+        Z.zero_layout_build([1, -2], 2)
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_layout_build([2 ** 62, 2 ** 62], 2)
+    assert e.value.status == -3
+    h = Z.zero_layout_build([10], 2)
+    try:
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_layout_segments(h, 2)
+        assert e.value.status == -3
+        with pytest.raises(Z.ZeroError):
+            Z.zero_layout_buckets(h, 0, 0)
+        with pytest.raises(Z.ZeroError):
+            Z.zero_layout_mem_values(h, 4)
+        # capacity protocol: too small a capacity reports the count and ZERO_E_RANGE
+        n = ctypes.c_int64()
+        out = (Z.zero_segment * 1)()
+        h2 = Z.zero_layout_build([4, 4, 4], 1)
+        rc = Z.lib().zero_layout_segments(h2, 0, out, 1, ctypes.byref(n))
+        assert rc == -3 and n.value == 3
+        Z.zero_layout_free(h2)
+    finally:
+        Z.zero_layout_free(h)
+
+
+FAKE = 1 << 40          # a 16-byte aligned address; validation fails before any use
+
+
+def base_args(Z, **kw):
+    S = kw.pop("shard_S", 64)
+    d = dict(p_in=FAKE, m_in=FAKE + 4096, v_in=FAKE + 8192, p_out=FAKE + 12288,
+             m_out=FAKE + 16384, v_out=FAKE + 20480, slot=FAKE + 24576, shard_S=S,
+             lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step_t=1,
+             stats=FAKE + 28672, workspace=FAKE + 32768)
+    d.update(kw)
+    a = Z.make_adam_args(**d)
+    a.ws_bytes = Z.zero_workspace_bytes(S)
+    return a
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(), -1),                                             # neither replicas nor grad_f32
+    (dict(grad_f32=FAKE + 40960, replicas=[FAKE + 45056]), -1),   # both
+    (dict(grad_f32=FAKE + 40960, p_in=FAKE + 8), -2),          # misaligned
+    (dict(grad_f32=FAKE + 40960, p_in=0), -1),                 # NULL
+    (dict(grad_f32=FAKE + 40960, beta1=1.0), -1),
+    (dict(grad_f32=FAKE + 40960, step_t=0), -1),
+    (dict(grad_f32=FAKE + 40960, eps=float("nan")), -1),
+    (dict(grad_f32=FAKE + 40960, shard_S=-1), -3),
+    (dict(replicas=[FAKE + 45056] * 300), -3),                  # too many replicas
+    (dict(replicas=[FAKE + 45056], loss_scale=0.0), -1),
+    (dict(replicas=[FAKE + 45056], p_out=FAKE), -1),            # fused must be out of place
+    (dict(grad_f32=FAKE + 40960, p_out=FAKE + 100), -2),        # misaligned output
+    (dict(grad_f32=FAKE + 40960, p_out=FAKE + 64), -1),         # partial overlap with p_in
+    (dict(grad_f32=FAKE + 40960, slot=FAKE + 12288 + 16), -1),  # slot overlaps p_out
+    (dict(replicas=[FAKE + 45056], m_out=FAKE + 45056), -1),    # output overlaps a replica
+    (dict(grad_f32=FAKE + 40960, n_buckets=3), -1),             # bucket count without table
+])
+def test_adam_step_validation(Z, change, status):
+    a = base_args(Z, **change)
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_adam_step(a, stream=0)
+    assert e.value.status == status, str(e.value)
+    assert Z.zero_last_error()
+
+
+def test_adam_step_small_workspace_rejected(Z):
+    a = base_args(Z, grad_f32=FAKE + 40960)
+    a.ws_bytes = 8
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_adam_step(a, stream=0)
+    assert e.value.status == -3
+
+
+def test_reduce_and_gather_validation(Z):
+    L = Z.lib()
+    tbl = (ctypes.c_void_p * 2)(FAKE, FAKE + 8)
+    ws = Z.zero_workspace_bytes(64)
+    assert L.zero_reduce_shard(tbl, 2, 1, 64, None, 0, 1.0, None, FAKE + 4096, FAKE + 8192, ws, None) == -2
+    tbl = (ctypes.c_void_p * 2)(FAKE, FAKE + 256)
+    assert L.zero_reduce_shard(tbl, 0, 1, 64, None, 0, 1.0, None, FAKE + 4096, FAKE + 8192, ws, None) == -3
+    assert L.zero_reduce_shard(tbl, 2, 7, 64, None, 0, 1.0, None, FAKE + 4096, FAKE + 8192, ws, None) == -1
+    assert L.zero_reduce_shard(tbl, 2, 1, 64, None, 0, -1.0, None, FAKE + 4096, FAKE + 8192, ws, None) == -1
+    assert L.zero_reduce_shard(tbl, 2, 1, 64, None, 0, 1.0, FAKE + 64, FAKE + 4096, FAKE + 8192, ws, None) == -1
+    assert L.zero_reduce_shard(tbl, 2, 1, 64, None, 0, 1.0, None, None, FAKE + 8192, ws, None) == -1
+    assert L.zero_gather_slot(FAKE, 64, FAKE + 8, None) == -2
+    assert L.zero_gather_slot(FAKE, 64, FAKE + 64, None) == -1
+    assert L.zero_gather_slot(None, 64, FAKE, None) == -1
+    assert L.zero_gather_slot(FAKE, -1, FAKE + 4096, None) == -3
+    assert L.zero_gather_slot(FAKE, 0, FAKE + 4096, None) == 0     # empty: nothing to launch
+
+
+def test_commit_rule_matches_oracle_trainer(Z):
+    st = Z.zero_train_state(t=0, n_skipped=0, loss_scale=65536.0, min_loss_scale=1.0, dynamic=1)
+    flags = [0, 1, 1, 0, 1]
+    verdicts = []
+    for f in flags:
+        verdicts.append(Z.zero_commit_rule(st, Z.zero_stats(overflow=f, bad_buckets=0, sumsq=0.0)))
+    assert verdicts == [1, 2, 2, 1, 2]
+    assert st.t == 2 and st.n_skipped == 3 and st.loss_scale == 8192.0
+    st = Z.zero_train_state(t=5, n_skipped=0, loss_scale=2.0, min_loss_scale=1.0, dynamic=1)
+    for _ in range(3):
+        Z.zero_commit_rule(st, Z.zero_stats(overflow=1))
+    assert st.loss_scale == 1.0 and st.t == 5
+    st = Z.zero_train_state(t=0, n_skipped=0, loss_scale=4.0, min_loss_scale=1.0, dynamic=0)
+    Z.zero_commit_rule(st, Z.zero_stats(overflow=1))
+    assert st.loss_scale == 4.0

@@ -1,0 +1,20 @@
+"""zero_partitioned_optimizer_amd -- the per-rank ZeRO stage-1/2 optimizer step on one
+MI355X (gfx950): N resident gradient replicas of this rank's shard are folded in
+ring order, averaged and unscaled, checked for overflow, used for an Adam/AdamW
+update of fp32 master / m / v, and the bf16 result lands in this rank's slot of
+the gathered parameter buffer.
+
+The compute lives in ``libzero.so`` (hand-written HIP for gfx950 behind a C ABI,
+``include/zero.h``); this package is its ctypes binding (same function names)
+plus ``ShardStep``, which owns buffers and applies the commit rule. There is no
+CPU fallback: without the built library every call raises.
+"""
+from ._binding import (  # noqa: F401
+    ZERO_BF16, ZERO_COMMIT, ZERO_F32, ZERO_MAX_REPLICAS, ZERO_SKIP, ZeroError, lib,
+    make_adam_args, stats_from_tensor, zero_adam_args, zero_adam_step, zero_bucket,
+    zero_commit_rule, zero_gather_slot, zero_last_error, zero_layout_buckets,
+    zero_layout_buckets_raw, zero_layout_build, zero_layout_free, zero_layout_info,
+    zero_layout_info_get, zero_layout_mem_bytes, zero_layout_mem_values, zero_layout_offsets,
+    zero_layout_segments, zero_reduce_shard, zero_segment, zero_stats, zero_train_state,
+    zero_version, zero_workspace_bytes)
+from .shard_step import ShardStep  # noqa: F401

@@ -1,0 +1,297 @@
+"""ctypes binding of libzero's C ABI (include/zero.h), argument marshalling only.
+
+Every function keeps the C name. Device buffers are passed as torch tensors (or
+raw integer addresses); torch provides device memory and streams, nothing else.
+torch is imported before the library is opened so that libzero binds to the
+HIP runtime torch already loaded (both carry the soname libamdhip64.so.7).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch  # noqa: F401  (must come before the library is opened)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libzero.so")
+
+i32, i64, u32, f64, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_double,
+                              ctypes.c_void_p, ctypes.c_size_t)
+
+ZERO_OK, ZERO_E_INVAL, ZERO_E_ALIGN, ZERO_E_RANGE, ZERO_E_NOMEM, ZERO_E_HIP, ZERO_E_UNSUPPORTED = \
+    0, -1, -2, -3, -4, -5, -6
+ZERO_F32, ZERO_BF16 = 0, 1
+ZERO_COMMIT, ZERO_SKIP = 1, 2
+ZERO_MAX_REPLICAS = 256
+
+_STATUS = {0: "ZERO_OK", -1: "ZERO_E_INVAL", -2: "ZERO_E_ALIGN", -3: "ZERO_E_RANGE",
+           -4: "ZERO_E_NOMEM", -5: "ZERO_E_HIP", -6: "ZERO_E_UNSUPPORTED"}
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class zero_layout_info(ctypes.Structure):
+    _fields_ = [("n_tensors", i64), ("psi", i64), ("used_L", i64), ("padded_L", i64),
+                ("shard_S", i64), ("tensor_align_A", i64), ("shard_align_B", i64),
+                ("world_N", i32), ("reserved", i32)]
+
+
+class zero_segment(ctypes.Structure):
+    _fields_ = [("tensor", i32), ("reserved", i32), ("tensor_off", i64), ("shard_off", i64),
+                ("len", i64)]
+
+
+class zero_bucket(ctypes.Structure):
+    _fields_ = [("shard_off", i64), ("len", i32), ("tensor", i32)]
+
+
+class zero_stats(ctypes.Structure):
+    _fields_ = [("overflow", u32), ("bad_buckets", u32), ("sumsq", f64)]
+
+
+class zero_adam_args(ctypes.Structure):
+    _fields_ = [("replicas", ctypes.POINTER(vp)), ("n_replicas", i32), ("grad_dtype", i32),
+                ("grad_f32", vp),
+                ("p_in", vp), ("m_in", vp), ("v_in", vp), ("p_out", vp), ("m_out", vp),
+                ("v_out", vp), ("slot_bf16", vp), ("shard_S", i64), ("buckets_dev", vp),
+                ("n_buckets", i64), ("lr", f64), ("beta1", f64), ("beta2", f64), ("eps", f64),
+                ("weight_decay", f64), ("loss_scale", f64), ("step_t", i64),
+                ("stats_dev", vp), ("workspace_dev", vp), ("ws_bytes", sz),
+                ("event_begin", vp), ("event_end", vp)]
+
+
+class zero_train_state(ctypes.Structure):
+    _fields_ = [("t", i64), ("n_skipped", i64), ("loss_scale", f64), ("min_loss_scale", f64),
+                ("dynamic", i32), ("reserved", i32)]
+
+
+assert ctypes.sizeof(zero_bucket) == 16 and ctypes.sizeof(zero_stats) == 16
+assert ctypes.sizeof(zero_segment) == 32
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Open libzero.so (building it first only if it does not exist)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    L.zero_layout_build.argtypes = [P(i64), i64, i32, i64, i64, P(vp)]
+    L.zero_layout_info_get.argtypes = [vp, P(zero_layout_info)]
+    L.zero_layout_offsets.argtypes = [vp, P(i64)]
+    L.zero_layout_segments.argtypes = [vp, i32, P(zero_segment), i64, P(i64)]
+    L.zero_layout_buckets.argtypes = [vp, i32, i64, P(zero_bucket), i64, P(i64)]
+    L.zero_layout_mem_values.argtypes = [vp, i32, P(i64)]
+    L.zero_layout_mem_bytes.argtypes = [vp, i32, P(i64)]
+    L.zero_layout_free.argtypes = [vp]
+    L.zero_layout_free.restype = None
+    L.zero_workspace_bytes.argtypes = [i64]
+    L.zero_workspace_bytes.restype = sz
+    L.zero_reduce_shard.argtypes = [P(vp), i32, i32, i64, vp, i64, f64, vp, vp, vp, sz, vp]
+    L.zero_adam_step.argtypes = [P(zero_adam_args), vp]
+    L.zero_gather_slot.argtypes = [vp, i64, vp, vp]
+    L.zero_commit_rule.argtypes = [P(zero_train_state), P(zero_stats)]
+    L.zero_last_error.argtypes = []
+    L.zero_last_error.restype = ctypes.c_char_p
+    L.zero_version.argtypes = []
+    L.zero_version.restype = ctypes.c_char_p
+    for name in ("zero_layout_build", "zero_layout_info_get", "zero_layout_offsets",
+                 "zero_layout_segments", "zero_layout_buckets", "zero_layout_mem_values",
+                 "zero_layout_mem_bytes", "zero_reduce_shard", "zero_adam_step",
+                 "zero_gather_slot", "zero_commit_rule"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise ZeroError(rc, lib().zero_last_error().decode())
+    return rc
+
+
+def _addr(x) -> int:
+    """Device address of a tensor (or an int address, or None -> 0)."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# layout (host only)
+# ---------------------------------------------------------------------------
+
+def zero_layout_build(numels: Sequence[int], world_N: int, tensor_align_A: int = 1,
+                      shard_align_B: int = 8) -> int:
+    """Returns an opaque layout handle (free with zero_layout_free)."""
+    arr = (i64 * max(len(numels), 1))(*[int(n) for n in numels])
+    h = vp()
+    _check(lib().zero_layout_build(arr, len(numels), int(world_N), int(tensor_align_A),
+                                   int(shard_align_B), ctypes.byref(h)))
+    return h.value
+
+
+def zero_layout_info_get(h: int) -> zero_layout_info:
+    info = zero_layout_info()
+    _check(lib().zero_layout_info_get(h, ctypes.byref(info)))
+    return info
+
+
+def zero_layout_offsets(h: int) -> list:
+    n = zero_layout_info_get(h).n_tensors
+    out = (i64 * max(n, 1))()
+    _check(lib().zero_layout_offsets(h, out))
+    return list(out)[:n]
+
+
+def zero_layout_segments(h: int, rank: int) -> list:
+    """List of (tensor, tensor_off, shard_off, len)."""
+    n = i64()
+    _check(lib().zero_layout_segments(h, int(rank), None, 0, ctypes.byref(n)))
+    out = (zero_segment * max(n.value, 1))()
+    _check(lib().zero_layout_segments(h, int(rank), out, n.value, ctypes.byref(n)))
+    return [(s.tensor, s.tensor_off, s.shard_off, s.len) for s in out[:n.value]]
+
+
+def zero_layout_buckets_raw(h: int, rank: int, bucket_elems: int):
+    """The bucket table as a ctypes array of zero_bucket (16 bytes each) and its length."""
+    n = i64()
+    _check(lib().zero_layout_buckets(h, int(rank), int(bucket_elems), None, 0, ctypes.byref(n)))
+    out = (zero_bucket * max(n.value, 1))()
+    _check(lib().zero_layout_buckets(h, int(rank), int(bucket_elems), out, n.value, ctypes.byref(n)))
+    return out, n.value
+
+
+def zero_layout_buckets(h: int, rank: int, bucket_elems: int) -> list:
+    """List of (shard_off, len, tensor)."""
+    out, n = zero_layout_buckets_raw(h, rank, bucket_elems)
+    return [(b.shard_off, b.len, b.tensor) for b in out[:n]]
+
+
+def zero_layout_mem_values(h: int, stage: int) -> list:
+    out = (i64 * 4)()
+    _check(lib().zero_layout_mem_values(h, int(stage), out))
+    return list(out)
+
+
+def zero_layout_mem_bytes(h: int, stage: int) -> list:
+    out = (i64 * 4)()
+    _check(lib().zero_layout_mem_bytes(h, int(stage), out))
+    return list(out)
+
+
+def zero_layout_free(h: int) -> None:
+    lib().zero_layout_free(h)
+
+
+# ---------------------------------------------------------------------------
+# device step
+# ---------------------------------------------------------------------------
+
+def zero_workspace_bytes(shard_S: int) -> int:
+    return int(lib().zero_workspace_bytes(int(shard_S)))
+
+
+def _replica_table(replicas):
+    return (vp * max(len(replicas), 1))(*[_addr(r) for r in replicas])
+
+
+def zero_reduce_shard(replicas, grad_dtype: int, shard_S: int, stats, workspace, *,
+                      buckets=None, n_buckets: int = 0, loss_scale: float = 1.0,
+                      grad_out=None, stream=None) -> None:
+    table = _replica_table(replicas)
+    ws = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    _check(lib().zero_reduce_shard(table, len(replicas), int(grad_dtype), int(shard_S),
+                                   _addr(buckets), int(n_buckets), float(loss_scale),
+                                   _addr(grad_out), _addr(stats), _addr(workspace), ws,
+                                   _stream(stream)))
+
+
+def make_adam_args(*, replicas=None, grad_dtype: int = ZERO_BF16, grad_f32=None, p_in, m_in, v_in,
+                   p_out, m_out, v_out, slot=None, shard_S: int, buckets=None, n_buckets: int = 0,
+                   lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+                   loss_scale: float = 1.0, step_t: int, stats, workspace, event_begin=None,
+                   event_end=None):
+    a = zero_adam_args()
+    keep = []
+    if replicas is not None:
+        table = _replica_table(replicas)
+        keep.append(table)
+        a.replicas = ctypes.cast(table, ctypes.POINTER(vp))
+        a.n_replicas = len(replicas)
+    a.grad_dtype = int(grad_dtype)
+    a.grad_f32 = _addr(grad_f32) or None
+    for name, t in (("p_in", p_in), ("m_in", m_in), ("v_in", v_in), ("p_out", p_out),
+                    ("m_out", m_out), ("v_out", v_out), ("slot_bf16", slot)):
+        setattr(a, name, _addr(t) or None)
+    a.shard_S = int(shard_S)
+    a.buckets_dev = _addr(buckets) or None
+    a.n_buckets = int(n_buckets)
+    a.lr, a.beta1, a.beta2, a.eps = float(lr), float(beta1), float(beta2), float(eps)
+    a.weight_decay, a.loss_scale, a.step_t = float(weight_decay), float(loss_scale), int(step_t)
+    a.stats_dev = _addr(stats) or None
+    a.workspace_dev = _addr(workspace) or None
+    a.ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    a.event_begin = _event(event_begin)
+    a.event_end = _event(event_end)
+    a._keep = keep
+    return a
+
+
+def _event(ev):
+    """hipEvent_t handle of a torch.cuda.Event (created on first record if needed)."""
+    if ev is None:
+        return None
+    if isinstance(ev, int):
+        return ev
+    h = ev.cuda_event
+    if not h:
+        ev.record()
+        h = ev.cuda_event
+    return h
+
+
+def zero_adam_step(args: zero_adam_args, stream=None) -> None:
+    _check(lib().zero_adam_step(ctypes.byref(args), _stream(stream)))
+
+
+def zero_gather_slot(master, shard_S: int, slot, stream=None) -> None:
+    _check(lib().zero_gather_slot(_addr(master), int(shard_S), _addr(slot), _stream(stream)))
+
+
+def zero_commit_rule(state: zero_train_state, stats_host: zero_stats) -> int:
+    return _check(lib().zero_commit_rule(ctypes.byref(state), ctypes.byref(stats_host)))
+
+
+def zero_last_error() -> str:
+    return lib().zero_last_error().decode()
+
+
+def zero_version() -> str:
+    return lib().zero_version().decode()
+
+
+def stats_from_tensor(t) -> zero_stats:
+    """Read a 16-byte device zero_stats (uint8 tensor) into a host struct (synchronizes)."""
+    raw = bytes(t.detach().to("cpu").numpy().tobytes())
+    return zero_stats.from_buffer_copy(raw)

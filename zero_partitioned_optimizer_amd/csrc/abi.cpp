@@ -1,0 +1,373 @@
+// abi.cpp -- the C entry points of libzero that launch device work: argument
+// validation, the fp32 scalars of an update, error text, and the host-side
+// commit rule. Kernels live in step_kernels.hip, the layout in layout.cpp.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "zero.h"
+#include "zero_internal.h"
+
+namespace zl {
+
+static thread_local std::string g_err;
+
+void set_error(const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+}
+
+}  // namespace zl
+
+namespace {
+
+using zl::set_error;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    const char* name;
+    uintptr_t lo, hi;               // [lo, hi)
+};
+
+Span span(const char* name, const void* p, int64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{name, lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlap(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return ZERO_OK;
+    set_error("%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+    return ZERO_E_HIP;
+}
+
+// beta^t as the t-fold product in double (1.0 * beta * beta * ...). A per-thread
+// memo of the last (beta, t, beta^t) per beta lets consecutive steps extend the
+// product by one multiply instead of t.
+double pow_t(double beta, int64_t t) {
+    struct Memo {
+        double beta;
+        int64_t t;
+        double value;
+    };
+    static thread_local Memo memo[2] = {{-1.0, -1, 1.0}, {-1.0, -1, 1.0}};
+    static thread_local int next = 0;
+    Memo* m = nullptr;
+    for (Memo& x : memo)
+        if (x.beta == beta && x.t >= 0 && x.t <= t) m = &x;
+    if (!m) {
+        m = &memo[next];
+        next ^= 1;
+        *m = Memo{beta, 0, 1.0};
+    }
+    double v = m->value;
+    for (int64_t k = m->t; k < t; ++k) v = v * beta;
+    m->t = t;
+    m->value = v;
+    return v;
+}
+
+zk::Scalars adam_scalars(const zero_adam_args& a, int32_t n, double loss_scale) {
+    zk::Scalars s;
+    s.inv = (float)(1.0 / ((double)n * loss_scale));
+    s.b1 = (float)a.beta1;
+    s.b2 = (float)a.beta2;
+    s.omb1 = (float)(1.0 - a.beta1);
+    s.omb2 = (float)(1.0 - a.beta2);
+    s.bc1 = (float)(1.0 - pow_t(a.beta1, a.step_t));
+    s.bc2 = (float)(1.0 - pow_t(a.beta2, a.step_t));
+    s.lr = (float)a.lr;
+    s.eps = (float)a.eps;
+    s.decay = (float)(1.0 - a.lr * a.weight_decay);
+    return s;
+}
+
+int check_replicas(const char* fn, const void* const* replicas, int32_t n, zero_dtype dt,
+                   int64_t S) {
+    if (!replicas) {
+        set_error("%s: replicas is NULL", fn);
+        return ZERO_E_INVAL;
+    }
+    if (n < 1 || n > ZERO_MAX_REPLICAS) {
+        set_error("%s: n_replicas=%d outside [1, %d]", fn, (int)n, ZERO_MAX_REPLICAS);
+        return ZERO_E_RANGE;
+    }
+    if (dt != ZERO_F32 && dt != ZERO_BF16) {
+        set_error("%s: grad_dtype %d is neither ZERO_F32 nor ZERO_BF16", fn, (int)dt);
+        return ZERO_E_INVAL;
+    }
+    for (int32_t j = 0; j < n; ++j) {
+        if (!replicas[j] && S > 0) {
+            set_error("%s: replicas[%d] is NULL", fn, (int)j);
+            return ZERO_E_INVAL;
+        }
+        if (!aligned16(replicas[j])) {
+            set_error("%s: replicas[%d]=%p is not 16-byte aligned", fn, (int)j, replicas[j]);
+            return ZERO_E_ALIGN;
+        }
+    }
+    return ZERO_OK;
+}
+
+int check_common(const char* fn, int64_t S, const zero_bucket* buckets, int64_t n_buckets,
+                 const zero_stats* stats, const void* ws, size_t ws_bytes) {
+    if (S < 0) {
+        set_error("%s: shard_S=%lld is negative", fn, (long long)S);
+        return ZERO_E_RANGE;
+    }
+    if (n_buckets < 0) {
+        set_error("%s: n_buckets=%lld is negative", fn, (long long)n_buckets);
+        return ZERO_E_RANGE;
+    }
+    if (n_buckets > 0 && !buckets) {
+        set_error("%s: n_buckets=%lld with a NULL bucket table", fn, (long long)n_buckets);
+        return ZERO_E_INVAL;
+    }
+    if (n_buckets > 0 && (reinterpret_cast<uintptr_t>(buckets) & 7u)) {
+        set_error("%s: bucket table %p is not 8-byte aligned", fn, (const void*)buckets);
+        return ZERO_E_ALIGN;
+    }
+    if (!stats || !ws) {
+        set_error("%s: stats_dev or workspace_dev is NULL", fn);
+        return ZERO_E_INVAL;
+    }
+    if (!aligned16(stats) || !aligned16(ws)) {
+        set_error("%s: stats_dev or workspace_dev is not 16-byte aligned", fn);
+        return ZERO_E_ALIGN;
+    }
+    const size_t need = (size_t)zk::grid_for(S, n_buckets) * sizeof(zk::Partial);
+    if (ws_bytes < need) {
+        set_error("%s: workspace of %zu bytes < %zu needed", fn, ws_bytes, need);
+        return ZERO_E_RANGE;
+    }
+    return ZERO_OK;
+}
+
+bool finite_in(double x, double lo, double hi) { return isfinite(x) && x >= lo && x < hi; }
+
+}  // namespace
+
+extern "C" {
+
+const char* zero_last_error(void) { return zl::g_err.c_str(); }
+
+const char* zero_version(void) { return "libzero 1.0 (gfx950)"; }
+
+size_t zero_workspace_bytes(int64_t shard_S) {
+    (void)shard_S;
+    return (size_t)zk::kGridMax * sizeof(zk::Partial);
+}
+
+int zero_reduce_shard(const void* const* replicas, int32_t n_replicas, zero_dtype grad_dtype,
+                      int64_t shard_S, const zero_bucket* buckets_dev, int64_t n_buckets,
+                      double loss_scale, float* grad_out_dev, zero_stats* stats_dev,
+                      void* workspace_dev, size_t ws_bytes, void* stream) {
+    static const char* fn = "zero_reduce_shard";
+    int rc = check_replicas(fn, replicas, n_replicas, grad_dtype, shard_S);
+    if (rc) return rc;
+    rc = check_common(fn, shard_S, buckets_dev, n_buckets, stats_dev, workspace_dev, ws_bytes);
+    if (rc) return rc;
+    if (!(isfinite(loss_scale) && loss_scale > 0.0)) {
+        set_error("%s: loss_scale=%g must be finite and > 0", fn, loss_scale);
+        return ZERO_E_INVAL;
+    }
+    if (grad_out_dev && !aligned16(grad_out_dev)) {
+        set_error("%s: grad_out_dev is not 16-byte aligned", fn);
+        return ZERO_E_ALIGN;
+    }
+    const int64_t gb = grad_dtype == ZERO_BF16 ? 2 : 4;
+    if (grad_out_dev) {
+        const Span out = span("grad_out", grad_out_dev, 4 * shard_S);
+        for (int32_t j = 0; j < n_replicas; ++j)
+            if (overlap(out, span("replica", replicas[j], gb * shard_S))) {
+                set_error("%s: grad_out overlaps replicas[%d]", fn, (int)j);
+                return ZERO_E_INVAL;
+            }
+        if (overlap(out, span("stats", stats_dev, 16)) ||
+            overlap(out, span("workspace", workspace_dev, (int64_t)ws_bytes))) {
+            set_error("%s: grad_out overlaps stats or workspace", fn);
+            return ZERO_E_INVAL;
+        }
+    }
+    zk::StepDesc d{};
+    d.replicas = replicas;
+    d.n_rep = n_replicas;
+    d.dtype = grad_dtype;
+    d.S = shard_S;
+    d.buckets = n_buckets > 0 ? buckets_dev : nullptr;
+    d.n_buckets = n_buckets;
+    d.adam = false;
+    d.g_out = grad_out_dev;
+    d.sc = zk::Scalars{};
+    d.sc.inv = (float)(1.0 / ((double)n_replicas * loss_scale));
+    d.stats = stats_dev;
+    d.partials = static_cast<zk::Partial*>(workspace_dev);
+    return hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
+}
+
+int zero_adam_step(const zero_adam_args* args, void* stream) {
+    static const char* fn = "zero_adam_step";
+    if (!args) {
+        set_error("%s: args is NULL", fn);
+        return ZERO_E_INVAL;
+    }
+    const zero_adam_args& a = *args;
+    const bool fused = a.replicas != nullptr;
+    if (fused == (a.grad_f32 != nullptr)) {
+        set_error("%s: exactly one of replicas and grad_f32 must be given", fn);
+        return ZERO_E_INVAL;
+    }
+    const int64_t S = a.shard_S;
+    int rc = check_common(fn, S, a.buckets_dev, a.n_buckets, a.stats_dev, a.workspace_dev, a.ws_bytes);
+    if (rc) return rc;
+    if (fused) {
+        rc = check_replicas(fn, a.replicas, a.n_replicas, a.grad_dtype, S);
+        if (rc) return rc;
+    }
+    const void* need[] = {fused ? (const void*)a.replicas : (const void*)a.grad_f32, a.p_in, a.m_in,
+                          a.v_in, a.p_out, a.m_out, a.v_out};
+    for (const void* p : need) {
+        if (!p && (S > 0 || p == (const void*)a.replicas)) {
+            set_error("%s: a state or gradient buffer (p/m/v in/out, grad_f32) is NULL", fn);
+            return ZERO_E_INVAL;
+        }
+        if (!aligned16(p) && p != (const void*)a.replicas) {
+            set_error("%s: a state or gradient buffer is not 16-byte aligned", fn);
+            return ZERO_E_ALIGN;
+        }
+    }
+    if (a.slot_bf16 && !aligned16(a.slot_bf16)) {
+        set_error("%s: slot_bf16 is not 16-byte aligned", fn);
+        return ZERO_E_ALIGN;
+    }
+    if (!finite_in(a.beta1, 0.0, 1.0) || !finite_in(a.beta2, 0.0, 1.0) || !(isfinite(a.lr) && a.lr >= 0) ||
+        !(isfinite(a.eps) && a.eps >= 0) || !(isfinite(a.weight_decay) && a.weight_decay >= 0) ||
+        a.step_t < 1 || (fused && !(isfinite(a.loss_scale) && a.loss_scale > 0))) {
+        set_error("%s: hyperparameters out of domain (lr=%g beta1=%g beta2=%g eps=%g wd=%g "
+                  "loss_scale=%g t=%lld)", fn, a.lr, a.beta1, a.beta2, a.eps, a.weight_decay,
+                  a.loss_scale, (long long)a.step_t);
+        return ZERO_E_INVAL;
+    }
+    // Aliasing: outputs must be pairwise disjoint and disjoint from every input,
+    // except that the unfused path may update p, m, v exactly in place.
+    const int64_t b4 = 4 * S;
+    const Span outs[] = {span("p_out", a.p_out, b4), span("m_out", a.m_out, b4),
+                         span("v_out", a.v_out, b4),
+                         span("slot", a.slot_bf16, a.slot_bf16 ? 2 * S : 0),
+                         span("stats", a.stats_dev, 16),
+                         span("workspace", a.workspace_dev, (int64_t)a.ws_bytes)};
+    const int n_outs = 6;
+    for (int i = 0; i < n_outs; ++i)
+        for (int k = i + 1; k < n_outs; ++k)
+            if (overlap(outs[i], outs[k])) {
+                set_error("%s: outputs %s and %s overlap", fn, outs[i].name, outs[k].name);
+                return ZERO_E_INVAL;
+            }
+    const Span ins_state[] = {span("p_in", a.p_in, b4), span("m_in", a.m_in, b4),
+                              span("v_in", a.v_in, b4)};
+    for (int i = 0; i < n_outs; ++i) {
+        for (int k = 0; k < 3; ++k) {
+            if (!overlap(outs[i], ins_state[k])) continue;
+            const bool exact_alias = !fused && i == k && outs[i].lo == ins_state[k].lo;
+            if (!exact_alias) {
+                set_error("%s: output %s overlaps input %s%s", fn, outs[i].name, ins_state[k].name,
+                          fused ? " (the fused step must be out of place)" : "");
+                return ZERO_E_INVAL;
+            }
+        }
+        if (fused) {
+            const int64_t gb = a.grad_dtype == ZERO_BF16 ? 2 : 4;
+            for (int32_t j = 0; j < a.n_replicas; ++j)
+                if (overlap(outs[i], span("replica", a.replicas[j], gb * S))) {
+                    set_error("%s: output %s overlaps replicas[%d]", fn, outs[i].name, (int)j);
+                    return ZERO_E_INVAL;
+                }
+        } else if (overlap(outs[i], span("grad_f32", a.grad_f32, b4))) {
+            set_error("%s: output %s overlaps grad_f32", fn, outs[i].name);
+            return ZERO_E_INVAL;
+        }
+        if (a.n_buckets > 0 &&
+            overlap(outs[i], span("buckets", a.buckets_dev, 16 * a.n_buckets))) {
+            set_error("%s: output %s overlaps the bucket table", fn, outs[i].name);
+            return ZERO_E_INVAL;
+        }
+    }
+    const void* one_rep[1] = {a.grad_f32};
+    zk::StepDesc d{};
+    d.replicas = fused ? a.replicas : one_rep;
+    d.n_rep = fused ? a.n_replicas : 1;
+    d.dtype = fused ? a.grad_dtype : ZERO_F32;
+    d.S = S;
+    d.buckets = a.n_buckets > 0 ? a.buckets_dev : nullptr;
+    d.n_buckets = a.n_buckets;
+    d.adam = true;
+    d.p_in = a.p_in;
+    d.m_in = a.m_in;
+    d.v_in = a.v_in;
+    d.p_out = a.p_out;
+    d.m_out = a.m_out;
+    d.v_out = a.v_out;
+    d.slot = a.slot_bf16;
+    d.g_out = nullptr;
+    // the unfused source is already averaged and unscaled: inv = 1 (x * 1 == x)
+    d.sc = adam_scalars(a, fused ? a.n_replicas : 1, fused ? a.loss_scale : 1.0);
+    d.stats = a.stats_dev;
+    d.partials = static_cast<zk::Partial*>(a.workspace_dev);
+    d.ev_begin = static_cast<hipEvent_t>(a.event_begin);
+    d.ev_end = static_cast<hipEvent_t>(a.event_end);
+    return hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
+}
+
+int zero_gather_slot(const float* master_dev, int64_t shard_S, uint16_t* slot_bf16_dev,
+                     void* stream) {
+    static const char* fn = "zero_gather_slot";
+    if (shard_S < 0) {
+        set_error("%s: shard_S=%lld is negative", fn, (long long)shard_S);
+        return ZERO_E_RANGE;
+    }
+    if (shard_S > 0 && (!master_dev || !slot_bf16_dev)) {
+        set_error("%s: NULL buffer", fn);
+        return ZERO_E_INVAL;
+    }
+    if (!aligned16(master_dev) || !aligned16(slot_bf16_dev)) {
+        set_error("%s: buffers must be 16-byte aligned", fn);
+        return ZERO_E_ALIGN;
+    }
+    if (overlap(span("master", master_dev, 4 * shard_S), span("slot", slot_bf16_dev, 2 * shard_S))) {
+        set_error("%s: master and slot overlap", fn);
+        return ZERO_E_INVAL;
+    }
+    if (shard_S == 0) return ZERO_OK;
+    return hip_status(zk::launch_cast_slot(master_dev, shard_S, slot_bf16_dev,
+                                           static_cast<hipStream_t>(stream)), fn);
+}
+
+int zero_commit_rule(zero_train_state* state, const zero_stats* stats_host) {
+    if (!state || !stats_host) {
+        set_error("zero_commit_rule: NULL argument");
+        return ZERO_E_INVAL;
+    }
+    if (stats_host->overflow == 0u) {
+        state->t += 1;
+        return ZERO_COMMIT;
+    }
+    state->n_skipped += 1;
+    if (state->dynamic) {
+        const double floor = state->min_loss_scale > 0 ? state->min_loss_scale : 1.0;
+        const double half = state->loss_scale / 2.0;
+        state->loss_scale = half > floor ? half : floor;
+    }
+    return ZERO_SKIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,472 @@
+// step_kernels.hip -- gfx950 kernels of the per-rank ZeRO stage-1/2 shard step.
+//
+// One pass over this rank's shard: fold the N gradient replicas in slot order
+// (the ring order of the reduce-scatter walk in "Why DeepSpeed ZeRO paper says
+// reduce-scatter (or all-gather) has data movement of Psi elements?",
+// GuanhuaWang's reply), average and unscale, flag overflow and accumulate the
+// squared norm, update fp32 master / m / v with Adam, and write the bf16 result
+// into this rank's slot of the gathered parameter buffer ("[REQUEST] Direct
+// Correspondence between Gradient and Optimizer States to Reduce
+// Communication", "Problem").
+//
+// The work is pure streaming: (N * gradient bytes + 26) bytes per element against
+// about 25 fp32 operations (three divisions and a square root among them), far
+// under the fp32 vector ridge, so HBM bandwidth bounds it. There is no dense
+// contraction and no MFMA. Design points:
+//  - wave64 lanes each own one quad (4 consecutive elements) per row: bf16
+//    replicas come in as dwordx2, fp32 state as dwordx4, so a wave reads 512 B
+//    (bf16) or 1 KiB (fp32) contiguous per instruction;
+//  - every lane issues its p/m/v loads and a whole batch of up to 8 replica
+//    loads before the first add, for bytes in flight;
+//  - a fixed grid of at most kGridMax workgroups strides over the shard, so the
+//    working front stays compact in HBM and the per-workgroup partials stay few;
+//  - the flag and the fp64 squared norm are reduced with wave shuffles, then
+//    LDS, then one partial per workgroup; a one-workgroup finalize sums the
+//    partials in workgroup order, so the norm is bit-reproducible and no
+//    atomics or memsets are needed;
+//  - loads of data read once use the nontemporal hint, and so do the stores.
+// Arithmetic is one IEEE fp32 operation per source operation, built with
+// -ffp-contract=off; division and sqrt are the correctly rounded forms.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_internal.h"
+
+#ifndef ZERO_NT
+#define ZERO_NT 1
+#endif
+
+namespace zk {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+struct KParams {
+    const void* rep[ZERO_MAX_REPLICAS];
+    int32_t n_rep;
+    int32_t has_slot;
+    int64_t S;
+    const zero_bucket* buckets;
+    int64_t n_buckets;
+    const float* p_in;
+    const float* m_in;
+    const float* v_in;
+    float* p_out;
+    float* m_out;
+    float* v_out;
+    uint16_t* slot;
+    float* g_out;
+    Partial* partials;
+    Scalars sc;
+};
+
+// ---------------------------------------------------------------------------
+// memory access
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ T ld(const T* p) {
+#if ZERO_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+template <typename T>
+__device__ __forceinline__ void st(T* p, T v) {
+#if ZERO_NT
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+__device__ __forceinline__ float bf2f(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// fp32 -> bf16, round to nearest even; any NaN becomes 0x7FC0.
+__device__ __forceinline__ uint32_t f2bf(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ bool nonfinite(float x) {
+    return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u;
+}
+
+// A quad (4 consecutive elements) of one gradient replica, widened to fp32.
+template <typename RT>
+struct Quad;
+
+template <>
+struct Quad<uint16_t> {
+    using V = u32x2;
+    static __device__ __forceinline__ V load(const void* base, int64_t q) {
+        return ld(reinterpret_cast<const u32x2*>(base) + q);
+    }
+    static __device__ __forceinline__ f32x4 widen(V w) {
+        f32x4 r;
+        r.x = __uint_as_float(w.x << 16);
+        r.y = __uint_as_float(w.x & 0xffff0000u);
+        r.z = __uint_as_float(w.y << 16);
+        r.w = __uint_as_float(w.y & 0xffff0000u);
+        return r;
+    }
+    static __device__ __forceinline__ float one(const void* base, int64_t e) {
+        return bf2f(reinterpret_cast<const uint16_t*>(base)[e]);
+    }
+};
+
+template <>
+struct Quad<float> {
+    using V = f32x4;
+    static __device__ __forceinline__ V load(const void* base, int64_t q) {
+        return ld(reinterpret_cast<const f32x4*>(base) + q);
+    }
+    static __device__ __forceinline__ f32x4 widen(V w) { return w; }
+    static __device__ __forceinline__ float one(const void* base, int64_t e) {
+        return reinterpret_cast<const float*>(base)[e];
+    }
+};
+
+// ---------------------------------------------------------------------------
+// arithmetic
+// ---------------------------------------------------------------------------
+
+// Adam / AdamW on one element, one fp32 operation per line (no contraction).
+__device__ __forceinline__ void adam1(float g, float p, float m, float v, const Scalars& s,
+                                      float& pn, float& m1, float& v1) {
+    const float mt = s.b1 * m;
+    const float mg = s.omb1 * g;
+    m1 = mt + mg;
+    const float gg = g * g;
+    const float vt = s.b2 * v;
+    const float vg = s.omb2 * gg;
+    v1 = vt + vg;
+    const float mh = m1 / s.bc1;
+    const float vh = v1 / s.bc2;
+    const float den = sqrtf(vh) + s.eps;
+    const float u = mh / den;
+    const float p1 = p * s.decay;
+    const float lu = s.lr * u;
+    pn = p1 - lu;
+}
+
+// Load K replicas (slots j .. j+K-1) for ROWS quads, then add them in slot order.
+template <typename RT, int ROWS, int K>
+__device__ __forceinline__ void fold_batch(const KParams& a, int j, int64_t q0, int64_t qs,
+                                           f32x4 (&acc)[ROWS]) {
+    typename Quad<RT>::V buf[K][ROWS];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const void* base = a.rep[j + k];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) buf[k][r] = Quad<RT>::load(base, q0 + r * qs);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) acc[r] = acc[r] + Quad<RT>::widen(buf[k][r]);
+    }
+}
+
+// acc = R_0 + R_1 + ... + R_{N-1}, left to right, for ROWS quads.
+template <typename RT, int ROWS>
+__device__ __forceinline__ void fold(const KParams& a, int64_t q0, int64_t qs, f32x4 (&acc)[ROWS]) {
+    {
+        const void* base = a.rep[0];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) acc[r] = Quad<RT>::widen(Quad<RT>::load(base, q0 + r * qs));
+    }
+    const int n = a.n_rep;
+    int j = 1;
+    for (; j + 8 <= n; j += 8) fold_batch<RT, ROWS, 8>(a, j, q0, qs, acc);
+    switch (n - j) {
+        case 7: fold_batch<RT, ROWS, 7>(a, j, q0, qs, acc); break;
+        case 6: fold_batch<RT, ROWS, 6>(a, j, q0, qs, acc); break;
+        case 5: fold_batch<RT, ROWS, 5>(a, j, q0, qs, acc); break;
+        case 4: fold_batch<RT, ROWS, 4>(a, j, q0, qs, acc); break;
+        case 3: fold_batch<RT, ROWS, 3>(a, j, q0, qs, acc); break;
+        case 2: fold_batch<RT, ROWS, 2>(a, j, q0, qs, acc); break;
+        case 1: fold_batch<RT, ROWS, 1>(a, j, q0, qs, acc); break;
+        default: break;
+    }
+}
+
+// ROWS quads at q0, q0 + qs, ...: the whole step for 4*ROWS elements of this lane.
+template <typename RT, bool ADAM, bool WRITE_G, int ROWS>
+__device__ __forceinline__ void quads(const KParams& a, int64_t q0, int64_t qs, double& sq,
+                                      uint32_t& bad) {
+    f32x4 p[ROWS], m[ROWS], v[ROWS];
+    if constexpr (ADAM) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const int64_t q = q0 + r * qs;
+            p[r] = ld(reinterpret_cast<const f32x4*>(a.p_in) + q);
+            m[r] = ld(reinterpret_cast<const f32x4*>(a.m_in) + q);
+            v[r] = ld(reinterpret_cast<const f32x4*>(a.v_in) + q);
+        }
+    }
+    f32x4 acc[ROWS];
+    fold<RT, ROWS>(a, q0, qs, acc);
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const int64_t q = q0 + r * qs;
+        f32x4 g = acc[r] * a.sc.inv;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bad |= nonfinite(g[c]) ? 1u : 0u;
+            const double gd = (double)g[c];
+            sq += gd * gd;
+        }
+        if constexpr (WRITE_G) st(reinterpret_cast<f32x4*>(a.g_out) + q, g);
+        if constexpr (ADAM) {
+            f32x4 pn, m1, v1;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                float x, y, z;
+                adam1(g[c], p[r][c], m[r][c], v[r][c], a.sc, x, y, z);
+                pn[c] = x;
+                m1[c] = y;
+                v1[c] = z;
+            }
+            st(reinterpret_cast<f32x4*>(a.p_out) + q, pn);
+            st(reinterpret_cast<f32x4*>(a.m_out) + q, m1);
+            st(reinterpret_cast<f32x4*>(a.v_out) + q, v1);
+            if (a.has_slot) {
+                u32x2 w;
+                w.x = f2bf(pn.x) | (f2bf(pn.y) << 16);
+                w.y = f2bf(pn.z) | (f2bf(pn.w) << 16);
+                st(reinterpret_cast<u32x2*>(a.slot) + q, w);
+            }
+        }
+    }
+}
+
+// One element, for bucket edges and the shard tail.
+template <typename RT, bool ADAM, bool WRITE_G>
+__device__ __forceinline__ void one_elem(const KParams& a, int64_t e, double& sq, uint32_t& bad) {
+    float acc = Quad<RT>::one(a.rep[0], e);
+    for (int j = 1; j < a.n_rep; ++j) acc = acc + Quad<RT>::one(a.rep[j], e);
+    const float g = acc * a.sc.inv;
+    bad |= nonfinite(g) ? 1u : 0u;
+    const double gd = (double)g;
+    sq += gd * gd;
+    if constexpr (WRITE_G) a.g_out[e] = g;
+    if constexpr (ADAM) {
+        float pn, m1, v1;
+        adam1(g, a.p_in[e], a.m_in[e], a.v_in[e], a.sc, pn, m1, v1);
+        a.p_out[e] = pn;
+        a.m_out[e] = m1;
+        a.v_out[e] = v1;
+        if (a.has_slot) a.slot[e] = (uint16_t)f2bf(pn);
+    }
+}
+
+// All elements of [lo, hi) by the threads of one workgroup.
+template <typename RT, bool ADAM, bool WRITE_G>
+__device__ __forceinline__ void range(const KParams& a, int64_t lo, int64_t hi, double& sq,
+                                      uint32_t& bad) {
+    const int tid = threadIdx.x;
+    const int64_t qa = (lo + 3) >> 2;       // first whole quad
+    const int64_t qb = hi >> 2;             // one past the last whole quad
+    if (qa >= qb) {
+        for (int64_t e = lo + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, e, sq, bad);
+        return;
+    }
+    for (int64_t e = lo + tid; e < qa * 4; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, e, sq, bad);
+    int64_t q = qa + tid;
+    for (; q + (kRows - 1) * kBlock < qb; q += kRows * kBlock)
+        quads<RT, ADAM, WRITE_G, kRows>(a, q, kBlock, sq, bad);
+    for (; q < qb; q += kBlock) quads<RT, ADAM, WRITE_G, 1>(a, q, 0, sq, bad);
+    for (int64_t e = qb * 4 + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, e, sq, bad);
+}
+
+// Wave64 shuffles, then LDS across the workgroup's waves, in a fixed order.
+__device__ __forceinline__ void block_reduce(double& sq, uint32_t& bad, uint32_t& badb) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        sq += __shfl_xor(sq, off, 64);
+        bad |= __shfl_xor(bad, off, 64);
+        badb += __shfl_xor(badb, off, 64);
+    }
+    constexpr int kWaves = kBlock / 64;
+    __shared__ double s_sq[kWaves];
+    __shared__ uint32_t s_bad[kWaves];
+    __shared__ uint32_t s_badb[kWaves];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) {
+        s_sq[w] = sq;
+        s_bad[w] = bad;
+        s_badb[w] = badb;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = s_sq[0];
+        uint32_t b = s_bad[0], bb = s_badb[0];
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) {
+            t += s_sq[i];
+            b |= s_bad[i];
+            bb += s_badb[i];
+        }
+        sq = t;
+        bad = b;
+        badb = bb;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// kernels
+// ---------------------------------------------------------------------------
+
+template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G>
+__global__ void __launch_bounds__(kBlock) k_step(const KParams a) {
+    double sq = 0.0;
+    uint32_t bad = 0u, badb = 0u;
+    if constexpr (!BUCKETS) {
+        const int64_t nq = a.S >> 2;
+        const int64_t per_trip = (int64_t)kRows * kBlock;
+        const int64_t ntrips = nq / per_trip;
+        for (int64_t trip = blockIdx.x; trip < ntrips; trip += gridDim.x)
+            quads<RT, ADAM, WRITE_G, kRows>(a, trip * per_trip + threadIdx.x, kBlock, sq, bad);
+        // whole quads after the last full trip, and the last S % 4 elements
+        if ((int64_t)blockIdx.x == ntrips % gridDim.x) {
+            for (int64_t q = ntrips * per_trip + threadIdx.x; q < nq; q += kBlock)
+                quads<RT, ADAM, WRITE_G, 1>(a, q, 0, sq, bad);
+            const int64_t e = nq * 4 + threadIdx.x;
+            if (e < a.S) one_elem<RT, ADAM, WRITE_G>(a, e, sq, bad);
+        }
+    } else {
+        for (int64_t b = blockIdx.x; b < a.n_buckets; b += gridDim.x) {
+            const zero_bucket bk = a.buckets[b];
+            const int64_t lo = bk.shard_off, len = bk.len;
+            if (lo < 0 || len < 0 || lo > a.S || len > a.S - lo) {
+                if (threadIdx.x == 0) badb += 1u;
+                continue;
+            }
+            range<RT, ADAM, WRITE_G>(a, lo, lo + len, sq, bad);
+        }
+    }
+    block_reduce(sq, bad, badb);
+    if (threadIdx.x == 0) {
+        Partial pt;
+        pt.sumsq = sq;
+        pt.bad = bad;
+        pt.bad_buckets = badb;
+        a.partials[blockIdx.x] = pt;
+    }
+}
+
+// Sum the per-workgroup partials in workgroup order and write the stats.
+__global__ void __launch_bounds__(kFinalizeBlock) k_finalize(const Partial* parts, int n,
+                                                            zero_stats* out) {
+    double sq = 0.0;
+    uint32_t bad = 0u, badb = 0u;
+    for (int i = threadIdx.x; i < n; i += kFinalizeBlock) {
+        const Partial pt = parts[i];
+        sq += pt.sumsq;
+        bad |= pt.bad;
+        badb += pt.bad_buckets;
+    }
+    block_reduce(sq, bad, badb);
+    if (threadIdx.x == 0) {
+        out->overflow = bad ? 1u : 0u;
+        out->bad_buckets = badb;
+        out->sumsq = sq;
+    }
+}
+
+// slot[i] = bf16(master[i])
+__global__ void __launch_bounds__(kBlock) k_cast_slot(const float* master, int64_t S,
+                                                     uint16_t* slot) {
+    const int64_t nq = S >> 2;
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x; q < nq; q += stride) {
+        const f32x4 x = ld(reinterpret_cast<const f32x4*>(master) + q);
+        u32x2 w;
+        w.x = f2bf(x.x) | (f2bf(x.y) << 16);
+        w.y = f2bf(x.z) | (f2bf(x.w) << 16);
+        st(reinterpret_cast<u32x2*>(slot) + q, w);
+    }
+    if (blockIdx.x == 0) {
+        const int64_t e = nq * 4 + threadIdx.x;
+        if (e < S) slot[e] = (uint16_t)f2bf(master[e]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+int grid_for(int64_t S, int64_t n_buckets) {
+    if (n_buckets > 0) return (int)(n_buckets < kGridMax ? n_buckets : kGridMax);
+    const int64_t per_trip = (int64_t)kRows * kBlock * kVec;
+    const int64_t trips = (S + per_trip - 1) / per_trip;
+    if (trips < 1) return 1;
+    return (int)(trips < kGridMax ? trips : kGridMax);
+}
+
+template <typename RT, bool BUCKETS>
+static void launch_typed(const StepDesc& d, const KParams& k, int grid, hipStream_t st) {
+    if (d.adam)
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, true, false>), dim3(grid), dim3(kBlock), 0, st, k);
+    else if (d.g_out)
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, true>), dim3(grid), dim3(kBlock), 0, st, k);
+    else
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, false>), dim3(grid), dim3(kBlock), 0, st, k);
+}
+
+hipError_t launch_step(const StepDesc& d, hipStream_t st) {
+    KParams k;
+    for (int j = 0; j < ZERO_MAX_REPLICAS; ++j) k.rep[j] = j < d.n_rep ? d.replicas[j] : nullptr;
+    k.n_rep = d.n_rep;
+    k.has_slot = d.slot != nullptr;
+    k.S = d.S;
+    k.buckets = d.buckets;
+    k.n_buckets = d.n_buckets;
+    k.p_in = d.p_in;
+    k.m_in = d.m_in;
+    k.v_in = d.v_in;
+    k.p_out = d.p_out;
+    k.m_out = d.m_out;
+    k.v_out = d.v_out;
+    k.slot = d.slot;
+    k.g_out = d.g_out;
+    k.partials = d.partials;
+    k.sc = d.sc;
+    const bool buckets = d.n_buckets > 0;
+    const int grid = grid_for(d.S, d.n_buckets);
+    if (d.ev_begin) {
+        hipError_t e = hipEventRecord(d.ev_begin, st);
+        if (e != hipSuccess) return e;
+    }
+    if (d.dtype == ZERO_BF16) {
+        if (buckets) launch_typed<uint16_t, true>(d, k, grid, st);
+        else launch_typed<uint16_t, false>(d, k, grid, st);
+    } else {
+        if (buckets) launch_typed<float, true>(d, k, grid, st);
+        else launch_typed<float, false>(d, k, grid, st);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (d.ev_end) {
+        e = hipEventRecord(d.ev_end, st);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kFinalizeBlock), 0, st,
+                       (const Partial*)d.partials, grid, d.stats);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t st) {
+    const int64_t nq = S >> 2;
+    int64_t blocks = (nq + kBlock - 1) / kBlock;
+    if (blocks < 1) blocks = 1;
+    if (blocks > kGridMax) blocks = kGridMax;
+    hipLaunchKernelGGL(k_cast_slot, dim3((unsigned)blocks), dim3(kBlock), 0, st, master, S, slot);
+    return hipGetLastError();
+}
+
+}  // namespace zk

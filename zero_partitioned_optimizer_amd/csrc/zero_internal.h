@@ -1,0 +1,62 @@
+// zero_internal.h -- internal interface between the C ABI layer (abi.cpp) and
+// the gfx950 kernels (step_kernels.hip). Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero.h"
+
+namespace zk {
+
+constexpr int kBlock = 256;         // threads per workgroup: 4 wave64s
+constexpr int kVec = 4;             // elements per lane per row (one quad)
+constexpr int kRows = 2;            // quads per lane per trip of the main loop
+constexpr int kGridMax = 2048;      // workgroups of the grid-stride step kernels
+constexpr int kFinalizeBlock = 256;
+
+// Per-workgroup partial result of the overflow flag and the squared norm.
+struct Partial {
+    double sumsq;
+    uint32_t bad;
+    uint32_t bad_buckets;
+};
+static_assert(sizeof(Partial) == 16, "partials are 16 bytes");
+
+// fp32 scalars of one update, each rounded once from double on the host.
+struct Scalars {
+    float inv;                      // 1 / (N * loss_scale)
+    float b1, b2, omb1, omb2;       // beta1, beta2, 1 - beta1, 1 - beta2
+    float bc1, bc2;                 // 1 - beta1^t, 1 - beta2^t
+    float lr, eps, decay;           // decay = 1 - lr * weight_decay
+};
+
+// What one launch of the step kernel does.
+struct StepDesc {
+    const void* const* replicas;    // host array of n_rep device pointers
+    int32_t n_rep;
+    zero_dtype dtype;
+    int64_t S;
+    const zero_bucket* buckets;     // device, or nullptr for the whole shard
+    int64_t n_buckets;
+    bool adam;                      // false: reduce only
+    const float* p_in;
+    const float* m_in;
+    const float* v_in;
+    float* p_out;
+    float* m_out;
+    float* v_out;
+    uint16_t* slot;                 // may be nullptr
+    float* g_out;                   // may be nullptr
+    Scalars sc;
+    zero_stats* stats;
+    Partial* partials;              // workspace, >= grid_for() entries
+    hipEvent_t ev_begin;            // optional, around the main kernel only
+    hipEvent_t ev_end;
+};
+
+int grid_for(int64_t S, int64_t n_buckets);
+hipError_t launch_step(const StepDesc& d, hipStream_t stream);
+hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t stream);
+
+}  // namespace zk

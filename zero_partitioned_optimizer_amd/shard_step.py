@@ -1,0 +1,126 @@
+"""ShardStep: one rank's ZeRO stage-1/2 optimizer step around libzero.
+
+Device work runs in libzero's kernels; this class only owns buffers (through
+torch) and applies the host commit rule:
+
+* the fused step reads the N resident gradient replicas and the committed state
+  (p, m, v "in"), and writes the candidate state (p, m, v "out") plus the bf16
+  slot, with the overflow flag and squared norm in a 16-byte stats record;
+* ``zero_commit_rule`` decides: a clean step swaps the in/out buffers and advances
+  t; an overflowed step keeps the in buffers, restores the slot from the
+  committed master copy and (dynamic scaling) halves the loss scale.
+
+The step and its data flow follow "[REQUEST] Direct Correspondence between
+Gradient and Optimizer States to Reduce Communication", "Problem"; mixed
+precision is named in "ZeRO Optimizer", "Hybrid Approaches".
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _binding as B
+
+
+class ShardStep:
+    def __init__(self, shard_S: int, n_replicas: int, grad_dtype: int, p0: torch.Tensor, *,
+                 lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+                 loss_scale: float = 1.0, dynamic: bool = False, min_loss_scale: float = 1.0,
+                 slot: Optional[torch.Tensor] = None, buckets: Optional[torch.Tensor] = None,
+                 n_buckets: int = 0):
+        dev = p0.device
+        S = int(shard_S)
+        assert p0.dtype == torch.float32 and p0.numel() == S and p0.is_contiguous()
+        self.S, self.N, self.grad_dtype = S, int(n_replicas), int(grad_dtype)
+        self.hyper = dict(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay)
+        self.p = [p0.clone(), torch.zeros_like(p0)]   # zeros: bucket steps skip padding
+        self.m = [torch.zeros_like(p0), torch.zeros_like(p0)]
+        self.v = [torch.zeros_like(p0), torch.zeros_like(p0)]
+        self.cur = 0
+        self.slot = slot if slot is not None else torch.empty(S, dtype=torch.int16, device=dev)
+        assert self.slot.numel() == S and self.slot.element_size() == 2
+        self.buckets, self.n_buckets = buckets, int(n_buckets)
+        self.stats = torch.zeros(16, dtype=torch.uint8, device=dev)
+        self.stats_host = torch.zeros(16, dtype=torch.uint8, pin_memory=True)
+        self.ws = torch.empty(B.zero_workspace_bytes(S), dtype=torch.uint8, device=dev)
+        self.state = B.zero_train_state(t=0, n_skipped=0, loss_scale=float(loss_scale),
+                                        min_loss_scale=float(min_loss_scale), dynamic=int(dynamic))
+        B.zero_gather_slot(self.p[0], S, self.slot)
+        self._args = [None, None]
+        self._args_key = None
+
+    # committed state
+    @property
+    def master(self) -> torch.Tensor:
+        return self.p[self.cur]
+
+    @property
+    def exp_avg(self) -> torch.Tensor:
+        return self.m[self.cur]
+
+    @property
+    def exp_avg_sq(self) -> torch.Tensor:
+        return self.v[self.cur]
+
+    @property
+    def t(self) -> int:
+        return int(self.state.t)
+
+    @property
+    def loss_scale(self) -> float:
+        return float(self.state.loss_scale)
+
+    def _args_for(self, replicas: Sequence[torch.Tensor]):
+        """The argument block for the current direction (in -> out). Two blocks are
+        built once per replica set and reused; only t, the loss scale and the
+        events change from step to step."""
+        key = tuple(r.data_ptr() for r in replicas)
+        if self._args_key != key:
+            self._args = [None, None]
+            self._args_key = key
+        i, o = self.cur, 1 - self.cur
+        a = self._args[i]
+        if a is None:
+            a = B.make_adam_args(replicas=list(replicas), grad_dtype=self.grad_dtype,
+                                 p_in=self.p[i], m_in=self.m[i], v_in=self.v[i], p_out=self.p[o],
+                                 m_out=self.m[o], v_out=self.v[o], slot=self.slot, shard_S=self.S,
+                                 buckets=self.buckets, n_buckets=self.n_buckets,
+                                 loss_scale=self.state.loss_scale, step_t=self.state.t + 1,
+                                 stats=self.stats, workspace=self.ws, **self.hyper)
+            self._args[i] = a
+        a.step_t = self.state.t + 1
+        a.loss_scale = self.state.loss_scale
+        return a
+
+    def launch(self, replicas: Sequence[torch.Tensor], stream=None, events=None) -> None:
+        """Enqueue the fused step (no synchronization). ``events`` = optional pair of
+        torch.cuda.Event recorded around the main kernel."""
+        a = self._args_for(replicas)
+        if events is not None:
+            a.event_begin = B._event(events[0])
+            a.event_end = B._event(events[1])
+        else:
+            a.event_begin = a.event_end = None
+        B.zero_adam_step(a, stream)
+
+    def read_stats(self, stream=None) -> B.zero_stats:
+        self.stats_host.copy_(self.stats, non_blocking=True)
+        (stream or torch.cuda.current_stream()).synchronize()
+        return B.zero_stats.from_buffer_copy(self.stats_host.numpy().tobytes())
+
+    def commit(self, st: B.zero_stats, stream=None) -> int:
+        verdict = B.zero_commit_rule(self.state, st)
+        if verdict == B.ZERO_COMMIT:
+            self.cur = 1 - self.cur
+        else:
+            B.zero_gather_slot(self.p[self.cur], self.S, self.slot, stream)
+        return verdict
+
+    def step(self, replicas: Sequence[torch.Tensor], stream=None, events=None):
+        """One full step: fused kernel, read the 16-byte stats, apply the commit rule."""
+        self.launch(replicas, stream, events)
+        st = self.read_stats(stream)
+        verdict = self.commit(st, stream)
+        return st, verdict
