@@ -90,6 +90,9 @@ def main() -> int:
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--bucket-elems", type=int, default=0,
                     help="launch over the layout's bucket table cut at this size (0: whole shard)")
+    ap.add_argument("--commit", default="device", choices=["device", "host"],
+                    help="device: commit kernel, no host round trip per step; host: read the "
+                         "stats back and apply the commit rule on the host every step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -134,9 +137,10 @@ def main() -> int:
         reps.append(buf.view(tdt))
     p0 = torch.empty(S, dtype=torch.float32, device=dev)
     W.device_fill_params(p0, w, covered, args.rank)
-    step = Z.ShardStep(S, w.N, gdt, p0, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                       weight_decay=w.wd, loss_scale=w.loss_scale, dynamic=w.dynamic_loss_scale,
-                       buckets=buckets_t, n_buckets=nb)
+    Step = Z.DeviceShardStep if args.commit == "device" else Z.ShardStep
+    step = Step(S, w.N, gdt, p0, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                weight_decay=w.wd, loss_scale=w.loss_scale, dynamic=w.dynamic_loss_scale,
+                buckets=buckets_t, n_buckets=nb)
     torch.cuda.synchronize()
     log("inputs resident; warmup", args.warmup)
 
@@ -148,11 +152,18 @@ def main() -> int:
     skipped = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(K):
-        st, verdict = step.step(reps, events=ev[k])
-        skipped += verdict == Z.ZERO_SKIP
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    if args.commit == "device":
+        for k in range(K):
+            step.step(reps, events=ev[k])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        skipped = int(step.state().n_skipped)
+    else:
+        for k in range(K):
+            st, verdict = step.step(reps, events=ev[k])
+            skipped += verdict == Z.ZERO_SKIP
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     kms = [a.elapsed_time(b) for a, b in ev]
     log(f"timed {K} steps in {elapsed:.4f} s; kernel mean {statistics.mean(kms) * 1e3:.1f} us, "
         f"median {statistics.median(kms) * 1e3:.1f} us, skipped {skipped}")
@@ -176,7 +187,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{w.name} shard, rank {args.rank} of N={w.N}", "shard_elems": S,
                    "n_replicas": w.N, "grad_dtype": w.grad_dtype, "state_dtype": "f32",
-                   "bytes_per_elem": bpe, "bucket_elems": args.bucket_elems},
+                   "bytes_per_elem": bpe, "bucket_elems": args.bucket_elems,
+                   "commit": args.commit},
         "step_gbps": S * bpe / (elapsed / K) / 1e9,
         "kernel_us_mean": kernel_s * 1e6,
         "kernel_us_median": statistics.median(kms) * 1e3,

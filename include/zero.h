@@ -283,6 +283,78 @@ enum { ZERO_COMMIT = 1, ZERO_SKIP = 2 };
 
 int zero_commit_rule(zero_train_state* state, const zero_stats* stats_host);
 
+/* ------------------------------------------------------------------------ */
+/* Device-resident step: commit on the GPU, no host round trip per step       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The committed-state record of one rank's shard, in device memory (88 bytes,
+ * 16-byte aligned, caller-owned). zero_train_step reads it to pick the current
+ * state set, t, the loss scale and beta^t, and its commit kernel updates it, so
+ * consecutive steps need no host synchronization (and can be graph-captured).
+ * The host may copy it back at any time after synchronizing the stream.
+ */
+typedef struct {
+    double beta1, beta2;           /* fixed for the life of the record */
+    double beta1_pow, beta2_pow;   /* beta^t of the committed t (t-fold products) */
+    double loss_scale;
+    double min_loss_scale;
+    double last_sumsq;             /* squared norm of the last step's averaged gradient */
+    int64_t t;                     /* committed updates */
+    int64_t n_skipped;             /* steps skipped on overflow */
+    uint32_t cur;                  /* 0/1: which state set holds the committed state */
+    uint32_t dynamic;              /* nonzero: halve the loss scale on overflow */
+    uint32_t last_overflow;
+    uint32_t reserved;
+} zero_device_state;
+
+/*
+ * Enqueue the initialisation of a device state record (a one-thread kernel, no
+ * memset): t = 0, beta^0 = 1, set 0 current. beta1, beta2 in [0, 1); loss_scale
+ * finite > 0; min_loss_scale in (0, loss_scale]. Errors: ZERO_E_INVAL,
+ * ZERO_E_ALIGN, ZERO_E_HIP.
+ */
+int zero_device_state_init(zero_device_state* state_dev, double beta1, double beta2,
+                           double loss_scale, double min_loss_scale, int32_t dynamic,
+                           void* stream);
+
+typedef struct {
+    const void* const* replicas;   /* host array of n_replicas device pointers, slot order */
+    int32_t n_replicas;
+    zero_dtype grad_dtype;
+    float* p[2];                   /* the two fp32 state sets, [shard_S] each */
+    float* m[2];
+    float* v[2];
+    uint16_t* slot_bf16;           /* this rank's slot, or NULL */
+    int64_t shard_S;
+    const zero_bucket* buckets_dev;
+    int64_t n_buckets;
+    double lr, eps, weight_decay;  /* may change from step to step; betas live in the record */
+    zero_device_state* state_dev;
+    zero_stats* stats_dev;
+    void* workspace_dev;
+    size_t ws_bytes;
+    void* event_begin;             /* optional hipEvent_t around the main kernel */
+    void* event_end;
+} zero_train_args;
+
+/*
+ * One whole step of this rank's shard with the commit on the device: the fused
+ * pass of zero_adam_step (fold in slot order, average and unscale, overflow flag
+ * and squared norm, Adam/AdamW, bf16 slot), reading set state->cur and writing
+ * the other set, then a commit kernel that applies the skip rule of
+ * zero_commit_rule to *state_dev (clean: t += 1 and the written set becomes
+ * current; overflow: nothing committed, slot restored from the current master,
+ * dynamic loss scale halved). Same arithmetic as zero_adam_step, bit for bit.
+ * Source of the step: "[REQUEST] Direct Correspondence between Gradient and
+ * Optimizer States to Reduce Communication", "Problem"; ring order as in
+ * GuanhuaWang's reply in "Why DeepSpeed ZeRO paper says reduce-scatter (or
+ * all-gather) has data movement of Psi elements?".
+ * The six state buffers, the slot, stats, workspace and record must not overlap
+ * each other or the replicas. Errors as for zero_adam_step.
+ */
+int zero_train_step(const zero_train_args* args, void* stream);
+
 /* Thread-local text for the last non-OK return on this thread ("" if none). */
 const char* zero_last_error(void);
 

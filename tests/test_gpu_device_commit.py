@@ -1,0 +1,147 @@
+"""GPU parity of the device-commit step (zero_train_step) against the oracle.
+
+The commit rule runs on the GPU: the fused kernel reads the committed-state
+record (current set, t, loss scale, beta^t) and a commit kernel applies the skip
+rule. These tests compare the committed state after every step with the
+oracle's multi-step rule (bit for bit), queue many steps with no host
+synchronization in between (an overflow injected mid-chain), and check that the
+device path equals the host-commit path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import NTHREADS, check_state, say, sumsq_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def layout_of(w, rank):
+    lay = oracle.Layout(w.numels, N=w.N, A=w.A, B=w.B)
+    return lay, [(int(s[2]), int(s[3])) for s in lay.segments(rank)]
+
+
+def bucket_table(Z, w, rank, bucket_elems):
+    h = Z.zero_layout_build(list(w.numels), w.N, w.A, w.B)
+    raw, nb = Z.zero_layout_buckets_raw(h, rank, bucket_elems)
+    Z.zero_layout_free(h)
+    return torch.frombuffer(bytearray(bytes(raw)[: 16 * nb]), dtype=torch.uint8).to("cuda"), nb
+
+
+def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None):
+    lay, covered = layout_of(w, rank)
+    S = lay.S
+    gdt = Z.ZERO_BF16 if w.grad_dtype == "bf16" else Z.ZERO_F32
+    p0 = W.host_params(w, S, covered, rank)
+    bt, nb = bucket_table(Z, w, rank, bucket_elems) if bucket_elems else (None, 0)
+    step = Z.DeviceShardStep(S, w.N, gdt, to_dev(p0), lr=w.lr, beta1=w.beta1, beta2=w.beta2,
+                             eps=w.eps, weight_decay=w.wd, loss_scale=w.loss_scale,
+                             dynamic=w.dynamic_loss_scale, buckets=bt, n_buckets=nb)
+    tr = oracle.Trainer(p0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
+                        oracle.f32_to_bf16(p0), loss_scale=w.loss_scale, dynamic=w.dynamic_loss_scale,
+                        nthreads=NTHREADS, **w.hyper())
+    flags = []
+    for s in range(w.steps if steps is None else steps):
+        say(f"device {w.name} rank={rank} step={s} buckets={nb}")
+        reps = W.host_replicas(w, S, covered, rank, s)
+        step.step([to_dev(r) for r in reps])
+        flag, sumsq = tr.step(reps)
+        flags.append(flag)
+        rec = step.state()
+        st = step.last_stats()
+        assert st.overflow == flag == rec.last_overflow and st.bad_buckets == 0
+        assert rec.t == tr.t and rec.loss_scale == tr.loss_scale
+        assert rec.n_skipped == sum(flags)
+        assert sumsq_close(st.sumsq, sumsq) and sumsq_close(rec.last_sumsq, sumsq)
+        P, M, V = step.committed()
+        check_state(f"device {w.name} r{rank} s{s}", to_host(P), to_host(M), to_host(V),
+                    to_host(step.slot), tr.p, tr.m, tr.v, tr.slot)
+    return flags
+
+
+def test_tiny_every_rank(Z):
+    w = W.get("tiny")
+    for rank in range(w.N):
+        assert run_device_protocol(Z, w, rank) == [0, 0, 0]
+
+
+@pytest.mark.parametrize("rank,bucket_elems", [(0, 0), (63, 0), (0, 4096), (31, 1000)])
+def test_ragged_injection(Z, rank, bucket_elems):
+    w = W.get("ragged")
+    lay, covered = layout_of(w, rank)
+    inj = W.injection(w, lay.S, covered, rank)
+    flags = run_device_protocol(Z, w, rank, bucket_elems)
+    assert flags == [1 if s == inj[0] else 0 for s in range(w.steps)]
+
+
+def test_gpt2_device_equals_host_commit(Z):
+    w = W.get("gpt2s")
+    lay, covered = layout_of(w, 0)
+    S = lay.S
+    p0 = to_dev(W.host_params(w, S, covered, 0))
+    kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.wd,
+              loss_scale=w.loss_scale)
+    hs = Z.ShardStep(S, w.N, Z.ZERO_BF16, p0, **kw)
+    ds = Z.DeviceShardStep(S, w.N, Z.ZERO_BF16, p0, **kw)
+    for s in range(3):
+        say(f"gpt2s device vs host step {s}")
+        dreps = [to_dev(r) for r in W.host_replicas(w, S, covered, 0, s)]
+        st_h, _ = hs.step(dreps)
+        ds.step(dreps)
+        torch.cuda.synchronize()
+        P, M, V = ds.committed()
+        assert torch.equal(P, hs.master) and torch.equal(M, hs.exp_avg) and torch.equal(V, hs.exp_avg_sq)
+        assert torch.equal(ds.slot, hs.slot)
+        assert ds.last_stats().sumsq == st_h.sumsq
+        assert ds.state().t == hs.t == s + 1
+
+
+def test_queued_chain_with_overflow(Z):
+    """20 steps enqueued back to back with no host synchronization; step 7 carries
+    a NaN and step 13 an +inf. The final state equals the oracle's trajectory."""
+    S, N, K = 300_007, 8, 20
+    rng = np.random.default_rng(77)
+    sets = []
+    for k in range(K):
+        reps = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * 1e-4 * 1024.0))
+                for _ in range(N)]
+        if k == 7:
+            reps[3][12345] = 0x7FC0
+        if k == 13:
+            reps[0][S - 1] = 0x7F80
+        sets.append(reps)
+    p0 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    hy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    step = Z.DeviceShardStep(S, N, Z.ZERO_BF16, to_dev(p0), weight_decay=0.01, loss_scale=1024.0,
+                             dynamic=True, **hy)
+    dsets = [[to_dev(r) for r in reps] for reps in sets]
+    torch.cuda.synchronize()
+    say("queued chain: enqueue 20 steps")
+    for k in range(K):
+        step.step(dsets[k])
+    tr = oracle.Trainer(p0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
+                        oracle.f32_to_bf16(p0), loss_scale=1024.0, dynamic=True, wd=0.01,
+                        nthreads=NTHREADS, **hy)
+    flags = [tr.step(reps)[0] for reps in sets]
+    assert flags == [1 if k in (7, 13) else 0 for k in range(K)]
+    rec = step.state()
+    assert rec.t == tr.t == K - 2 and rec.n_skipped == 2 and rec.loss_scale == tr.loss_scale == 256.0
+    P, M, V = step.committed()
+    check_state("queued chain", to_host(P), to_host(M), to_host(V), to_host(step.slot), tr.p, tr.m,
+                tr.v, tr.slot)
+
+
+def test_record_init_and_validation(Z):
+    rec = torch.zeros(128, dtype=torch.uint8, device="cuda")
+    Z.zero_device_state_init(rec, 0.8, 0.95, 512.0, 2.0, True)
+    r = Z.device_state_from_tensor(rec)
+    assert (r.beta1, r.beta2, r.beta1_pow, r.beta2_pow) == (0.8, 0.95, 1.0, 1.0)
+    assert (r.loss_scale, r.min_loss_scale, r.t, r.n_skipped, r.cur, r.dynamic) == (512.0, 2.0, 0, 0, 0, 1)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_device_state_init(rec, 1.0, 0.9, 1.0)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_device_state_init(rec[8:], 0.9, 0.9, 1.0)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_device_state_init(rec, 0.9, 0.9, 1.0, min_loss_scale=2.0)

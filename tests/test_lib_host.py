@@ -216,3 +216,32 @@ def test_commit_rule_matches_oracle_trainer(Z):
     st = Z.zero_train_state(t=0, n_skipped=0, loss_scale=4.0, min_loss_scale=1.0, dynamic=0)
     Z.zero_commit_rule(st, Z.zero_stats(overflow=1))
     assert st.loss_scale == 4.0
+
+
+def test_train_step_validation(Z):
+    FAKEREC = FAKE + 65536
+    base = dict(replicas=[FAKE + 45056], grad_dtype=1, p=(FAKE, FAKE + 4096), m=(FAKE + 8192, FAKE + 12288),
+                v=(FAKE + 16384, FAKE + 20480), slot=FAKE + 24576, shard_S=64, lr=1e-3, eps=1e-8,
+                weight_decay=0.0, state=FAKEREC, stats=FAKE + 28672, workspace=FAKE + 32768)
+    def call(**kw):
+        d = dict(base)
+        d.update(kw)
+        a = Z.make_train_args(**d)
+        a.ws_bytes = Z.zero_workspace_bytes(64)
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_train_step(a, stream=0)
+        return e.value.status
+    assert call(state=0) == -1
+    assert call(state=FAKEREC + 8) == -2
+    assert call(p=(FAKE, FAKE)) == -1                      # both sets alias
+    assert call(m=(FAKE + 8192, FAKE + 8192 + 64)) == -1   # partial overlap
+    assert call(slot=FAKE + 4096 + 32) == -1               # slot inside p[1]
+    assert call(replicas=[FAKE + 4096]) == -1              # replica overlaps p[1]
+    assert call(lr=-1.0) == -1
+    assert call(replicas=[]) == -3
+    assert call(p=(FAKE + 4, FAKE + 4096)) == -2
+    L = Z.lib()
+    assert L.zero_device_state_init(None, 0.9, 0.999, 1.0, 1.0, 0, None) == -1
+    assert L.zero_device_state_init(FAKEREC + 4, 0.9, 0.999, 1.0, 1.0, 0, None) == -2
+    assert L.zero_device_state_init(FAKEREC, 0.9, 1.5, 1.0, 1.0, 0, None) == -1
+    assert L.zero_device_state_init(FAKEREC, 0.9, 0.999, float("inf"), 1.0, 0, None) == -1

@@ -70,6 +70,22 @@ class zero_train_state(ctypes.Structure):
                 ("dynamic", i32), ("reserved", i32)]
 
 
+class zero_device_state(ctypes.Structure):
+    _fields_ = [("beta1", f64), ("beta2", f64), ("beta1_pow", f64), ("beta2_pow", f64),
+                ("loss_scale", f64), ("min_loss_scale", f64), ("last_sumsq", f64),
+                ("t", i64), ("n_skipped", i64), ("cur", u32), ("dynamic", u32),
+                ("last_overflow", u32), ("reserved", u32)]
+
+
+class zero_train_args(ctypes.Structure):
+    _fields_ = [("replicas", ctypes.POINTER(vp)), ("n_replicas", i32), ("grad_dtype", i32),
+                ("p", vp * 2), ("m", vp * 2), ("v", vp * 2), ("slot_bf16", vp), ("shard_S", i64),
+                ("buckets_dev", vp), ("n_buckets", i64), ("lr", f64), ("eps", f64),
+                ("weight_decay", f64), ("state_dev", vp), ("stats_dev", vp),
+                ("workspace_dev", vp), ("ws_bytes", sz), ("event_begin", vp), ("event_end", vp)]
+
+
+assert ctypes.sizeof(zero_device_state) == 88
 assert ctypes.sizeof(zero_bucket) == 16 and ctypes.sizeof(zero_stats) == 16
 assert ctypes.sizeof(zero_segment) == 32
 
@@ -101,6 +117,8 @@ def lib() -> ctypes.CDLL:
     L.zero_adam_step.argtypes = [P(zero_adam_args), vp]
     L.zero_gather_slot.argtypes = [vp, i64, vp, vp]
     L.zero_commit_rule.argtypes = [P(zero_train_state), P(zero_stats)]
+    L.zero_device_state_init.argtypes = [vp, f64, f64, f64, f64, i32, vp]
+    L.zero_train_step.argtypes = [P(zero_train_args), vp]
     L.zero_last_error.argtypes = []
     L.zero_last_error.restype = ctypes.c_char_p
     L.zero_version.argtypes = []
@@ -108,7 +126,8 @@ def lib() -> ctypes.CDLL:
     for name in ("zero_layout_build", "zero_layout_info_get", "zero_layout_offsets",
                  "zero_layout_segments", "zero_layout_buckets", "zero_layout_mem_values",
                  "zero_layout_mem_bytes", "zero_reduce_shard", "zero_adam_step",
-                 "zero_gather_slot", "zero_commit_rule"):
+                 "zero_gather_slot", "zero_commit_rule", "zero_device_state_init",
+                 "zero_train_step"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -281,6 +300,47 @@ def zero_gather_slot(master, shard_S: int, slot, stream=None) -> None:
 
 def zero_commit_rule(state: zero_train_state, stats_host: zero_stats) -> int:
     return _check(lib().zero_commit_rule(ctypes.byref(state), ctypes.byref(stats_host)))
+
+
+def zero_device_state_init(state, beta1: float, beta2: float, loss_scale: float,
+                           min_loss_scale: float = 1.0, dynamic: bool = False, stream=None) -> None:
+    _check(lib().zero_device_state_init(_addr(state), float(beta1), float(beta2), float(loss_scale),
+                                        float(min_loss_scale), int(bool(dynamic)), _stream(stream)))
+
+
+def make_train_args(*, replicas, grad_dtype: int, p, m, v, slot=None, shard_S: int, buckets=None,
+                    n_buckets: int = 0, lr: float, eps: float, weight_decay: float, state, stats,
+                    workspace, event_begin=None, event_end=None) -> zero_train_args:
+    a = zero_train_args()
+    table = _replica_table(replicas)
+    a.replicas = ctypes.cast(table, ctypes.POINTER(vp))
+    a.n_replicas = len(replicas)
+    a.grad_dtype = int(grad_dtype)
+    for name, pair in (("p", p), ("m", m), ("v", v)):
+        setattr(a, name, (vp * 2)(_addr(pair[0]) or None, _addr(pair[1]) or None))
+    a.slot_bf16 = _addr(slot) or None
+    a.shard_S = int(shard_S)
+    a.buckets_dev = _addr(buckets) or None
+    a.n_buckets = int(n_buckets)
+    a.lr, a.eps, a.weight_decay = float(lr), float(eps), float(weight_decay)
+    a.state_dev = _addr(state) or None
+    a.stats_dev = _addr(stats) or None
+    a.workspace_dev = _addr(workspace) or None
+    a.ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    a.event_begin = _event(event_begin)
+    a.event_end = _event(event_end)
+    a._keep = [table]
+    return a
+
+
+def zero_train_step(args: zero_train_args, stream=None) -> None:
+    _check(lib().zero_train_step(ctypes.byref(args), _stream(stream)))
+
+
+def device_state_from_tensor(t) -> zero_device_state:
+    """Read a device zero_device_state (uint8 tensor of 88+ bytes) to the host (synchronizes)."""
+    raw = bytes(t.detach().to("cpu").numpy().tobytes())[: ctypes.sizeof(zero_device_state)]
+    return zero_device_state.from_buffer_copy(raw)
 
 
 def zero_last_error() -> str:

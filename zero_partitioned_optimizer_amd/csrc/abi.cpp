@@ -328,6 +328,122 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
     return hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
 }
 
+int zero_device_state_init(zero_device_state* state_dev, double beta1, double beta2,
+                           double loss_scale, double min_loss_scale, int32_t dynamic,
+                           void* stream) {
+    static const char* fn = "zero_device_state_init";
+    if (!state_dev) {
+        set_error("%s: state_dev is NULL", fn);
+        return ZERO_E_INVAL;
+    }
+    if (!aligned16(state_dev)) {
+        set_error("%s: state_dev is not 16-byte aligned", fn);
+        return ZERO_E_ALIGN;
+    }
+    if (!finite_in(beta1, 0.0, 1.0) || !finite_in(beta2, 0.0, 1.0) ||
+        !(isfinite(loss_scale) && loss_scale > 0) ||
+        !(isfinite(min_loss_scale) && min_loss_scale > 0 && min_loss_scale <= loss_scale)) {
+        set_error("%s: beta1=%g beta2=%g loss_scale=%g min_loss_scale=%g out of domain", fn, beta1,
+                  beta2, loss_scale, min_loss_scale);
+        return ZERO_E_INVAL;
+    }
+    return hip_status(zk::launch_state_init(state_dev, beta1, beta2, loss_scale, min_loss_scale,
+                                            dynamic ? 1u : 0u, static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+int zero_train_step(const zero_train_args* args, void* stream) {
+    static const char* fn = "zero_train_step";
+    if (!args) {
+        set_error("%s: args is NULL", fn);
+        return ZERO_E_INVAL;
+    }
+    const zero_train_args& a = *args;
+    const int64_t S = a.shard_S;
+    int rc = check_common(fn, S, a.buckets_dev, a.n_buckets, a.stats_dev, a.workspace_dev, a.ws_bytes);
+    if (rc) return rc;
+    rc = check_replicas(fn, a.replicas, a.n_replicas, a.grad_dtype, S);
+    if (rc) return rc;
+    if (!a.state_dev) {
+        set_error("%s: state_dev is NULL", fn);
+        return ZERO_E_INVAL;
+    }
+    if (!aligned16(a.state_dev)) {
+        set_error("%s: state_dev is not 16-byte aligned", fn);
+        return ZERO_E_ALIGN;
+    }
+    const float* sets[6] = {a.p[0], a.p[1], a.m[0], a.m[1], a.v[0], a.v[1]};
+    for (const float* p : sets) {
+        if (!p && S > 0) {
+            set_error("%s: a state buffer is NULL", fn);
+            return ZERO_E_INVAL;
+        }
+        if (!aligned16(p)) {
+            set_error("%s: a state buffer is not 16-byte aligned", fn);
+            return ZERO_E_ALIGN;
+        }
+    }
+    if (a.slot_bf16 && !aligned16(a.slot_bf16)) {
+        set_error("%s: slot_bf16 is not 16-byte aligned", fn);
+        return ZERO_E_ALIGN;
+    }
+    if (!(isfinite(a.lr) && a.lr >= 0) || !(isfinite(a.eps) && a.eps >= 0) ||
+        !(isfinite(a.weight_decay) && a.weight_decay >= 0)) {
+        set_error("%s: lr=%g eps=%g weight_decay=%g out of domain", fn, a.lr, a.eps, a.weight_decay);
+        return ZERO_E_INVAL;
+    }
+    const int64_t b4 = 4 * S;
+    const Span bufs[] = {span("p[0]", a.p[0], b4), span("p[1]", a.p[1], b4),
+                         span("m[0]", a.m[0], b4), span("m[1]", a.m[1], b4),
+                         span("v[0]", a.v[0], b4), span("v[1]", a.v[1], b4),
+                         span("slot", a.slot_bf16, a.slot_bf16 ? 2 * S : 0),
+                         span("stats", a.stats_dev, 16),
+                         span("workspace", a.workspace_dev, (int64_t)a.ws_bytes),
+                         span("state", a.state_dev, (int64_t)sizeof(zero_device_state))};
+    const int nb = 10;
+    for (int i = 0; i < nb; ++i) {
+        for (int k = i + 1; k < nb; ++k)
+            if (overlap(bufs[i], bufs[k])) {
+                set_error("%s: buffers %s and %s overlap", fn, bufs[i].name, bufs[k].name);
+                return ZERO_E_INVAL;
+            }
+        const int64_t gb = a.grad_dtype == ZERO_BF16 ? 2 : 4;
+        for (int32_t j = 0; j < a.n_replicas; ++j)
+            if (overlap(bufs[i], span("replica", a.replicas[j], gb * S))) {
+                set_error("%s: %s overlaps replicas[%d]", fn, bufs[i].name, (int)j);
+                return ZERO_E_INVAL;
+            }
+        if (a.n_buckets > 0 && overlap(bufs[i], span("buckets", a.buckets_dev, 16 * a.n_buckets))) {
+            set_error("%s: %s overlaps the bucket table", fn, bufs[i].name);
+            return ZERO_E_INVAL;
+        }
+    }
+    zk::StepDesc d{};
+    d.replicas = a.replicas;
+    d.n_rep = a.n_replicas;
+    d.dtype = a.grad_dtype;
+    d.S = S;
+    d.buckets = a.n_buckets > 0 ? a.buckets_dev : nullptr;
+    d.n_buckets = a.n_buckets;
+    d.adam = true;
+    for (int i = 0; i < 2; ++i) {
+        d.set_p[i] = a.p[i];
+        d.set_m[i] = a.m[i];
+        d.set_v[i] = a.v[i];
+    }
+    d.ctrl = a.state_dev;
+    d.slot = a.slot_bf16;
+    d.sc = zk::Scalars{};
+    d.sc.lr = (float)a.lr;
+    d.sc.eps = (float)a.eps;
+    d.sc.decay = (float)(1.0 - a.lr * a.weight_decay);
+    d.stats = a.stats_dev;
+    d.partials = static_cast<zk::Partial*>(a.workspace_dev);
+    d.ev_begin = static_cast<hipEvent_t>(a.event_begin);
+    d.ev_end = static_cast<hipEvent_t>(a.event_end);
+    return hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
+}
+
 int zero_gather_slot(const float* master_dev, int64_t shard_S, uint16_t* slot_bf16_dev,
                      void* stream) {
     static const char* fn = "zero_gather_slot";

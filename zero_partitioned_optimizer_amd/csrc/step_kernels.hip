@@ -35,6 +35,14 @@
 #ifndef ZERO_NT
 #define ZERO_NT 1
 #endif
+#ifndef ZERO_WAVES_PER_EU
+#define ZERO_WAVES_PER_EU 0
+#endif
+#if ZERO_WAVES_PER_EU > 0
+#define ZERO_STEP_BOUNDS __launch_bounds__(kBlock, ZERO_WAVES_PER_EU)
+#else
+#define ZERO_STEP_BOUNDS __launch_bounds__(kBlock)
+#endif
 
 namespace zk {
 
@@ -54,10 +62,25 @@ struct KParams {
     float* p_out;
     float* m_out;
     float* v_out;
+    float* set_p[2];                        // device-commit path: both state sets
+    float* set_m[2];
+    float* set_v[2];
+    const zero_device_state* ctrl;          // device-commit path: committed t, scale, set
     uint16_t* slot;
     float* g_out;
     Partial* partials;
     Scalars sc;
+};
+
+// What one workgroup works with: the update's scalars and the in/out state.
+struct Res {
+    Scalars sc;
+    const float* p_in;
+    const float* m_in;
+    const float* v_in;
+    float* p_out;
+    float* m_out;
+    float* v_out;
 };
 
 // ---------------------------------------------------------------------------
@@ -194,18 +217,56 @@ __device__ __forceinline__ void fold(const KParams& a, int64_t q0, int64_t qs, f
     }
 }
 
+// Host-commit launches carry everything in the kernel arguments. Device-commit
+// launches read the committed state's record: which state set is current, the
+// loss scale and beta^t; each workgroup derives the update's scalars from it
+// with the same double operations, rounded once to fp32, that the host uses.
+template <bool CTRL>
+__device__ __forceinline__ Res resolve(const KParams& a) {
+    Res r;
+    r.sc = a.sc;
+    if constexpr (!CTRL) {
+        r.p_in = a.p_in;
+        r.m_in = a.m_in;
+        r.v_in = a.v_in;
+        r.p_out = a.p_out;
+        r.m_out = a.m_out;
+        r.v_out = a.v_out;
+    } else {
+        const zero_device_state* c = a.ctrl;
+        const uint32_t cur = c->cur & 1u, nxt = cur ^ 1u;
+        const double b1 = c->beta1, b2 = c->beta2;
+        const double pow1 = c->beta1_pow * b1;      // beta^(t+1), one more factor of the product
+        const double pow2 = c->beta2_pow * b2;
+        r.sc.inv = (float)(1.0 / ((double)a.n_rep * c->loss_scale));
+        r.sc.b1 = (float)b1;
+        r.sc.b2 = (float)b2;
+        r.sc.omb1 = (float)(1.0 - b1);
+        r.sc.omb2 = (float)(1.0 - b2);
+        r.sc.bc1 = (float)(1.0 - pow1);
+        r.sc.bc2 = (float)(1.0 - pow2);
+        r.p_in = a.set_p[cur];
+        r.m_in = a.set_m[cur];
+        r.v_in = a.set_v[cur];
+        r.p_out = a.set_p[nxt];
+        r.m_out = a.set_m[nxt];
+        r.v_out = a.set_v[nxt];
+    }
+    return r;
+}
+
 // ROWS quads at q0, q0 + qs, ...: the whole step for 4*ROWS elements of this lane.
 template <typename RT, bool ADAM, bool WRITE_G, int ROWS>
-__device__ __forceinline__ void quads(const KParams& a, int64_t q0, int64_t qs, double& sq,
-                                      uint32_t& bad) {
+__device__ __forceinline__ void quads(const KParams& a, const Res& rs, int64_t q0, int64_t qs,
+                                      double& sq, uint32_t& bad) {
     f32x4 p[ROWS], m[ROWS], v[ROWS];
     if constexpr (ADAM) {
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
             const int64_t q = q0 + r * qs;
-            p[r] = ld(reinterpret_cast<const f32x4*>(a.p_in) + q);
-            m[r] = ld(reinterpret_cast<const f32x4*>(a.m_in) + q);
-            v[r] = ld(reinterpret_cast<const f32x4*>(a.v_in) + q);
+            p[r] = ld(reinterpret_cast<const f32x4*>(rs.p_in) + q);
+            m[r] = ld(reinterpret_cast<const f32x4*>(rs.m_in) + q);
+            v[r] = ld(reinterpret_cast<const f32x4*>(rs.v_in) + q);
         }
     }
     f32x4 acc[ROWS];
@@ -213,7 +274,7 @@ __device__ __forceinline__ void quads(const KParams& a, int64_t q0, int64_t qs, 
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
         const int64_t q = q0 + r * qs;
-        f32x4 g = acc[r] * a.sc.inv;
+        f32x4 g = acc[r] * rs.sc.inv;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             bad |= nonfinite(g[c]) ? 1u : 0u;
@@ -226,14 +287,14 @@ __device__ __forceinline__ void quads(const KParams& a, int64_t q0, int64_t qs, 
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 float x, y, z;
-                adam1(g[c], p[r][c], m[r][c], v[r][c], a.sc, x, y, z);
+                adam1(g[c], p[r][c], m[r][c], v[r][c], rs.sc, x, y, z);
                 pn[c] = x;
                 m1[c] = y;
                 v1[c] = z;
             }
-            st(reinterpret_cast<f32x4*>(a.p_out) + q, pn);
-            st(reinterpret_cast<f32x4*>(a.m_out) + q, m1);
-            st(reinterpret_cast<f32x4*>(a.v_out) + q, v1);
+            st(reinterpret_cast<f32x4*>(rs.p_out) + q, pn);
+            st(reinterpret_cast<f32x4*>(rs.m_out) + q, m1);
+            st(reinterpret_cast<f32x4*>(rs.v_out) + q, v1);
             if (a.has_slot) {
                 u32x2 w;
                 w.x = f2bf(pn.x) | (f2bf(pn.y) << 16);
@@ -246,41 +307,42 @@ __device__ __forceinline__ void quads(const KParams& a, int64_t q0, int64_t qs, 
 
 // One element, for bucket edges and the shard tail.
 template <typename RT, bool ADAM, bool WRITE_G>
-__device__ __forceinline__ void one_elem(const KParams& a, int64_t e, double& sq, uint32_t& bad) {
+__device__ __forceinline__ void one_elem(const KParams& a, const Res& rs, int64_t e, double& sq,
+                                         uint32_t& bad) {
     float acc = Quad<RT>::one(a.rep[0], e);
     for (int j = 1; j < a.n_rep; ++j) acc = acc + Quad<RT>::one(a.rep[j], e);
-    const float g = acc * a.sc.inv;
+    const float g = acc * rs.sc.inv;
     bad |= nonfinite(g) ? 1u : 0u;
     const double gd = (double)g;
     sq += gd * gd;
     if constexpr (WRITE_G) a.g_out[e] = g;
     if constexpr (ADAM) {
         float pn, m1, v1;
-        adam1(g, a.p_in[e], a.m_in[e], a.v_in[e], a.sc, pn, m1, v1);
-        a.p_out[e] = pn;
-        a.m_out[e] = m1;
-        a.v_out[e] = v1;
+        adam1(g, rs.p_in[e], rs.m_in[e], rs.v_in[e], rs.sc, pn, m1, v1);
+        rs.p_out[e] = pn;
+        rs.m_out[e] = m1;
+        rs.v_out[e] = v1;
         if (a.has_slot) a.slot[e] = (uint16_t)f2bf(pn);
     }
 }
 
 // All elements of [lo, hi) by the threads of one workgroup.
 template <typename RT, bool ADAM, bool WRITE_G>
-__device__ __forceinline__ void range(const KParams& a, int64_t lo, int64_t hi, double& sq,
-                                      uint32_t& bad) {
+__device__ __forceinline__ void range(const KParams& a, const Res& rs, int64_t lo, int64_t hi,
+                                      double& sq, uint32_t& bad) {
     const int tid = threadIdx.x;
     const int64_t qa = (lo + 3) >> 2;       // first whole quad
     const int64_t qb = hi >> 2;             // one past the last whole quad
     if (qa >= qb) {
-        for (int64_t e = lo + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, e, sq, bad);
+        for (int64_t e = lo + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
         return;
     }
-    for (int64_t e = lo + tid; e < qa * 4; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, e, sq, bad);
+    for (int64_t e = lo + tid; e < qa * 4; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
     int64_t q = qa + tid;
     for (; q + (kRows - 1) * kBlock < qb; q += kRows * kBlock)
-        quads<RT, ADAM, WRITE_G, kRows>(a, q, kBlock, sq, bad);
-    for (; q < qb; q += kBlock) quads<RT, ADAM, WRITE_G, 1>(a, q, 0, sq, bad);
-    for (int64_t e = qb * 4 + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, e, sq, bad);
+        quads<RT, ADAM, WRITE_G, kRows>(a, rs, q, kBlock, sq, bad);
+    for (; q < qb; q += kBlock) quads<RT, ADAM, WRITE_G, 1>(a, rs, q, 0, sq, bad);
+    for (int64_t e = qb * 4 + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
 }
 
 // Wave64 shuffles, then LDS across the workgroup's waves, in a fixed order.
@@ -321,8 +383,9 @@ __device__ __forceinline__ void block_reduce(double& sq, uint32_t& bad, uint32_t
 // kernels
 // ---------------------------------------------------------------------------
 
-template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G>
-__global__ void __launch_bounds__(kBlock) k_step(const KParams a) {
+template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL>
+__global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
+    const Res rs = resolve<CTRL>(a);
     double sq = 0.0;
     uint32_t bad = 0u, badb = 0u;
     if constexpr (!BUCKETS) {
@@ -330,13 +393,13 @@ __global__ void __launch_bounds__(kBlock) k_step(const KParams a) {
         const int64_t per_trip = (int64_t)kRows * kBlock;
         const int64_t ntrips = nq / per_trip;
         for (int64_t trip = blockIdx.x; trip < ntrips; trip += gridDim.x)
-            quads<RT, ADAM, WRITE_G, kRows>(a, trip * per_trip + threadIdx.x, kBlock, sq, bad);
+            quads<RT, ADAM, WRITE_G, kRows>(a, rs, trip * per_trip + threadIdx.x, kBlock, sq, bad);
         // whole quads after the last full trip, and the last S % 4 elements
         if ((int64_t)blockIdx.x == ntrips % gridDim.x) {
             for (int64_t q = ntrips * per_trip + threadIdx.x; q < nq; q += kBlock)
-                quads<RT, ADAM, WRITE_G, 1>(a, q, 0, sq, bad);
+                quads<RT, ADAM, WRITE_G, 1>(a, rs, q, 0, sq, bad);
             const int64_t e = nq * 4 + threadIdx.x;
-            if (e < a.S) one_elem<RT, ADAM, WRITE_G>(a, e, sq, bad);
+            if (e < a.S) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
         }
     } else {
         for (int64_t b = blockIdx.x; b < a.n_buckets; b += gridDim.x) {
@@ -346,7 +409,7 @@ __global__ void __launch_bounds__(kBlock) k_step(const KParams a) {
                 if (threadIdx.x == 0) badb += 1u;
                 continue;
             }
-            range<RT, ADAM, WRITE_G>(a, lo, lo + len, sq, bad);
+            range<RT, ADAM, WRITE_G>(a, rs, lo, lo + len, sq, bad);
         }
     }
     block_reduce(sq, bad, badb);
@@ -378,9 +441,8 @@ __global__ void __launch_bounds__(kFinalizeBlock) k_finalize(const Partial* part
     }
 }
 
-// slot[i] = bf16(master[i])
-__global__ void __launch_bounds__(kBlock) k_cast_slot(const float* master, int64_t S,
-                                                     uint16_t* slot) {
+// slot[i] = bf16(master[i]) over quads [0, S/4) by the whole grid, tail by workgroup 0.
+__device__ __forceinline__ void cast_range(const float* master, int64_t S, uint16_t* slot) {
     const int64_t nq = S >> 2;
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x; q < nq; q += stride) {
@@ -396,6 +458,76 @@ __global__ void __launch_bounds__(kBlock) k_cast_slot(const float* master, int64
     }
 }
 
+__global__ void __launch_bounds__(kBlock) k_cast_slot(const float* master, int64_t S,
+                                                     uint16_t* slot) {
+    cast_range(master, S, slot);
+}
+
+// Device-side commit of a train step. Every workgroup folds the step kernel's
+// partials into the verdict; on overflow the grid restores the slot from the
+// committed master (the current set, which a skipped step leaves current).
+// Workgroup 0 writes the stats and the new committed-state record:
+//   clean:    t += 1, beta^t *= beta, the out set becomes current;
+//   overflow: skipped += 1, a dynamic loss scale halves (not below its floor).
+// Only an overflowed step reads `cur` outside workgroup 0, and such a step does
+// not change it, so the grid never races on the record.
+__global__ void __launch_bounds__(kBlock) k_commit(const Partial* parts, int n, zero_stats* stats,
+                                                  zero_device_state* ctrl, const float* set_p0,
+                                                  const float* set_p1, uint16_t* slot, int64_t S) {
+    double sq = 0.0;
+    uint32_t bad = 0u, badb = 0u;
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        const Partial pt = parts[i];
+        sq += pt.sumsq;
+        bad |= pt.bad;
+        badb += pt.bad_buckets;
+    }
+    block_reduce(sq, bad, badb);
+    __shared__ uint32_t s_bad;
+    if (threadIdx.x == 0) s_bad = bad;
+    __syncthreads();
+    const bool overflow = s_bad != 0u;
+    if (overflow && slot) cast_range((ctrl->cur & 1u) ? set_p1 : set_p0, S, slot);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        stats->overflow = overflow ? 1u : 0u;
+        stats->bad_buckets = badb;
+        stats->sumsq = sq;
+        ctrl->last_overflow = overflow ? 1u : 0u;
+        ctrl->last_sumsq = sq;
+        if (!overflow) {
+            ctrl->t = ctrl->t + 1;
+            ctrl->beta1_pow = ctrl->beta1_pow * ctrl->beta1;
+            ctrl->beta2_pow = ctrl->beta2_pow * ctrl->beta2;
+            ctrl->cur = (ctrl->cur & 1u) ^ 1u;
+        } else {
+            ctrl->n_skipped = ctrl->n_skipped + 1;
+            if (ctrl->dynamic) {
+                const double half = ctrl->loss_scale / 2.0;
+                ctrl->loss_scale = half > ctrl->min_loss_scale ? half : ctrl->min_loss_scale;
+            }
+        }
+    }
+}
+
+__global__ void k_state_init(zero_device_state* s, double beta1, double beta2, double loss_scale,
+                             double min_loss_scale, uint32_t dynamic) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        s->beta1 = beta1;
+        s->beta2 = beta2;
+        s->beta1_pow = 1.0;
+        s->beta2_pow = 1.0;
+        s->loss_scale = loss_scale;
+        s->min_loss_scale = min_loss_scale;
+        s->last_sumsq = 0.0;
+        s->t = 0;
+        s->n_skipped = 0;
+        s->cur = 0u;
+        s->dynamic = dynamic;
+        s->last_overflow = 0u;
+        s->reserved = 0u;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -408,14 +540,24 @@ int grid_for(int64_t S, int64_t n_buckets) {
     return (int)(trips < kGridMax ? trips : kGridMax);
 }
 
+static int grid_stream(int64_t S) {
+    const int64_t per = (int64_t)kBlock * kVec * 4;
+    int64_t g = (S + per - 1) / per;
+    if (g < 1) g = 1;
+    if (g > kCommitGrid) g = kCommitGrid;
+    return (int)g;
+}
+
 template <typename RT, bool BUCKETS>
 static void launch_typed(const StepDesc& d, const KParams& k, int grid, hipStream_t st) {
-    if (d.adam)
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, true, false>), dim3(grid), dim3(kBlock), 0, st, k);
+    if (d.ctrl)
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, true, false, true>), dim3(grid), dim3(kBlock), 0, st, k);
+    else if (d.adam)
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, true, false, false>), dim3(grid), dim3(kBlock), 0, st, k);
     else if (d.g_out)
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, true>), dim3(grid), dim3(kBlock), 0, st, k);
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, true, false>), dim3(grid), dim3(kBlock), 0, st, k);
     else
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, false>), dim3(grid), dim3(kBlock), 0, st, k);
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, false, false>), dim3(grid), dim3(kBlock), 0, st, k);
 }
 
 hipError_t launch_step(const StepDesc& d, hipStream_t st) {
@@ -432,6 +574,12 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     k.p_out = d.p_out;
     k.m_out = d.m_out;
     k.v_out = d.v_out;
+    for (int i = 0; i < 2; ++i) {
+        k.set_p[i] = d.set_p[i];
+        k.set_m[i] = d.set_m[i];
+        k.set_v[i] = d.set_v[i];
+    }
+    k.ctrl = d.ctrl;
     k.slot = d.slot;
     k.g_out = d.g_out;
     k.partials = d.partials;
@@ -455,17 +603,26 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
         e = hipEventRecord(d.ev_end, st);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kFinalizeBlock), 0, st,
-                       (const Partial*)d.partials, grid, d.stats);
+    if (d.ctrl) {
+        hipLaunchKernelGGL(k_commit, dim3(grid_stream(d.S)), dim3(kBlock), 0, st,
+                           (const Partial*)d.partials, grid, d.stats, d.ctrl,
+                           (const float*)d.set_p[0], (const float*)d.set_p[1], d.slot, d.S);
+    } else {
+        hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kFinalizeBlock), 0, st,
+                           (const Partial*)d.partials, grid, d.stats);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t st) {
-    const int64_t nq = S >> 2;
-    int64_t blocks = (nq + kBlock - 1) / kBlock;
-    if (blocks < 1) blocks = 1;
-    if (blocks > kGridMax) blocks = kGridMax;
-    hipLaunchKernelGGL(k_cast_slot, dim3((unsigned)blocks), dim3(kBlock), 0, st, master, S, slot);
+    hipLaunchKernelGGL(k_cast_slot, dim3(grid_stream(S)), dim3(kBlock), 0, st, master, S, slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_init(zero_device_state* s, double beta1, double beta2, double loss_scale,
+                             double min_loss_scale, uint32_t dynamic, hipStream_t st) {
+    hipLaunchKernelGGL(k_state_init, dim3(1), dim3(64), 0, st, s, beta1, beta2, loss_scale,
+                       min_loss_scale, dynamic);
     return hipGetLastError();
 }
 

@@ -9,10 +9,18 @@
 
 namespace zk {
 
+#ifndef ZERO_ROWS
+#define ZERO_ROWS 2
+#endif
+#ifndef ZERO_GRID_MAX
+#define ZERO_GRID_MAX 2048
+#endif
+
 constexpr int kBlock = 256;         // threads per workgroup: 4 wave64s
 constexpr int kVec = 4;             // elements per lane per row (one quad)
-constexpr int kRows = 2;            // quads per lane per trip of the main loop
-constexpr int kGridMax = 2048;      // workgroups of the grid-stride step kernels
+constexpr int kRows = ZERO_ROWS;    // quads per lane per trip of the main loop
+constexpr int kGridMax = ZERO_GRID_MAX;  // workgroups of the grid-stride step kernel
+constexpr int kCommitGrid = 512;    // workgroups of the commit / cast kernels
 constexpr int kFinalizeBlock = 256;
 
 // Per-workgroup partial result of the overflow flag and the squared norm.
@@ -49,6 +57,10 @@ struct StepDesc {
     uint16_t* slot;                 // may be nullptr
     float* g_out;                   // may be nullptr
     Scalars sc;
+    float* set_p[2];                // device-commit path: both state sets
+    float* set_m[2];
+    float* set_v[2];
+    zero_device_state* ctrl;        // device-commit path, else nullptr
     zero_stats* stats;
     Partial* partials;              // workspace, >= grid_for() entries
     hipEvent_t ev_begin;            // optional, around the main kernel only
@@ -58,5 +70,7 @@ struct StepDesc {
 int grid_for(int64_t S, int64_t n_buckets);
 hipError_t launch_step(const StepDesc& d, hipStream_t stream);
 hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t stream);
+hipError_t launch_state_init(zero_device_state* s, double beta1, double beta2, double loss_scale,
+                             double min_loss_scale, uint32_t dynamic, hipStream_t stream);
 
 }  // namespace zk

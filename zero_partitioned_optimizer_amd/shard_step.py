@@ -124,3 +124,70 @@ class ShardStep:
         st = self.read_stats(stream)
         verdict = self.commit(st, stream)
         return st, verdict
+
+
+class DeviceShardStep:
+    """The same step with the commit on the device (``zero_train_step``): the fused
+    kernel reads the committed-state record, and a commit kernel applies the skip
+    rule to it, so steps queue back to back with no host synchronization. The host
+    reads the record (t, loss scale, current set) only when it wants to."""
+
+    def __init__(self, shard_S: int, n_replicas: int, grad_dtype: int, p0: torch.Tensor, *,
+                 lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+                 loss_scale: float = 1.0, dynamic: bool = False, min_loss_scale: float = 1.0,
+                 slot: Optional[torch.Tensor] = None, buckets: Optional[torch.Tensor] = None,
+                 n_buckets: int = 0):
+        dev = p0.device
+        S = int(shard_S)
+        assert p0.dtype == torch.float32 and p0.numel() == S and p0.is_contiguous()
+        self.S, self.N, self.grad_dtype = S, int(n_replicas), int(grad_dtype)
+        self.lr, self.eps, self.weight_decay = float(lr), float(eps), float(weight_decay)
+        self.p = [p0.clone(), torch.zeros_like(p0)]
+        self.m = [torch.zeros_like(p0), torch.zeros_like(p0)]
+        self.v = [torch.zeros_like(p0), torch.zeros_like(p0)]
+        self.slot = slot if slot is not None else torch.empty(S, dtype=torch.int16, device=dev)
+        assert self.slot.numel() == S and self.slot.element_size() == 2
+        self.buckets, self.n_buckets = buckets, int(n_buckets)
+        self.stats = torch.zeros(16, dtype=torch.uint8, device=dev)
+        self.record = torch.zeros(128, dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(B.zero_workspace_bytes(S), dtype=torch.uint8, device=dev)
+        B.zero_device_state_init(self.record, beta1, beta2, loss_scale, min_loss_scale, dynamic)
+        B.zero_gather_slot(self.p[0], S, self.slot)
+        self._args = None
+        self._args_key = None
+
+    def _args_for(self, replicas):
+        key = tuple(r.data_ptr() for r in replicas)
+        if self._args_key != key:
+            self._args = B.make_train_args(replicas=list(replicas), grad_dtype=self.grad_dtype,
+                                           p=self.p, m=self.m, v=self.v, slot=self.slot,
+                                           shard_S=self.S, buckets=self.buckets,
+                                           n_buckets=self.n_buckets, lr=self.lr, eps=self.eps,
+                                           weight_decay=self.weight_decay, state=self.record,
+                                           stats=self.stats, workspace=self.ws)
+            self._args_key = key
+        a = self._args
+        a.lr, a.eps, a.weight_decay = self.lr, self.eps, self.weight_decay
+        return a
+
+    def step(self, replicas: Sequence[torch.Tensor], stream=None, events=None) -> None:
+        """Enqueue one whole step (fused kernel + device commit); no synchronization."""
+        a = self._args_for(replicas)
+        if events is not None:
+            a.event_begin = B._event(events[0])
+            a.event_end = B._event(events[1])
+        else:
+            a.event_begin = a.event_end = None
+        B.zero_train_step(a, stream)
+
+    def state(self) -> B.zero_device_state:
+        """Copy the committed-state record back (synchronizes)."""
+        return B.device_state_from_tensor(self.record)
+
+    def last_stats(self) -> B.zero_stats:
+        return B.stats_from_tensor(self.stats)
+
+    def committed(self):
+        """(master, m, v) of the committed state (synchronizes)."""
+        c = self.state().cur & 1
+        return self.p[c], self.m[c], self.v[c]
