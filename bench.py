@@ -11,7 +11,8 @@ and resident in HBM before the timed region starts.
 
 Prints one JSON line. ``roofline`` is for the dominant kernel (the fused step
 kernel): algorithmic bytes per launch, S * (N * 2 + 26), over its mean duration
-measured with HIP events recorded around that kernel on its own stream.
+measured with HIP events recorded around that kernel on its own stream (on every
+tenth timed step by default: an event pair costs the stream more than 10 us).
 ``cpu_baseline`` is the CPU oracle timed on this host on the same shard.
 """
 from __future__ import annotations
@@ -93,6 +94,15 @@ def main() -> int:
     ap.add_argument("--commit", default="device", choices=["device", "host"],
                     help="device: commit kernel, no host round trip per step; host: read the "
                          "stats back and apply the commit rule on the host every step")
+    ap.add_argument("--single-slot", action="store_true",
+                    help="device commit with one slot buffer (restore kernel after an overflow) "
+                         "instead of a double-buffered slot")
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="record HIP events around the step kernel of every k-th timed step "
+                         "(an event pair costs the stream more than 10 us)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run a plain device copy of 1 GiB three times "
+                         "(the known-size reference for HBM byte counters under rocprofv3)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -137,34 +147,38 @@ def main() -> int:
         reps.append(buf.view(tdt))
     p0 = torch.empty(S, dtype=torch.float32, device=dev)
     W.device_fill_params(p0, w, covered, args.rank)
-    Step = Z.DeviceShardStep if args.commit == "device" else Z.ShardStep
-    step = Step(S, w.N, gdt, p0, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                weight_decay=w.wd, loss_scale=w.loss_scale, dynamic=w.dynamic_loss_scale,
-                buckets=buckets_t, n_buckets=nb)
+    kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.wd,
+              loss_scale=w.loss_scale, dynamic=w.dynamic_loss_scale, buckets=buckets_t,
+              n_buckets=nb)
+    if args.commit == "device":
+        step = Z.DeviceShardStep(S, w.N, gdt, p0, double_slot=not args.single_slot, **kw)
+    else:
+        step = Z.ShardStep(S, w.N, gdt, p0, **kw)
     torch.cuda.synchronize()
     log("inputs resident; warmup", args.warmup)
 
     for _ in range(args.warmup):
         step.step(reps)
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    every = max(1, args.event_every)
+    ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for k in range(0, K, every)}
     skipped = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if args.commit == "device":
         for k in range(K):
-            step.step(reps, events=ev[k])
+            step.step(reps, events=ev.get(k))
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         skipped = int(step.state().n_skipped)
     else:
         for k in range(K):
-            st, verdict = step.step(reps, events=ev[k])
+            st, verdict = step.step(reps, events=ev.get(k))
             skipped += verdict == Z.ZERO_SKIP
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-    kms = [a.elapsed_time(b) for a, b in ev]
+    kms = [a.elapsed_time(b) for a, b in ev.values()]
     log(f"timed {K} steps in {elapsed:.4f} s; kernel mean {statistics.mean(kms) * 1e3:.1f} us, "
         f"median {statistics.median(kms) * 1e3:.1f} us, skipped {skipped}")
 
@@ -188,16 +202,27 @@ def main() -> int:
         "config": {"workload": f"{w.name} shard, rank {args.rank} of N={w.N}", "shard_elems": S,
                    "n_replicas": w.N, "grad_dtype": w.grad_dtype, "state_dtype": "f32",
                    "bytes_per_elem": bpe, "bucket_elems": args.bucket_elems,
-                   "commit": args.commit},
+                   "commit": args.commit,
+                   "slot": "single" if (args.single_slot or args.commit == "host") else "double"},
         "step_gbps": S * bpe / (elapsed / K) / 1e9,
         "kernel_us_mean": kernel_s * 1e6,
         "kernel_us_median": statistics.median(kms) * 1e3,
         "kernel_us_min": min(kms) * 1e3,
+        "kernel_samples": len(kms),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "cpu_baseline": None,
         "skipped_steps": skipped,
     }
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4,
+                                         "launches": 3}
+        del src, dst
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         host_reps = []

@@ -305,7 +305,7 @@ typedef struct {
     uint32_t cur;                  /* 0/1: which state set holds the committed state */
     uint32_t dynamic;              /* nonzero: halve the loss scale on overflow */
     uint32_t last_overflow;
-    uint32_t reserved;
+    uint32_t ticket;               /* internal: workgroups done in the running step; 0 between steps */
 } zero_device_state;
 
 /*
@@ -325,7 +325,9 @@ typedef struct {
     float* p[2];                   /* the two fp32 state sets, [shard_S] each */
     float* m[2];
     float* v[2];
-    uint16_t* slot_bf16;           /* this rank's slot, or NULL */
+    /* this rank's slot of the gathered bf16 parameters: slot[0] alone (slot[1] = NULL),
+       or a double-buffered pair in which slot[cur] holds the committed parameters */
+    uint16_t* slot[2];
     int64_t shard_S;
     const zero_bucket* buckets_dev;
     int64_t n_buckets;
@@ -342,10 +344,14 @@ typedef struct {
  * One whole step of this rank's shard with the commit on the device: the fused
  * pass of zero_adam_step (fold in slot order, average and unscale, overflow flag
  * and squared norm, Adam/AdamW, bf16 slot), reading set state->cur and writing
- * the other set, then a commit kernel that applies the skip rule of
- * zero_commit_rule to *state_dev (clean: t += 1 and the written set becomes
- * current; overflow: nothing committed, slot restored from the current master,
- * dynamic loss scale halved). Same arithmetic as zero_adam_step, bit for bit.
+ * the other set; the last workgroup to finish folds the per-workgroup partials
+ * and applies the skip rule of zero_commit_rule to *state_dev (clean: t += 1 and
+ * the written set becomes current; overflow: nothing committed, dynamic loss
+ * scale halved). With a single slot the candidate bf16 values go straight into
+ * it and a second kernel restores it from the current master after an overflow;
+ * with a double-buffered slot the candidate goes into slot[1 - cur] and the
+ * commit flips it with the state sets, so a step is one kernel. Same arithmetic
+ * as zero_adam_step, bit for bit.
  * Source of the step: "[REQUEST] Direct Correspondence between Gradient and
  * Optimizer States to Reduce Communication", "Problem"; ring order as in
  * GuanhuaWang's reply in "Why DeepSpeed ZeRO paper says reduce-scatter (or

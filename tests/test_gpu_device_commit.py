@@ -30,7 +30,7 @@ def bucket_table(Z, w, rank, bucket_elems):
     return torch.frombuffer(bytearray(bytes(raw)[: 16 * nb]), dtype=torch.uint8).to("cuda"), nb
 
 
-def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None):
+def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None, double_slot=False):
     lay, covered = layout_of(w, rank)
     S = lay.S
     gdt = Z.ZERO_BF16 if w.grad_dtype == "bf16" else Z.ZERO_F32
@@ -38,7 +38,8 @@ def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None):
     bt, nb = bucket_table(Z, w, rank, bucket_elems) if bucket_elems else (None, 0)
     step = Z.DeviceShardStep(S, w.N, gdt, to_dev(p0), lr=w.lr, beta1=w.beta1, beta2=w.beta2,
                              eps=w.eps, weight_decay=w.wd, loss_scale=w.loss_scale,
-                             dynamic=w.dynamic_loss_scale, buckets=bt, n_buckets=nb)
+                             dynamic=w.dynamic_loss_scale, buckets=bt, n_buckets=nb,
+                             double_slot=double_slot)
     tr = oracle.Trainer(p0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
                         oracle.f32_to_bf16(p0), loss_scale=w.loss_scale, dynamic=w.dynamic_loss_scale,
                         nthreads=NTHREADS, **w.hyper())
@@ -57,22 +58,24 @@ def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None):
         assert sumsq_close(st.sumsq, sumsq) and sumsq_close(rec.last_sumsq, sumsq)
         P, M, V = step.committed()
         check_state(f"device {w.name} r{rank} s{s}", to_host(P), to_host(M), to_host(V),
-                    to_host(step.slot), tr.p, tr.m, tr.v, tr.slot)
+                    to_host(step.current_slot()), tr.p, tr.m, tr.v, tr.slot)
     return flags
 
 
-def test_tiny_every_rank(Z):
+@pytest.mark.parametrize("double_slot", [False, True])
+def test_tiny_every_rank(Z, double_slot):
     w = W.get("tiny")
     for rank in range(w.N):
-        assert run_device_protocol(Z, w, rank) == [0, 0, 0]
+        assert run_device_protocol(Z, w, rank, double_slot=double_slot) == [0, 0, 0]
 
 
-@pytest.mark.parametrize("rank,bucket_elems", [(0, 0), (63, 0), (0, 4096), (31, 1000)])
-def test_ragged_injection(Z, rank, bucket_elems):
+@pytest.mark.parametrize("rank,bucket_elems,double_slot", [(0, 0, False), (63, 0, True),
+                                                          (0, 4096, True), (31, 1000, False)])
+def test_ragged_injection(Z, rank, bucket_elems, double_slot):
     w = W.get("ragged")
     lay, covered = layout_of(w, rank)
     inj = W.injection(w, lay.S, covered, rank)
-    flags = run_device_protocol(Z, w, rank, bucket_elems)
+    flags = run_device_protocol(Z, w, rank, bucket_elems, double_slot=double_slot)
     assert flags == [1 if s == inj[0] else 0 for s in range(w.steps)]
 
 
@@ -98,7 +101,8 @@ def test_gpt2_device_equals_host_commit(Z):
         assert ds.state().t == hs.t == s + 1
 
 
-def test_queued_chain_with_overflow(Z):
+@pytest.mark.parametrize("double_slot", [False, True])
+def test_queued_chain_with_overflow(Z, double_slot):
     """20 steps enqueued back to back with no host synchronization; step 7 carries
     a NaN and step 13 an +inf. The final state equals the oracle's trajectory."""
     S, N, K = 300_007, 8, 20
@@ -115,7 +119,7 @@ def test_queued_chain_with_overflow(Z):
     p0 = (rng.standard_normal(S) * 0.02).astype(np.float32)
     hy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
     step = Z.DeviceShardStep(S, N, Z.ZERO_BF16, to_dev(p0), weight_decay=0.01, loss_scale=1024.0,
-                             dynamic=True, **hy)
+                             dynamic=True, double_slot=double_slot, **hy)
     dsets = [[to_dev(r) for r in reps] for reps in sets]
     torch.cuda.synchronize()
     say("queued chain: enqueue 20 steps")
@@ -129,8 +133,8 @@ def test_queued_chain_with_overflow(Z):
     rec = step.state()
     assert rec.t == tr.t == K - 2 and rec.n_skipped == 2 and rec.loss_scale == tr.loss_scale == 256.0
     P, M, V = step.committed()
-    check_state("queued chain", to_host(P), to_host(M), to_host(V), to_host(step.slot), tr.p, tr.m,
-                tr.v, tr.slot)
+    check_state("queued chain", to_host(P), to_host(M), to_host(V), to_host(step.current_slot()),
+                tr.p, tr.m, tr.v, tr.slot)
 
 
 def test_record_init_and_validation(Z):

@@ -236,6 +236,8 @@ def test_train_step_validation(Z):
     assert call(p=(FAKE, FAKE)) == -1                      # both sets alias
     assert call(m=(FAKE + 8192, FAKE + 8192 + 64)) == -1   # partial overlap
     assert call(slot=FAKE + 4096 + 32) == -1               # slot inside p[1]
+    assert call(slot=(FAKE + 24576, FAKE + 24576 + 64)) == -1   # the two slots overlap
+    assert call(slot=(0, FAKE + 24576)) == -1              # slot[1] without slot[0]
     assert call(replicas=[FAKE + 4096]) == -1              # replica overlaps p[1]
     assert call(lr=-1.0) == -1
     assert call(replicas=[]) == -3

@@ -74,12 +74,12 @@ class zero_device_state(ctypes.Structure):
     _fields_ = [("beta1", f64), ("beta2", f64), ("beta1_pow", f64), ("beta2_pow", f64),
                 ("loss_scale", f64), ("min_loss_scale", f64), ("last_sumsq", f64),
                 ("t", i64), ("n_skipped", i64), ("cur", u32), ("dynamic", u32),
-                ("last_overflow", u32), ("reserved", u32)]
+                ("last_overflow", u32), ("ticket", u32)]
 
 
 class zero_train_args(ctypes.Structure):
     _fields_ = [("replicas", ctypes.POINTER(vp)), ("n_replicas", i32), ("grad_dtype", i32),
-                ("p", vp * 2), ("m", vp * 2), ("v", vp * 2), ("slot_bf16", vp), ("shard_S", i64),
+                ("p", vp * 2), ("m", vp * 2), ("v", vp * 2), ("slot", vp * 2), ("shard_S", i64),
                 ("buckets_dev", vp), ("n_buckets", i64), ("lr", f64), ("eps", f64),
                 ("weight_decay", f64), ("state_dev", vp), ("stats_dev", vp),
                 ("workspace_dev", vp), ("ws_bytes", sz), ("event_begin", vp), ("event_end", vp)]
@@ -318,7 +318,10 @@ def make_train_args(*, replicas, grad_dtype: int, p, m, v, slot=None, shard_S: i
     a.grad_dtype = int(grad_dtype)
     for name, pair in (("p", p), ("m", m), ("v", v)):
         setattr(a, name, (vp * 2)(_addr(pair[0]) or None, _addr(pair[1]) or None))
-    a.slot_bf16 = _addr(slot) or None
+    if isinstance(slot, (list, tuple)):
+        a.slot = (vp * 2)(_addr(slot[0]) or None, _addr(slot[1]) or None)
+    else:
+        a.slot = (vp * 2)(_addr(slot) or None, None)
     a.shard_S = int(shard_S)
     a.buckets_dev = _addr(buckets) or None
     a.n_buckets = int(n_buckets)

@@ -120,7 +120,7 @@ int check_replicas(const char* fn, const void* const* replicas, int32_t n, zero_
 }
 
 int check_common(const char* fn, int64_t S, const zero_bucket* buckets, int64_t n_buckets,
-                 const zero_stats* stats, const void* ws, size_t ws_bytes) {
+                 const zero_stats* stats, const void* ws, size_t ws_bytes, int32_t n_rep) {
     if (S < 0) {
         set_error("%s: shard_S=%lld is negative", fn, (long long)S);
         return ZERO_E_RANGE;
@@ -145,7 +145,7 @@ int check_common(const char* fn, int64_t S, const zero_bucket* buckets, int64_t 
         set_error("%s: stats_dev or workspace_dev is not 16-byte aligned", fn);
         return ZERO_E_ALIGN;
     }
-    const size_t need = (size_t)zk::grid_for(S, n_buckets) * sizeof(zk::Partial);
+    const size_t need = (size_t)zk::grid_for(S, n_buckets, n_rep) * sizeof(zk::Partial);
     if (ws_bytes < need) {
         set_error("%s: workspace of %zu bytes < %zu needed", fn, ws_bytes, need);
         return ZERO_E_RANGE;
@@ -175,7 +175,8 @@ int zero_reduce_shard(const void* const* replicas, int32_t n_replicas, zero_dtyp
     static const char* fn = "zero_reduce_shard";
     int rc = check_replicas(fn, replicas, n_replicas, grad_dtype, shard_S);
     if (rc) return rc;
-    rc = check_common(fn, shard_S, buckets_dev, n_buckets, stats_dev, workspace_dev, ws_bytes);
+    rc = check_common(fn, shard_S, buckets_dev, n_buckets, stats_dev, workspace_dev, ws_bytes,
+                      n_replicas);
     if (rc) return rc;
     if (!(isfinite(loss_scale) && loss_scale > 0.0)) {
         set_error("%s: loss_scale=%g must be finite and > 0", fn, loss_scale);
@@ -228,7 +229,8 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
         return ZERO_E_INVAL;
     }
     const int64_t S = a.shard_S;
-    int rc = check_common(fn, S, a.buckets_dev, a.n_buckets, a.stats_dev, a.workspace_dev, a.ws_bytes);
+    int rc = check_common(fn, S, a.buckets_dev, a.n_buckets, a.stats_dev, a.workspace_dev, a.ws_bytes,
+                          fused ? a.n_replicas : 1);
     if (rc) return rc;
     if (fused) {
         rc = check_replicas(fn, a.replicas, a.n_replicas, a.grad_dtype, S);
@@ -360,9 +362,10 @@ int zero_train_step(const zero_train_args* args, void* stream) {
     }
     const zero_train_args& a = *args;
     const int64_t S = a.shard_S;
-    int rc = check_common(fn, S, a.buckets_dev, a.n_buckets, a.stats_dev, a.workspace_dev, a.ws_bytes);
+    int rc = check_replicas(fn, a.replicas, a.n_replicas, a.grad_dtype, S);
     if (rc) return rc;
-    rc = check_replicas(fn, a.replicas, a.n_replicas, a.grad_dtype, S);
+    rc = check_common(fn, S, a.buckets_dev, a.n_buckets, a.stats_dev, a.workspace_dev, a.ws_bytes,
+                      a.n_replicas);
     if (rc) return rc;
     if (!a.state_dev) {
         set_error("%s: state_dev is NULL", fn);
@@ -383,9 +386,13 @@ int zero_train_step(const zero_train_args* args, void* stream) {
             return ZERO_E_ALIGN;
         }
     }
-    if (a.slot_bf16 && !aligned16(a.slot_bf16)) {
-        set_error("%s: slot_bf16 is not 16-byte aligned", fn);
+    if ((a.slot[0] && !aligned16(a.slot[0])) || (a.slot[1] && !aligned16(a.slot[1]))) {
+        set_error("%s: a slot buffer is not 16-byte aligned", fn);
         return ZERO_E_ALIGN;
+    }
+    if (a.slot[1] && !a.slot[0]) {
+        set_error("%s: slot[1] given without slot[0]", fn);
+        return ZERO_E_INVAL;
     }
     if (!(isfinite(a.lr) && a.lr >= 0) || !(isfinite(a.eps) && a.eps >= 0) ||
         !(isfinite(a.weight_decay) && a.weight_decay >= 0)) {
@@ -396,11 +403,12 @@ int zero_train_step(const zero_train_args* args, void* stream) {
     const Span bufs[] = {span("p[0]", a.p[0], b4), span("p[1]", a.p[1], b4),
                          span("m[0]", a.m[0], b4), span("m[1]", a.m[1], b4),
                          span("v[0]", a.v[0], b4), span("v[1]", a.v[1], b4),
-                         span("slot", a.slot_bf16, a.slot_bf16 ? 2 * S : 0),
+                         span("slot[0]", a.slot[0], a.slot[0] ? 2 * S : 0),
+                         span("slot[1]", a.slot[1], a.slot[1] ? 2 * S : 0),
                          span("stats", a.stats_dev, 16),
                          span("workspace", a.workspace_dev, (int64_t)a.ws_bytes),
                          span("state", a.state_dev, (int64_t)sizeof(zero_device_state))};
-    const int nb = 10;
+    const int nb = 11;
     for (int i = 0; i < nb; ++i) {
         for (int k = i + 1; k < nb; ++k)
             if (overlap(bufs[i], bufs[k])) {
@@ -432,7 +440,11 @@ int zero_train_step(const zero_train_args* args, void* stream) {
         d.set_v[i] = a.v[i];
     }
     d.ctrl = a.state_dev;
-    d.slot = a.slot_bf16;
+    d.slot = a.slot[0];
+    if (a.slot[1]) {
+        d.set_slot[0] = a.slot[0];
+        d.set_slot[1] = a.slot[1];
+    }
     d.sc = zk::Scalars{};
     d.sc.lr = (float)a.lr;
     d.sc.eps = (float)a.eps;

@@ -52,7 +52,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 struct KParams {
     const void* rep[ZERO_MAX_REPLICAS];
     int32_t n_rep;
-    int32_t has_slot;
+    int32_t reserved;
     int64_t S;
     const zero_bucket* buckets;
     int64_t n_buckets;
@@ -66,6 +66,9 @@ struct KParams {
     float* set_m[2];
     float* set_v[2];
     const zero_device_state* ctrl;          // device-commit path: committed t, scale, set
+    zero_device_state* ctrl_rw;             // the same record, written by the last workgroup
+    zero_stats* stats;
+    uint16_t* set_slot[2];                  // device-commit path with a double-buffered slot
     uint16_t* slot;
     float* g_out;
     Partial* partials;
@@ -81,6 +84,7 @@ struct Res {
     float* p_out;
     float* m_out;
     float* v_out;
+    uint16_t* slot;                         // where the bf16 result goes, or nullptr
 };
 
 // ---------------------------------------------------------------------------
@@ -232,6 +236,7 @@ __device__ __forceinline__ Res resolve(const KParams& a) {
         r.p_out = a.p_out;
         r.m_out = a.m_out;
         r.v_out = a.v_out;
+        r.slot = a.slot;
     } else {
         const zero_device_state* c = a.ctrl;
         const uint32_t cur = c->cur & 1u, nxt = cur ^ 1u;
@@ -251,14 +256,25 @@ __device__ __forceinline__ Res resolve(const KParams& a) {
         r.p_out = a.set_p[nxt];
         r.m_out = a.set_m[nxt];
         r.v_out = a.set_v[nxt];
+        // a double-buffered slot takes the candidate in the out buffer, like the state
+        r.slot = a.set_slot[1] ? a.set_slot[nxt] : a.slot;
     }
     return r;
 }
 
-// ROWS quads at q0, q0 + qs, ...: the whole step for 4*ROWS elements of this lane.
+// The update of ROWS quads, held in registers until it is stored.
+template <int ROWS>
+struct Outs {
+    f32x4 pn[ROWS], m1[ROWS], v1[ROWS];
+};
+
+// ROWS quads at q0, q0 + qs, ...: fold, average, flag, g^2 and (with ADAM) the
+// update of 4*ROWS elements of this lane. Reduce-only launches store g here;
+// the update is returned in `o` for quads_store.
 template <typename RT, bool ADAM, bool WRITE_G, int ROWS>
-__device__ __forceinline__ void quads(const KParams& a, const Res& rs, int64_t q0, int64_t qs,
-                                      double& sq, uint32_t& bad) {
+__device__ __forceinline__ void quads_compute(const KParams& a, const Res& rs, int64_t q0,
+                                              int64_t qs, double& sq, uint32_t& bad,
+                                              Outs<ROWS>& o) {
     f32x4 p[ROWS], m[ROWS], v[ROWS];
     if constexpr (ADAM) {
 #pragma unroll
@@ -283,26 +299,43 @@ __device__ __forceinline__ void quads(const KParams& a, const Res& rs, int64_t q
         }
         if constexpr (WRITE_G) st(reinterpret_cast<f32x4*>(a.g_out) + q, g);
         if constexpr (ADAM) {
-            f32x4 pn, m1, v1;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 float x, y, z;
                 adam1(g[c], p[r][c], m[r][c], v[r][c], rs.sc, x, y, z);
-                pn[c] = x;
-                m1[c] = y;
-                v1[c] = z;
-            }
-            st(reinterpret_cast<f32x4*>(rs.p_out) + q, pn);
-            st(reinterpret_cast<f32x4*>(rs.m_out) + q, m1);
-            st(reinterpret_cast<f32x4*>(rs.v_out) + q, v1);
-            if (a.has_slot) {
-                u32x2 w;
-                w.x = f2bf(pn.x) | (f2bf(pn.y) << 16);
-                w.y = f2bf(pn.z) | (f2bf(pn.w) << 16);
-                st(reinterpret_cast<u32x2*>(a.slot) + q, w);
+                o.pn[r][c] = x;
+                o.m1[r][c] = y;
+                o.v1[r][c] = z;
             }
         }
     }
+}
+
+template <int ROWS>
+__device__ __forceinline__ void quads_store(const Res& rs, int64_t q0, int64_t qs,
+                                            const Outs<ROWS>& o) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const int64_t q = q0 + r * qs;
+        st(reinterpret_cast<f32x4*>(rs.p_out) + q, o.pn[r]);
+        st(reinterpret_cast<f32x4*>(rs.m_out) + q, o.m1[r]);
+        st(reinterpret_cast<f32x4*>(rs.v_out) + q, o.v1[r]);
+        if (rs.slot) {
+            u32x2 w;
+            w.x = f2bf(o.pn[r].x) | (f2bf(o.pn[r].y) << 16);
+            w.y = f2bf(o.pn[r].z) | (f2bf(o.pn[r].w) << 16);
+            st(reinterpret_cast<u32x2*>(rs.slot) + q, w);
+        }
+    }
+}
+
+// The whole step for ROWS quads of this lane.
+template <typename RT, bool ADAM, bool WRITE_G, int ROWS>
+__device__ __forceinline__ void quads(const KParams& a, const Res& rs, int64_t q0, int64_t qs,
+                                      double& sq, uint32_t& bad) {
+    Outs<ROWS> o;
+    quads_compute<RT, ADAM, WRITE_G, ROWS>(a, rs, q0, qs, sq, bad, o);
+    if constexpr (ADAM) quads_store<ROWS>(rs, q0, qs, o);
 }
 
 // One element, for bucket edges and the shard tail.
@@ -322,12 +355,12 @@ __device__ __forceinline__ void one_elem(const KParams& a, const Res& rs, int64_
         rs.p_out[e] = pn;
         rs.m_out[e] = m1;
         rs.v_out[e] = v1;
-        if (a.has_slot) a.slot[e] = (uint16_t)f2bf(pn);
+        if (rs.slot) rs.slot[e] = (uint16_t)f2bf(pn);
     }
 }
 
 // All elements of [lo, hi) by the threads of one workgroup.
-template <typename RT, bool ADAM, bool WRITE_G>
+template <typename RT, bool ADAM, bool WRITE_G, int ROWS>
 __device__ __forceinline__ void range(const KParams& a, const Res& rs, int64_t lo, int64_t hi,
                                       double& sq, uint32_t& bad) {
     const int tid = threadIdx.x;
@@ -339,8 +372,8 @@ __device__ __forceinline__ void range(const KParams& a, const Res& rs, int64_t l
     }
     for (int64_t e = lo + tid; e < qa * 4; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
     int64_t q = qa + tid;
-    for (; q + (kRows - 1) * kBlock < qb; q += kRows * kBlock)
-        quads<RT, ADAM, WRITE_G, kRows>(a, rs, q, kBlock, sq, bad);
+    for (; q + (ROWS - 1) * kBlock < qb; q += ROWS * kBlock)
+        quads<RT, ADAM, WRITE_G, ROWS>(a, rs, q, kBlock, sq, bad);
     for (; q < qb; q += kBlock) quads<RT, ADAM, WRITE_G, 1>(a, rs, q, 0, sq, bad);
     for (int64_t e = qb * 4 + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
 }
@@ -383,23 +416,60 @@ __device__ __forceinline__ void block_reduce(double& sq, uint32_t& bad, uint32_t
 // kernels
 // ---------------------------------------------------------------------------
 
-template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL>
+// The commit of a device-resident step (thread 0 of the last workgroup):
+//   clean:    t += 1, beta^t *= beta, the written state set becomes current;
+//   overflow: skipped += 1, a dynamic loss scale halves (not below its floor).
+__device__ __forceinline__ void commit_record(zero_device_state* c, zero_stats* stats, double sq,
+                                              uint32_t bad, uint32_t badb) {
+    const bool overflow = bad != 0u;
+    stats->overflow = overflow ? 1u : 0u;
+    stats->bad_buckets = badb;
+    stats->sumsq = sq;
+    c->last_overflow = overflow ? 1u : 0u;
+    c->last_sumsq = sq;
+    if (!overflow) {
+        c->t = c->t + 1;
+        c->beta1_pow = c->beta1_pow * c->beta1;
+        c->beta2_pow = c->beta2_pow * c->beta2;
+        c->cur = (c->cur & 1u) ^ 1u;
+    } else {
+        c->n_skipped = c->n_skipped + 1;
+        if (c->dynamic) {
+            const double half = c->loss_scale / 2.0;
+            c->loss_scale = half > c->min_loss_scale ? half : c->min_loss_scale;
+        }
+    }
+}
+
+template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL, int ROWS>
 __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
     const Res rs = resolve<CTRL>(a);
     double sq = 0.0;
     uint32_t bad = 0u, badb = 0u;
+    // Device-commit launches hold back the stores of their last trip until the
+    // workgroup's partial is published (see below); others store as they go.
+    constexpr bool kDefer = CTRL && !BUCKETS && ADAM;
+    Outs<ROWS> last;
+    int64_t last_q = -1;
     if constexpr (!BUCKETS) {
         const int64_t nq = a.S >> 2;
-        const int64_t per_trip = (int64_t)kRows * kBlock;
+        const int64_t per_trip = (int64_t)ROWS * kBlock;
         const int64_t ntrips = nq / per_trip;
-        for (int64_t trip = blockIdx.x; trip < ntrips; trip += gridDim.x)
-            quads<RT, ADAM, WRITE_G, kRows>(a, rs, trip * per_trip + threadIdx.x, kBlock, sq, bad);
+        int64_t trip = blockIdx.x;
+        for (; trip + (kDefer ? (int64_t)gridDim.x : 0) < ntrips; trip += gridDim.x)
+            quads<RT, ADAM, WRITE_G, ROWS>(a, rs, trip * per_trip + threadIdx.x, kBlock, sq, bad);
         // whole quads after the last full trip, and the last S % 4 elements
         if ((int64_t)blockIdx.x == ntrips % gridDim.x) {
             for (int64_t q = ntrips * per_trip + threadIdx.x; q < nq; q += kBlock)
                 quads<RT, ADAM, WRITE_G, 1>(a, rs, q, 0, sq, bad);
             const int64_t e = nq * 4 + threadIdx.x;
             if (e < a.S) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
+        }
+        if constexpr (kDefer) {
+            if (trip < ntrips) {
+                last_q = trip * per_trip + threadIdx.x;
+                quads_compute<RT, ADAM, WRITE_G, ROWS>(a, rs, last_q, kBlock, sq, bad, last);
+            }
         }
     } else {
         for (int64_t b = blockIdx.x; b < a.n_buckets; b += gridDim.x) {
@@ -409,16 +479,63 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
                 if (threadIdx.x == 0) badb += 1u;
                 continue;
             }
-            range<RT, ADAM, WRITE_G>(a, rs, lo, lo + len, sq, bad);
+            range<RT, ADAM, WRITE_G, ROWS>(a, rs, lo, lo + len, sq, bad);
         }
     }
     block_reduce(sq, bad, badb);
-    if (threadIdx.x == 0) {
-        Partial pt;
-        pt.sumsq = sq;
-        pt.bad = bad;
-        pt.bad_buckets = badb;
-        a.partials[blockIdx.x] = pt;
+    if constexpr (!CTRL) {
+        if (threadIdx.x == 0) {
+            Partial pt;
+            pt.sumsq = sq;
+            pt.bad = bad;
+            pt.bad_buckets = badb;
+            a.partials[blockIdx.x] = pt;
+        }
+    } else {
+        // The last workgroup to take a ticket folds every partial and commits. No
+        // cache writeback is needed: the partial goes out as agent-scope atomic
+        // stores (written through to the coherence point shared by all XCDs), a
+        // waitcnt orders their completion before the ticket increment, and the
+        // last workgroup reads the partials with agent-scope atomic loads. The
+        // commit needs only the partials; the output stores still in flight
+        // complete before the kernel does, ahead of any later launch.
+        __shared__ uint32_t s_last;
+        if (threadIdx.x == 0) {
+            uint64_t* slot2 = reinterpret_cast<uint64_t*>(a.partials + blockIdx.x);
+            __hip_atomic_store(slot2, (uint64_t)__double_as_longlong(sq), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(slot2 + 1, (uint64_t)bad | ((uint64_t)badb << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(0);
+            const uint32_t ticket = __hip_atomic_fetch_add(&a.ctrl_rw->ticket, 1u, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+            s_last = ticket + 1u == gridDim.x ? 1u : 0u;
+        }
+        // The held-back trip is stored only now, so the wait above covers stores
+        // issued a whole trip earlier rather than this trip's.
+        if constexpr (kDefer) {
+            if (last_q >= 0) quads_store<ROWS>(rs, last_q, kBlock, last);
+        }
+        __syncthreads();
+        if (s_last) {
+            double tsq = 0.0;
+            uint32_t tbad = 0u, tbadb = 0u;
+            const int n = (int)gridDim.x;
+            for (int i = threadIdx.x; i < n; i += kBlock) {
+                uint64_t* slot2 = reinterpret_cast<uint64_t*>(a.partials + i);
+                const uint64_t w0 = __hip_atomic_load(slot2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t w1 = __hip_atomic_load(slot2 + 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+                tsq += __longlong_as_double((long long)w0);
+                tbad |= (uint32_t)w1;
+                tbadb += (uint32_t)(w1 >> 32);
+            }
+            block_reduce(tsq, tbad, tbadb);
+            if (threadIdx.x == 0) {
+                commit_record(a.ctrl_rw, a.stats, tsq, tbad, tbadb);
+                __hip_atomic_store(&a.ctrl_rw->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
 }
 
@@ -463,50 +580,15 @@ __global__ void __launch_bounds__(kBlock) k_cast_slot(const float* master, int64
     cast_range(master, S, slot);
 }
 
-// Device-side commit of a train step. Every workgroup folds the step kernel's
-// partials into the verdict; on overflow the grid restores the slot from the
+// After a device-resident step: if it overflowed, restore the slot from the
 // committed master (the current set, which a skipped step leaves current).
-// Workgroup 0 writes the stats and the new committed-state record:
-//   clean:    t += 1, beta^t *= beta, the out set becomes current;
-//   overflow: skipped += 1, a dynamic loss scale halves (not below its floor).
-// Only an overflowed step reads `cur` outside workgroup 0, and such a step does
-// not change it, so the grid never races on the record.
-__global__ void __launch_bounds__(kBlock) k_commit(const Partial* parts, int n, zero_stats* stats,
-                                                  zero_device_state* ctrl, const float* set_p0,
-                                                  const float* set_p1, uint16_t* slot, int64_t S) {
-    double sq = 0.0;
-    uint32_t bad = 0u, badb = 0u;
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-        const Partial pt = parts[i];
-        sq += pt.sumsq;
-        bad |= pt.bad;
-        badb += pt.bad_buckets;
-    }
-    block_reduce(sq, bad, badb);
-    __shared__ uint32_t s_bad;
-    if (threadIdx.x == 0) s_bad = bad;
-    __syncthreads();
-    const bool overflow = s_bad != 0u;
-    if (overflow && slot) cast_range((ctrl->cur & 1u) ? set_p1 : set_p0, S, slot);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        stats->overflow = overflow ? 1u : 0u;
-        stats->bad_buckets = badb;
-        stats->sumsq = sq;
-        ctrl->last_overflow = overflow ? 1u : 0u;
-        ctrl->last_sumsq = sq;
-        if (!overflow) {
-            ctrl->t = ctrl->t + 1;
-            ctrl->beta1_pow = ctrl->beta1_pow * ctrl->beta1;
-            ctrl->beta2_pow = ctrl->beta2_pow * ctrl->beta2;
-            ctrl->cur = (ctrl->cur & 1u) ^ 1u;
-        } else {
-            ctrl->n_skipped = ctrl->n_skipped + 1;
-            if (ctrl->dynamic) {
-                const double half = ctrl->loss_scale / 2.0;
-                ctrl->loss_scale = half > ctrl->min_loss_scale ? half : ctrl->min_loss_scale;
-            }
-        }
-    }
+// Every workgroup reads the verdict the step's last workgroup wrote and, on a
+// clean step, exits at once.
+__global__ void __launch_bounds__(kBlock) k_restore(const zero_device_state* ctrl,
+                                                   const float* set_p0, const float* set_p1,
+                                                   uint16_t* slot, int64_t S) {
+    if (ctrl->last_overflow == 0u) return;
+    cast_range((ctrl->cur & 1u) ? set_p1 : set_p0, S, slot);
 }
 
 __global__ void k_state_init(zero_device_state* s, double beta1, double beta2, double loss_scale,
@@ -524,7 +606,7 @@ __global__ void k_state_init(zero_device_state* s, double beta1, double beta2, d
         s->cur = 0u;
         s->dynamic = dynamic;
         s->last_overflow = 0u;
-        s->reserved = 0u;
+        s->ticket = 0u;
     }
 }
 
@@ -532,12 +614,24 @@ __global__ void k_state_init(zero_device_state* s, double beta1, double beta2, d
 // launchers
 // ---------------------------------------------------------------------------
 
-int grid_for(int64_t S, int64_t n_buckets) {
+// Quads per lane per trip: two rows keep more bytes in flight when few replica
+// streams are open; with many replicas one row keeps the register budget (and so
+// the occupancy) up.
+int rows_for(int32_t n_rep) { return n_rep <= 16 ? 2 : 1; }
+
+// Workgroups of the step kernel: about four times what the chip holds at once
+// (so faster CUs pick up more work), at most kGridMax, and balanced so that every
+// workgroup makes the same number of full trips (no ragged last round). Few
+// replica streams (two rows per lane, 4 waves per SIMD) settle best at 4096,
+// many (one row, 7-8 waves per SIMD) at 8192.
+int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep) {
     if (n_buckets > 0) return (int)(n_buckets < kGridMax ? n_buckets : kGridMax);
-    const int64_t per_trip = (int64_t)kRows * kBlock * kVec;
-    const int64_t trips = (S + per_trip - 1) / per_trip;
+    const int64_t per_trip = (int64_t)rows_for(n_rep) * kBlock * kVec;
+    const int64_t trips = S / per_trip;
     if (trips < 1) return 1;
-    return (int)(trips < kGridMax ? trips : kGridMax);
+    const int64_t cap = rows_for(n_rep) == 2 ? kGridMax / 2 : kGridMax;
+    const int64_t rounds = (trips + cap - 1) / cap;
+    return (int)((trips + rounds - 1) / rounds);
 }
 
 static int grid_stream(int64_t S) {
@@ -548,23 +642,29 @@ static int grid_stream(int64_t S) {
     return (int)g;
 }
 
+template <typename RT, bool BUCKETS, int ROWS>
+static void launch_rows(const StepDesc& d, const KParams& k, int grid, hipStream_t st) {
+    if (d.ctrl)
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, true, false, true, ROWS>), dim3(grid), dim3(kBlock), 0, st, k);
+    else if (d.adam)
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, true, false, false, ROWS>), dim3(grid), dim3(kBlock), 0, st, k);
+    else if (d.g_out)
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, true, false, ROWS>), dim3(grid), dim3(kBlock), 0, st, k);
+    else
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, false, false, ROWS>), dim3(grid), dim3(kBlock), 0, st, k);
+}
+
 template <typename RT, bool BUCKETS>
 static void launch_typed(const StepDesc& d, const KParams& k, int grid, hipStream_t st) {
-    if (d.ctrl)
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, true, false, true>), dim3(grid), dim3(kBlock), 0, st, k);
-    else if (d.adam)
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, true, false, false>), dim3(grid), dim3(kBlock), 0, st, k);
-    else if (d.g_out)
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, true, false>), dim3(grid), dim3(kBlock), 0, st, k);
-    else
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, false, false>), dim3(grid), dim3(kBlock), 0, st, k);
+    if (rows_for(d.n_rep) == 2) launch_rows<RT, BUCKETS, 2>(d, k, grid, st);
+    else launch_rows<RT, BUCKETS, 1>(d, k, grid, st);
 }
 
 hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     KParams k;
     for (int j = 0; j < ZERO_MAX_REPLICAS; ++j) k.rep[j] = j < d.n_rep ? d.replicas[j] : nullptr;
     k.n_rep = d.n_rep;
-    k.has_slot = d.slot != nullptr;
+    k.reserved = 0;
     k.S = d.S;
     k.buckets = d.buckets;
     k.n_buckets = d.n_buckets;
@@ -580,12 +680,16 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
         k.set_v[i] = d.set_v[i];
     }
     k.ctrl = d.ctrl;
+    k.ctrl_rw = d.ctrl;
+    k.stats = d.stats;
     k.slot = d.slot;
+    k.set_slot[0] = d.set_slot[0];
+    k.set_slot[1] = d.set_slot[1];
     k.g_out = d.g_out;
     k.partials = d.partials;
     k.sc = d.sc;
     const bool buckets = d.n_buckets > 0;
-    const int grid = grid_for(d.S, d.n_buckets);
+    const int grid = grid_for(d.S, d.n_buckets, d.n_rep);
     if (d.ev_begin) {
         hipError_t e = hipEventRecord(d.ev_begin, st);
         if (e != hipSuccess) return e;
@@ -604,9 +708,10 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     if (d.ctrl) {
-        hipLaunchKernelGGL(k_commit, dim3(grid_stream(d.S)), dim3(kBlock), 0, st,
-                           (const Partial*)d.partials, grid, d.stats, d.ctrl,
-                           (const float*)d.set_p[0], (const float*)d.set_p[1], d.slot, d.S);
+        if (d.slot && !d.set_slot[1])
+            hipLaunchKernelGGL(k_restore, dim3(grid_stream(d.S)), dim3(kBlock), 0, st,
+                               (const zero_device_state*)d.ctrl, (const float*)d.set_p[0],
+                               (const float*)d.set_p[1], d.slot, d.S);
     } else {
         hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kFinalizeBlock), 0, st,
                            (const Partial*)d.partials, grid, d.stats);

@@ -9,16 +9,12 @@
 
 namespace zk {
 
-#ifndef ZERO_ROWS
-#define ZERO_ROWS 2
-#endif
 #ifndef ZERO_GRID_MAX
-#define ZERO_GRID_MAX 2048
+#define ZERO_GRID_MAX 8192
 #endif
 
 constexpr int kBlock = 256;         // threads per workgroup: 4 wave64s
 constexpr int kVec = 4;             // elements per lane per row (one quad)
-constexpr int kRows = ZERO_ROWS;    // quads per lane per trip of the main loop
 constexpr int kGridMax = ZERO_GRID_MAX;  // workgroups of the grid-stride step kernel
 constexpr int kCommitGrid = 512;    // workgroups of the commit / cast kernels
 constexpr int kFinalizeBlock = 256;
@@ -61,13 +57,15 @@ struct StepDesc {
     float* set_m[2];
     float* set_v[2];
     zero_device_state* ctrl;        // device-commit path, else nullptr
+    uint16_t* set_slot[2];          // device-commit path, double-buffered slot (else nullptr)
     zero_stats* stats;
     Partial* partials;              // workspace, >= grid_for() entries
     hipEvent_t ev_begin;            // optional, around the main kernel only
     hipEvent_t ev_end;
 };
 
-int grid_for(int64_t S, int64_t n_buckets);
+int rows_for(int32_t n_rep);
+int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep);
 hipError_t launch_step(const StepDesc& d, hipStream_t stream);
 hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t stream);
 hipError_t launch_state_init(zero_device_state* s, double beta1, double beta2, double loss_scale,

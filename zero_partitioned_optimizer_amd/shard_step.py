@@ -136,17 +136,23 @@ class DeviceShardStep:
                  lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
                  loss_scale: float = 1.0, dynamic: bool = False, min_loss_scale: float = 1.0,
                  slot: Optional[torch.Tensor] = None, buckets: Optional[torch.Tensor] = None,
-                 n_buckets: int = 0):
+                 n_buckets: int = 0, double_slot: bool = False):
+        """double_slot: keep a second slot buffer so that the candidate bf16 values
+        land in the non-current one and a skipped step needs no restore kernel;
+        ``slot`` is then the pair's first buffer and ``current_slot()`` the
+        committed one."""
         dev = p0.device
         S = int(shard_S)
         assert p0.dtype == torch.float32 and p0.numel() == S and p0.is_contiguous()
         self.S, self.N, self.grad_dtype = S, int(n_replicas), int(grad_dtype)
         self.lr, self.eps, self.weight_decay = float(lr), float(eps), float(weight_decay)
+        self.double_slot = bool(double_slot)
         self.p = [p0.clone(), torch.zeros_like(p0)]
         self.m = [torch.zeros_like(p0), torch.zeros_like(p0)]
         self.v = [torch.zeros_like(p0), torch.zeros_like(p0)]
         self.slot = slot if slot is not None else torch.empty(S, dtype=torch.int16, device=dev)
         assert self.slot.numel() == S and self.slot.element_size() == 2
+        self.slot_alt = torch.zeros(S, dtype=torch.int16, device=dev) if self.double_slot else None
         self.buckets, self.n_buckets = buckets, int(n_buckets)
         self.stats = torch.zeros(16, dtype=torch.uint8, device=dev)
         self.record = torch.zeros(128, dtype=torch.uint8, device=dev)
@@ -159,8 +165,9 @@ class DeviceShardStep:
     def _args_for(self, replicas):
         key = tuple(r.data_ptr() for r in replicas)
         if self._args_key != key:
+            slot = (self.slot, self.slot_alt) if self.double_slot else self.slot
             self._args = B.make_train_args(replicas=list(replicas), grad_dtype=self.grad_dtype,
-                                           p=self.p, m=self.m, v=self.v, slot=self.slot,
+                                           p=self.p, m=self.m, v=self.v, slot=slot,
                                            shard_S=self.S, buckets=self.buckets,
                                            n_buckets=self.n_buckets, lr=self.lr, eps=self.eps,
                                            weight_decay=self.weight_decay, state=self.record,
@@ -191,3 +198,9 @@ class DeviceShardStep:
         """(master, m, v) of the committed state (synchronizes)."""
         c = self.state().cur & 1
         return self.p[c], self.m[c], self.v[c]
+
+    def current_slot(self) -> torch.Tensor:
+        """The slot buffer holding the committed bf16 parameters (synchronizes)."""
+        if not self.double_slot:
+            return self.slot
+        return self.slot_alt if self.state().cur & 1 else self.slot
