@@ -103,6 +103,9 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain device copy of 1 GiB three times "
                          "(the known-size reference for HBM byte counters under rocprofv3)")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="also run the plain-stream HBM probe (read, write, copy, 2:1 and 5:1 "
+                         "read:write mixes) and report it beside the roofline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -214,6 +217,17 @@ def main() -> int:
         "cpu_baseline": None,
         "skipped_steps": skipped,
     }
+    if args.hbm_probe:
+        import subprocess
+        probe = os.path.join(ROOT, "zero_partitioned_optimizer_amd", "hbm_probe")
+        log("hbm probe ...")
+        res = subprocess.run([probe], capture_output=True, text=True, timeout=300)
+        if res.returncode != 0:
+            raise RuntimeError("hbm_probe failed: " + res.stderr)
+        hp = json.loads(res.stdout.strip().splitlines()[-1])
+        mix = "mix_2to1" if bpe - 26 <= 2 * 14 else "mix_5to1"
+        hp["step_kernel_vs_" + mix] = achieved / hp[mix]
+        out["hbm_probe"] = hp
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

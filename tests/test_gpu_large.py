@@ -1,0 +1,144 @@
+"""GPU parity at full shard sizes: the Llama-7B shard (S = 842,301,952, N = 8, loss
+scale 65536) and the Llama-70B shard (S = 2,155,520,256, N = 32, AdamW), in the
+launch configuration bench.py times (device commit, double-buffered slot,
+whole-shard grid).
+
+The oracle cannot run whole shards this size in a test, so it follows the
+trajectory of sampled elements (each element's update depends only on its own
+inputs; the overflow flag is global and is checked to be 0 on both sides):
+the first and last 64 Ki elements, every tensor boundary of the shard, and
+random positions. Whole-shard properties close the gap: the fused step equals
+the unfused path (reduce, then Adam from the fp32 gradient) bit for bit, the
+unfused gradient equals the oracle on the samples, and the fused squared norm
+equals an fp64 sum of that gradient's squares.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import NTHREADS, check_state, say, sumsq_close, to_host
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def sample_index(S, covered, rng, n_random):
+    idx = [np.arange(0, min(S, 65536)), np.arange(max(0, S - 65536), S)]
+    for off, ln in covered:
+        for e in (off, off + 1, off + ln - 2, off + ln - 1):
+            if 0 <= e < S:
+                idx.append(np.array([e]))
+    idx.append(rng.integers(0, S, n_random))
+    return np.unique(np.concatenate(idx)).astype(np.int64)
+
+
+def gather(t, idx_t):
+    return t[idx_t]
+
+
+def run_large(Z, name, steps, n_random, sub_elems):
+    w = W.get(name)
+    lay = oracle.Layout(w.numels, N=w.N, A=w.A, B=w.B)
+    rank = 0
+    S = lay.S
+    covered = [(int(s[2]), int(s[3])) for s in lay.segments(rank)]
+    rng = np.random.default_rng(5)
+    idx = sample_index(S, covered, rng, n_random)
+    idx_t = torch.from_numpy(idx).cuda()
+    dev = torch.device("cuda")
+    say(f"{name}: S={S} N={w.N}, {idx.size} samples, allocating")
+    reps = [torch.empty(S, dtype=torch.bfloat16, device=dev) for _ in range(w.N)]
+    p0 = torch.empty(S, dtype=torch.float32, device=dev)
+    W.device_fill_params(p0, w, covered, rank)
+    p0_s = to_host(gather(p0, idx_t))
+    step = Z.DeviceShardStep(S, w.N, Z.ZERO_BF16, p0, lr=w.lr, beta1=w.beta1, beta2=w.beta2,
+                             eps=w.eps, weight_decay=w.wd, loss_scale=w.loss_scale,
+                             dynamic=w.dynamic_loss_scale, double_slot=True)
+    del p0
+    torch.cuda.empty_cache()
+    tr = oracle.Trainer(p0_s.copy(), np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32),
+                        oracle.f32_to_bf16(p0_s), loss_scale=w.loss_scale,
+                        dynamic=w.dynamic_loss_scale, nthreads=NTHREADS, **w.hyper())
+    for s in range(steps):
+        say(f"{name}: generating step {s} replicas")
+        for j, r in enumerate(reps):
+            W.device_fill_replica(r, w, covered, rank, s, j)
+        sreps = [to_host(gather(r.view(torch.int16), idx_t)) for r in reps]
+        dreps = [r.view(torch.int16) for r in reps]
+        if s == 0:
+            # whole-shard properties on the first step, before the state moves
+            unfused_properties(Z, w, S, step, dreps, idx, idx_t, sreps, sub_elems)
+        say(f"{name}: step {s}")
+        step.step(dreps)
+        flag, _ = tr.step(sreps)
+        rec = step.state()
+        st = step.last_stats()
+        assert flag == 0 and st.overflow == 0 and rec.last_overflow == 0
+        assert rec.t == tr.t == s + 1 and np.isfinite(st.sumsq) and st.sumsq > 0
+        P, M, V = step.committed()
+        check_state(f"{name} step {s} (samples)", to_host(gather(P, idx_t)), to_host(gather(M, idx_t)),
+                    to_host(gather(V, idx_t)), to_host(gather(step.current_slot(), idx_t)),
+                    tr.p, tr.m, tr.v, tr.slot)
+    del reps, dreps, step
+    torch.cuda.empty_cache()
+
+
+def unfused_properties(Z, w, S, step, dreps, idx, idx_t, sreps, sub_elems):
+    """On the first step's inputs: reduce_shard's g equals the oracle on the samples;
+    its squared norm equals an fp64 sum of g^2; the fused kernel's own norm agrees;
+    over the first `sub_elems` elements the unfused update equals the fused one
+    bit for bit."""
+    dev = torch.device("cuda")
+    say(f"{w.name}: reduce_shard over the whole shard")
+    G = torch.empty(S, dtype=torch.float32, device=dev)
+    stats = torch.zeros(16, dtype=torch.uint8, device=dev)
+    ws = torch.empty(Z.zero_workspace_bytes(S), dtype=torch.uint8, device=dev)
+    Z.zero_reduce_shard(dreps, Z.ZERO_BF16, S, stats, ws, loss_scale=w.loss_scale, grad_out=G)
+    torch.cuda.synchronize()
+    st = Z.stats_from_tensor(stats)
+    g_s, flag, _ = oracle.reduce(sreps, loss_scale=w.loss_scale, nthreads=NTHREADS)
+    assert st.overflow == 0 and flag == 0
+    gg = to_host(gather(G, idx_t))
+    assert np.array_equal(gg.view(np.uint32), g_s.view(np.uint32)), "reduced g differs on samples"
+    total = 0.0
+    for c0 in range(0, S, 1 << 28):
+        total += float(torch.sum(G[c0:c0 + (1 << 28)].double() ** 2).item())
+    assert sumsq_close(st.sumsq, total, 1e-9), (st.sumsq, total)
+    # unfused update over a sub-range equals the fused kernel on the same sub-range
+    n = min(S, sub_elems)
+    say(f"{w.name}: fused vs unfused over the first {n} elements")
+    P0 = step.p[0][:n]
+    Zr = torch.zeros(n, dtype=torch.float32, device=dev)
+    outs_u = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3)]
+    slot_u = torch.empty(n, dtype=torch.int16, device=dev)
+    a = Z.make_adam_args(grad_f32=G[:n], p_in=P0, m_in=Zr, v_in=Zr, p_out=outs_u[0], m_out=outs_u[1],
+                         v_out=outs_u[2], slot=slot_u, shard_S=n, lr=w.lr, beta1=w.beta1,
+                         beta2=w.beta2, eps=w.eps, weight_decay=w.wd, step_t=1, stats=stats,
+                         workspace=ws)
+    Z.zero_adam_step(a)
+    outs_f = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3)]
+    slot_f = torch.empty(n, dtype=torch.int16, device=dev)
+    a = Z.make_adam_args(replicas=[r[:n] for r in dreps], grad_dtype=Z.ZERO_BF16, p_in=P0, m_in=Zr,
+                         v_in=Zr, p_out=outs_f[0], m_out=outs_f[1], v_out=outs_f[2], slot=slot_f,
+                         shard_S=n, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                         weight_decay=w.wd, loss_scale=w.loss_scale, step_t=1, stats=stats,
+                         workspace=ws)
+    Z.zero_adam_step(a)
+    torch.cuda.synchronize()
+    for x, y in zip(outs_u + [slot_u], outs_f + [slot_f]):
+        assert torch.equal(x, y)
+    del G, outs_u, outs_f, slot_u, slot_f, Zr
+    torch.cuda.empty_cache()
+
+
+def test_llama7b_shard_full_size(Z):
+    run_large(Z, "llama7b", steps=W.get("llama7b").steps, n_random=400_000, sub_elems=1 << 28)
+
+
+def test_llama70b_shard_full_size(Z):
+    free, total = torch.cuda.mem_get_info()
+    need = 215 * (1 << 30)
+    if free < need:
+        pytest.skip(f"needs ~215 GiB of free device memory, {free / 2**30:.0f} GiB free")
+    run_large(Z, "llama70b", steps=W.get("llama70b").steps, n_random=300_000, sub_elems=1 << 27)

@@ -25,15 +25,25 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(out: str = LIB, extra=()) -> str:
-    """Compile every source into ``out`` (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs,
-           "-o", out + ".tmp"]
+PROBE = os.path.join(PKG, "hbm_probe")
+
+
+def _run(cmd):
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + proc.stdout + proc.stderr)
+
+
+def build(out: str = LIB, extra=(), probe: bool = True) -> str:
+    """Compile every source into ``out`` (always recompiles), and the HBM probe."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    _run([hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs,
+          "-o", out + ".tmp"])
     os.replace(out + ".tmp", out)
+    if probe:
+        flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+        _run([hipcc(), *flags, os.path.join(CSRC, "hbm_probe.hip"), "-o", PROBE + ".tmp"])
+        os.replace(PROBE + ".tmp", PROBE)
     return out
 
 
