@@ -1,6 +1,6 @@
 """Plain CPU oracle for the per-rank ZeRO stage-1/2 shard step.
 
-TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check (``smoke()``) and the
 ``cpu_baseline`` leg of ``bench.py`` are the only callers. The GPU product path
 (``zero_partitioned_optimizer_amd``) never imports this package, and this package
 never imports it: the two share no code.

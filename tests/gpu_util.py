@@ -80,7 +80,7 @@ def max_rel(got: np.ndarray, want: np.ndarray) -> float:
 
 
 def check_state(prefix, got_p, got_m, got_v, got_slot, p, m, v, slot):
-    """Spec acceptance: p, m, v within 1e-6 relative, slot within 1 bf16 ulp.
+    """Acceptance: p, m, v within 1e-6 relative, slot within 1 bf16 ulp.
     The implementation is expected bit-exact, so report that too."""
     for name, g, w in (("p", got_p, p), ("m", got_m, m), ("v", got_v, v)):
         r = max_rel(g, w)

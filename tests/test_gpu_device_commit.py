@@ -1,8 +1,8 @@
 """GPU parity of the device-commit step (zero_train_step) against the oracle.
 
 The commit rule runs on the GPU: the fused kernel reads the committed-state
-record (current set, t, loss scale, beta^t) and a commit kernel applies the skip
-rule. These tests compare the committed state after every step with the
+record (current set, t, loss scale, beta^t) and its last workgroup applies the
+skip rule. These tests compare the committed state after every step with the
 oracle's multi-step rule (bit for bit), queue many steps with no host
 synchronization in between (an overflow injected mid-chain), and check that the
 device path equals the host-commit path.
