@@ -167,8 +167,8 @@ typedef struct {
 } zero_stats;
 
 /*
- * Bytes of device workspace a reduce or Adam call needs (per-block fp64
- * partials, at most a few tens of KiB). The same workspace may be reused by
+ * Bytes of device workspace a reduce, Adam or train-step call needs (per-workgroup
+ * fp64 partials; 384 KiB). The same workspace may be reused by
  * consecutive calls on one stream; calls that run concurrently need their own.
  */
 size_t zero_workspace_bytes(int64_t shard_S);
@@ -305,18 +305,22 @@ typedef struct {
     uint32_t cur;                  /* 0/1: which state set holds the committed state */
     uint32_t dynamic;              /* nonzero: halve the loss scale on overflow */
     uint32_t last_overflow;
-    uint32_t ticket;               /* internal: workgroups done in the running step; 0 between steps */
+    uint32_t seq;                  /* steps run on this record (committed or skipped) */
 } zero_device_state;
 
 /*
- * Enqueue the initialisation of a device state record (a one-thread kernel, no
- * memset): t = 0, beta^0 = 1, set 0 current. beta1, beta2 in [0, 1); loss_scale
- * finite > 0; min_loss_scale in (0, loss_scale]. Errors: ZERO_E_INVAL,
- * ZERO_E_ALIGN, ZERO_E_HIP.
+ * Enqueue the initialisation of a device state record (a small kernel, no
+ * memset): t = 0, seq = 0, beta^0 = 1, set 0 current; and the clearing of the
+ * workspace (workspace_dev, ws_bytes) that the record's steps will use. That
+ * workspace belongs to the record from then on: the record's steps tag the
+ * partials they leave in it with their step number, and another call using the
+ * same workspace in between could leave stale words behind. beta1, beta2 in
+ * [0, 1); loss_scale finite > 0; min_loss_scale in (0, loss_scale].
+ * Errors: ZERO_E_INVAL, ZERO_E_ALIGN, ZERO_E_HIP.
  */
-int zero_device_state_init(zero_device_state* state_dev, double beta1, double beta2,
-                           double loss_scale, double min_loss_scale, int32_t dynamic,
-                           void* stream);
+int zero_device_state_init(zero_device_state* state_dev, void* workspace_dev, size_t ws_bytes,
+                           double beta1, double beta2, double loss_scale, double min_loss_scale,
+                           int32_t dynamic, void* stream);
 
 typedef struct {
     const void* const* replicas;   /* host array of n_replicas device pointers, slot order */
@@ -344,10 +348,14 @@ typedef struct {
  * One whole step of this rank's shard with the commit on the device: the fused
  * pass of zero_adam_step (fold in slot order, average and unscale, overflow flag
  * and squared norm, Adam/AdamW, bf16 slot), reading set state->cur and writing
- * the other set; the last workgroup to finish folds the per-workgroup partials
- * and applies the skip rule of zero_commit_rule to *state_dev (clean: t += 1 and
- * the written set becomes current; overflow: nothing committed, dynamic loss
- * scale halved). With a single slot the candidate bf16 values go straight into
+ * the other set; every workgroup leaves a partial tagged with the step's number
+ * in the workspace, and workgroup 0 waits for all of them, folds them in
+ * workgroup order and applies the skip rule of zero_commit_rule to *state_dev
+ * (clean: t += 1 and the written set becomes current; overflow: nothing
+ * committed, dynamic loss scale halved). The wait is bounded (2 s); should it run
+ * out, which a correct launch never does, nothing is committed and the stats
+ * read overflow = 1, bad_buckets = 0xFFFFFFFF. The workspace must be the one
+ * given to zero_device_state_init. With a single slot the candidate bf16 values go straight into
  * it and a second kernel restores it from the current master after an overflow;
  * with a double-buffered slot the candidate goes into slot[1 - cur] and the
  * commit flips it with the state sets, so a step is one kernel. Same arithmetic

@@ -138,14 +138,43 @@ def test_queued_chain_with_overflow(Z, double_slot):
 
 
 def test_record_init_and_validation(Z):
-    rec = torch.zeros(128, dtype=torch.uint8, device="cuda")
-    Z.zero_device_state_init(rec, 0.8, 0.95, 512.0, 2.0, True)
+    rec = torch.full((128,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws = torch.full((Z.zero_workspace_bytes(1 << 20),), 0x77, dtype=torch.uint8, device="cuda")
+    Z.zero_device_state_init(rec, ws, 0.8, 0.95, 512.0, 2.0, True)
     r = Z.device_state_from_tensor(rec)
     assert (r.beta1, r.beta2, r.beta1_pow, r.beta2_pow) == (0.8, 0.95, 1.0, 1.0)
     assert (r.loss_scale, r.min_loss_scale, r.t, r.n_skipped, r.cur, r.dynamic) == (512.0, 2.0, 0, 0, 0, 1)
+    assert (r.seq, r.last_overflow) == (0, 0)
+    assert not bool(ws.any().item()), "the workspace is cleared"
     with pytest.raises(Z.ZeroError):
-        Z.zero_device_state_init(rec, 1.0, 0.9, 1.0)
+        Z.zero_device_state_init(rec, ws, 1.0, 0.9, 1.0)
     with pytest.raises(Z.ZeroError):
-        Z.zero_device_state_init(rec[8:], 0.9, 0.9, 1.0)
+        Z.zero_device_state_init(rec[8:], ws, 0.9, 0.9, 1.0)
     with pytest.raises(Z.ZeroError):
-        Z.zero_device_state_init(rec, 0.9, 0.9, 1.0, min_loss_scale=2.0)
+        Z.zero_device_state_init(rec, ws, 0.9, 0.9, 1.0, min_loss_scale=2.0)
+
+
+def test_stale_workspace_from_an_earlier_record(Z):
+    """A workspace that an earlier record left holding partials tagged 1, 2, ... is
+    cleared by the next record's init, so its first step cannot take them for its
+    own: two records run back to back on one workspace match the oracle."""
+    S, N = 200_003, 4
+    rng = np.random.default_rng(3)
+    hy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    ws = torch.empty(Z.zero_workspace_bytes(S), dtype=torch.uint8, device="cuda")
+    for run in range(2):
+        reps = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * 1e-3)) for _ in range(N)]
+        p0 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+        step = Z.DeviceShardStep(S, N, Z.ZERO_BF16, to_dev(p0), weight_decay=0.0, **hy)
+        step.ws = ws
+        Z.zero_device_state_init(step.record, ws, 0.9, 0.999, 1.0)
+        dreps = [to_dev(r) for r in reps]
+        tr = oracle.Trainer(p0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
+                            oracle.f32_to_bf16(p0), wd=0.0, nthreads=NTHREADS, **hy)
+        for k in range(2):
+            step.step(dreps)
+            tr.step(reps)
+        P, M, V = step.committed()
+        check_state(f"record {run}", to_host(P), to_host(M), to_host(V), to_host(step.current_slot()),
+                    tr.p, tr.m, tr.v, tr.slot)
+        assert step.state().seq == 2

@@ -243,7 +243,10 @@ def test_train_step_validation(Z):
     assert call(replicas=[]) == -3
     assert call(p=(FAKE + 4, FAKE + 4096)) == -2
     L = Z.lib()
-    assert L.zero_device_state_init(None, 0.9, 0.999, 1.0, 1.0, 0, None) == -1
-    assert L.zero_device_state_init(FAKEREC + 4, 0.9, 0.999, 1.0, 1.0, 0, None) == -2
-    assert L.zero_device_state_init(FAKEREC, 0.9, 1.5, 1.0, 1.0, 0, None) == -1
-    assert L.zero_device_state_init(FAKEREC, 0.9, 0.999, float("inf"), 1.0, 0, None) == -1
+    WS = FAKE + 32768
+    assert L.zero_device_state_init(None, WS, 4096, 0.9, 0.999, 1.0, 1.0, 0, None) == -1
+    assert L.zero_device_state_init(FAKEREC, None, 4096, 0.9, 0.999, 1.0, 1.0, 0, None) == -1
+    assert L.zero_device_state_init(FAKEREC + 4, WS, 4096, 0.9, 0.999, 1.0, 1.0, 0, None) == -2
+    assert L.zero_device_state_init(FAKEREC, WS, 4096, 0.9, 1.5, 1.0, 1.0, 0, None) == -1
+    assert L.zero_device_state_init(FAKEREC, WS, 4096, 0.9, 0.999, float("inf"), 1.0, 0, None) == -1
+    assert L.zero_device_state_init(FAKEREC, FAKEREC - 64, 4096, 0.9, 0.999, 1.0, 1.0, 0, None) == -1

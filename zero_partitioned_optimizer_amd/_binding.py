@@ -74,7 +74,7 @@ class zero_device_state(ctypes.Structure):
     _fields_ = [("beta1", f64), ("beta2", f64), ("beta1_pow", f64), ("beta2_pow", f64),
                 ("loss_scale", f64), ("min_loss_scale", f64), ("last_sumsq", f64),
                 ("t", i64), ("n_skipped", i64), ("cur", u32), ("dynamic", u32),
-                ("last_overflow", u32), ("ticket", u32)]
+                ("last_overflow", u32), ("seq", u32)]
 
 
 class zero_train_args(ctypes.Structure):
@@ -117,7 +117,7 @@ def lib() -> ctypes.CDLL:
     L.zero_adam_step.argtypes = [P(zero_adam_args), vp]
     L.zero_gather_slot.argtypes = [vp, i64, vp, vp]
     L.zero_commit_rule.argtypes = [P(zero_train_state), P(zero_stats)]
-    L.zero_device_state_init.argtypes = [vp, f64, f64, f64, f64, i32, vp]
+    L.zero_device_state_init.argtypes = [vp, vp, sz, f64, f64, f64, f64, i32, vp]
     L.zero_train_step.argtypes = [P(zero_train_args), vp]
     L.zero_last_error.argtypes = []
     L.zero_last_error.restype = ctypes.c_char_p
@@ -302,10 +302,12 @@ def zero_commit_rule(state: zero_train_state, stats_host: zero_stats) -> int:
     return _check(lib().zero_commit_rule(ctypes.byref(state), ctypes.byref(stats_host)))
 
 
-def zero_device_state_init(state, beta1: float, beta2: float, loss_scale: float,
+def zero_device_state_init(state, workspace, beta1: float, beta2: float, loss_scale: float,
                            min_loss_scale: float = 1.0, dynamic: bool = False, stream=None) -> None:
-    _check(lib().zero_device_state_init(_addr(state), float(beta1), float(beta2), float(loss_scale),
-                                        float(min_loss_scale), int(bool(dynamic)), _stream(stream)))
+    ws = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    _check(lib().zero_device_state_init(_addr(state), _addr(workspace), ws, float(beta1),
+                                        float(beta2), float(loss_scale), float(min_loss_scale),
+                                        int(bool(dynamic)), _stream(stream)))
 
 
 def make_train_args(*, replicas, grad_dtype: int, p, m, v, slot=None, shard_S: int, buckets=None,

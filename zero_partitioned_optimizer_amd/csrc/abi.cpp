@@ -145,7 +145,7 @@ int check_common(const char* fn, int64_t S, const zero_bucket* buckets, int64_t 
         set_error("%s: stats_dev or workspace_dev is not 16-byte aligned", fn);
         return ZERO_E_ALIGN;
     }
-    const size_t need = (size_t)zk::grid_for(S, n_buckets, n_rep) * sizeof(zk::Partial);
+    const size_t need = (size_t)zk::grid_for(S, n_buckets, n_rep) * zk::kPartialBytes;
     if (ws_bytes < need) {
         set_error("%s: workspace of %zu bytes < %zu needed", fn, ws_bytes, need);
         return ZERO_E_RANGE;
@@ -165,7 +165,7 @@ const char* zero_version(void) { return "libzero 1.0 (gfx950)"; }
 
 size_t zero_workspace_bytes(int64_t shard_S) {
     (void)shard_S;
-    return (size_t)zk::kGridMax * sizeof(zk::Partial);
+    return (size_t)zk::kGridMax * zk::kPartialBytes;
 }
 
 int zero_reduce_shard(const void* const* replicas, int32_t n_replicas, zero_dtype grad_dtype,
@@ -330,17 +330,22 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
     return hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
 }
 
-int zero_device_state_init(zero_device_state* state_dev, double beta1, double beta2,
-                           double loss_scale, double min_loss_scale, int32_t dynamic,
-                           void* stream) {
+int zero_device_state_init(zero_device_state* state_dev, void* workspace_dev, size_t ws_bytes,
+                           double beta1, double beta2, double loss_scale, double min_loss_scale,
+                           int32_t dynamic, void* stream) {
     static const char* fn = "zero_device_state_init";
-    if (!state_dev) {
-        set_error("%s: state_dev is NULL", fn);
+    if (!state_dev || !workspace_dev) {
+        set_error("%s: state_dev or workspace_dev is NULL", fn);
         return ZERO_E_INVAL;
     }
-    if (!aligned16(state_dev)) {
-        set_error("%s: state_dev is not 16-byte aligned", fn);
+    if (!aligned16(state_dev) || !aligned16(workspace_dev)) {
+        set_error("%s: state_dev or workspace_dev is not 16-byte aligned", fn);
         return ZERO_E_ALIGN;
+    }
+    if (overlap(span("state", state_dev, (int64_t)sizeof(zero_device_state)),
+                span("workspace", workspace_dev, (int64_t)ws_bytes))) {
+        set_error("%s: state_dev and workspace_dev overlap", fn);
+        return ZERO_E_INVAL;
     }
     if (!finite_in(beta1, 0.0, 1.0) || !finite_in(beta2, 0.0, 1.0) ||
         !(isfinite(loss_scale) && loss_scale > 0) ||
@@ -350,7 +355,8 @@ int zero_device_state_init(zero_device_state* state_dev, double beta1, double be
         return ZERO_E_INVAL;
     }
     return hip_status(zk::launch_state_init(state_dev, beta1, beta2, loss_scale, min_loss_scale,
-                                            dynamic ? 1u : 0u, static_cast<hipStream_t>(stream)),
+                                            dynamic ? 1u : 0u, workspace_dev, ws_bytes,
+                                            static_cast<hipStream_t>(stream)),
                       fn);
 }
 

@@ -85,6 +85,7 @@ struct Res {
     float* m_out;
     float* v_out;
     uint16_t* slot;                         // where the bf16 result goes, or nullptr
+    uint32_t tag;                           // device-commit: number of this step (record seq + 1)
 };
 
 // ---------------------------------------------------------------------------
@@ -237,6 +238,7 @@ __device__ __forceinline__ Res resolve(const KParams& a) {
         r.m_out = a.m_out;
         r.v_out = a.v_out;
         r.slot = a.slot;
+        r.tag = 0u;
     } else {
         const zero_device_state* c = a.ctrl;
         const uint32_t cur = c->cur & 1u, nxt = cur ^ 1u;
@@ -258,6 +260,7 @@ __device__ __forceinline__ Res resolve(const KParams& a) {
         r.v_out = a.set_v[nxt];
         // a double-buffered slot takes the candidate in the out buffer, like the state
         r.slot = a.set_slot[1] ? a.set_slot[nxt] : a.slot;
+        r.tag = c->seq + 1u;
     }
     return r;
 }
@@ -441,22 +444,73 @@ __device__ __forceinline__ void commit_record(zero_device_state* c, zero_stats* 
     }
 }
 
+// Workgroup 0 of a device-commit launch: wait for every workgroup's tagged
+// partial, fold them in workgroup order (thread t takes partials t, t + 256, ...,
+// then the fixed tree of block_reduce) and commit. The wait is bounded by
+// kCollectTimeout ticks of the 100 MHz real-time counter; if it runs out (which a
+// correct launch never does) nothing is committed and the stats carry the marker
+// bad_buckets = 0xFFFFFFFF.
+constexpr uint64_t kCollectTimeout = 200000000ull;   // 2 s
+
+__device__ __noinline__ void collect_and_commit(const uint64_t* base, zero_stats* stats,
+                                               zero_device_state* c, uint32_t tag) {
+    const int n = (int)gridDim.x;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool timed_out = false;
+    double sq = 0.0;
+    uint32_t bad = 0u, badb = 0u;
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        uint64_t w0, w1, w2;
+        for (;;) {
+            w0 = __hip_atomic_load(base + 3 * (int64_t)i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            w1 = __hip_atomic_load(base + 3 * (int64_t)i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            w2 = __hip_atomic_load(base + 3 * (int64_t)i + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)(w0 >> 32) == tag && (uint32_t)(w1 >> 32) == tag && (uint32_t)(w2 >> 32) == tag)
+                break;
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kCollectTimeout) {
+                timed_out = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+        if (timed_out) break;
+        const uint64_t bits = ((w0 & 0xffffffffull) << 32) | (w1 & 0xffffffffull);
+        sq += __longlong_as_double((long long)bits);
+        bad |= (uint32_t)(w2 & 1u);
+        badb += (uint32_t)(w2 & 0xffffffffull) >> 1;
+    }
+    uint32_t tmo = timed_out ? 1u : 0u;
+    block_reduce(sq, bad, badb);
+    // every thread's time-out flag reaches thread 0 through the same tree
+    __shared__ uint32_t s_tmo[kBlock / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) tmo |= __shfl_xor(tmo, off, 64);
+    if ((threadIdx.x & 63) == 0) s_tmo[threadIdx.x >> 6] = tmo;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 0; w < kBlock / 64; ++w) tmo |= s_tmo[w];
+        if (tmo) {
+            stats->overflow = 1u;
+            stats->bad_buckets = 0xffffffffu;
+            stats->sumsq = __longlong_as_double(0x7ff8000000000000ll);
+            c->last_overflow = 1u;
+        } else {
+            commit_record(c, stats, sq, bad, badb);
+        }
+        c->seq = tag;
+    }
+}
+
 template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL, int ROWS>
 __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
     const Res rs = resolve<CTRL>(a);
     double sq = 0.0;
     uint32_t bad = 0u, badb = 0u;
-    // Device-commit launches hold back the stores of their last trip until the
-    // workgroup's partial is published (see below); others store as they go.
-    constexpr bool kDefer = CTRL && !BUCKETS && ADAM;
-    Outs<ROWS> last;
-    int64_t last_q = -1;
     if constexpr (!BUCKETS) {
         const int64_t nq = a.S >> 2;
         const int64_t per_trip = (int64_t)ROWS * kBlock;
         const int64_t ntrips = nq / per_trip;
-        int64_t trip = blockIdx.x;
-        for (; trip + (kDefer ? (int64_t)gridDim.x : 0) < ntrips; trip += gridDim.x)
+        for (int64_t trip = blockIdx.x; trip < ntrips; trip += gridDim.x)
             quads<RT, ADAM, WRITE_G, ROWS>(a, rs, trip * per_trip + threadIdx.x, kBlock, sq, bad);
         // whole quads after the last full trip, and the last S % 4 elements
         if ((int64_t)blockIdx.x == ntrips % gridDim.x) {
@@ -464,12 +518,6 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
                 quads<RT, ADAM, WRITE_G, 1>(a, rs, q, 0, sq, bad);
             const int64_t e = nq * 4 + threadIdx.x;
             if (e < a.S) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
-        }
-        if constexpr (kDefer) {
-            if (trip < ntrips) {
-                last_q = trip * per_trip + threadIdx.x;
-                quads_compute<RT, ADAM, WRITE_G, ROWS>(a, rs, last_q, kBlock, sq, bad, last);
-            }
         }
     } else {
         for (int64_t b = blockIdx.x; b < a.n_buckets; b += gridDim.x) {
@@ -492,50 +540,27 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
             a.partials[blockIdx.x] = pt;
         }
     } else {
-        // The last workgroup to take a ticket folds every partial and commits. No
-        // cache writeback is needed: the partial goes out as agent-scope atomic
-        // stores (written through to the coherence point shared by all XCDs), a
-        // waitcnt orders their completion before the ticket increment, and the
-        // last workgroup reads the partials with agent-scope atomic loads. The
-        // commit needs only the partials; the output stores still in flight
-        // complete before the kernel does, ahead of any later launch.
-        __shared__ uint32_t s_last;
+        // Each workgroup publishes its partial as three 64-bit agent-scope atomic
+        // stores (written through to the coherence point all XCDs share), each
+        // word tagged with this step's number, and leaves at once: no wait, no
+        // counter. Workgroup 0 -- dispatched first, so never starved of a CU --
+        // then polls the partials in workgroup order until every word carries the
+        // tag, sums them in that fixed order and commits the record. A word with
+        // an older tag is a partial not yet arrived; 64-bit aligned stores and
+        // loads are single-copy atomic, so no word is ever seen half written.
         if (threadIdx.x == 0) {
-            uint64_t* slot2 = reinterpret_cast<uint64_t*>(a.partials + blockIdx.x);
-            __hip_atomic_store(slot2, (uint64_t)__double_as_longlong(sq), __ATOMIC_RELAXED,
+            const uint64_t tag = (uint64_t)rs.tag << 32;
+            const uint64_t sqb = (uint64_t)__double_as_longlong(sq);
+            uint64_t* w = reinterpret_cast<uint64_t*>(a.partials) + 3 * (int64_t)blockIdx.x;
+            __hip_atomic_store(w + 0, tag | (sqb >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(w + 1, tag | (sqb & 0xffffffffull), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(slot2 + 1, (uint64_t)bad | ((uint64_t)badb << 32), __ATOMIC_RELAXED,
+            __hip_atomic_store(w + 2, tag | (uint64_t)((bad ? 1u : 0u) | (badb << 1)), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-            __builtin_amdgcn_s_waitcnt(0);
-            const uint32_t ticket = __hip_atomic_fetch_add(&a.ctrl_rw->ticket, 1u, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT);
-            s_last = ticket + 1u == gridDim.x ? 1u : 0u;
         }
-        // The held-back trip is stored only now, so the wait above covers stores
-        // issued a whole trip earlier rather than this trip's.
-        if constexpr (kDefer) {
-            if (last_q >= 0) quads_store<ROWS>(rs, last_q, kBlock, last);
-        }
-        __syncthreads();
-        if (s_last) {
-            double tsq = 0.0;
-            uint32_t tbad = 0u, tbadb = 0u;
-            const int n = (int)gridDim.x;
-            for (int i = threadIdx.x; i < n; i += kBlock) {
-                uint64_t* slot2 = reinterpret_cast<uint64_t*>(a.partials + i);
-                const uint64_t w0 = __hip_atomic_load(slot2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint64_t w1 = __hip_atomic_load(slot2 + 1, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-                tsq += __longlong_as_double((long long)w0);
-                tbad |= (uint32_t)w1;
-                tbadb += (uint32_t)(w1 >> 32);
-            }
-            block_reduce(tsq, tbad, tbadb);
-            if (threadIdx.x == 0) {
-                commit_record(a.ctrl_rw, a.stats, tsq, tbad, tbadb);
-                __hip_atomic_store(&a.ctrl_rw->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
+        if (blockIdx.x == 0)
+            collect_and_commit(reinterpret_cast<const uint64_t*>(a.partials), a.stats, a.ctrl_rw,
+                               rs.tag);
     }
 }
 
@@ -591,8 +616,13 @@ __global__ void __launch_bounds__(kBlock) k_restore(const zero_device_state* ctr
     cast_range((ctrl->cur & 1u) ? set_p1 : set_p0, S, slot);
 }
 
+// Record initialisation, and the clearing of the workspace its steps will use
+// (no partial may carry a tag before the record's first step).
 __global__ void k_state_init(zero_device_state* s, double beta1, double beta2, double loss_scale,
-                             double min_loss_scale, uint32_t dynamic) {
+                             double min_loss_scale, uint32_t dynamic, uint64_t* ws, int64_t ws_words) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ws_words; i += stride)
+        ws[i] = 0ull;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         s->beta1 = beta1;
         s->beta2 = beta2;
@@ -606,7 +636,7 @@ __global__ void k_state_init(zero_device_state* s, double beta1, double beta2, d
         s->cur = 0u;
         s->dynamic = dynamic;
         s->last_overflow = 0u;
-        s->ticket = 0u;
+        s->seq = 0u;
     }
 }
 
@@ -619,11 +649,10 @@ __global__ void k_state_init(zero_device_state* s, double beta1, double beta2, d
 // the occupancy) up.
 int rows_for(int32_t n_rep) { return n_rep <= 16 ? 2 : 1; }
 
-// Workgroups of the step kernel: about four times what the chip holds at once
-// (so faster CUs pick up more work), at most kGridMax, and balanced so that every
-// workgroup makes the same number of full trips (no ragged last round). Few
-// replica streams (two rows per lane, 4 waves per SIMD) settle best at 4096,
-// many (one row, 7-8 waves per SIMD) at 8192.
+// Workgroups of the step kernel: many more than the chip holds at once (short
+// workgroups, so faster CUs pick up more of the work and the tail is short), at
+// most 8192 with two rows per lane and kGridMax with one, and balanced so that
+// every workgroup makes the same number of full trips (no ragged last round).
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep) {
     if (n_buckets > 0) return (int)(n_buckets < kGridMax ? n_buckets : kGridMax);
     const int64_t per_trip = (int64_t)rows_for(n_rep) * kBlock * kVec;
@@ -725,9 +754,14 @@ hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipS
 }
 
 hipError_t launch_state_init(zero_device_state* s, double beta1, double beta2, double loss_scale,
-                             double min_loss_scale, uint32_t dynamic, hipStream_t st) {
-    hipLaunchKernelGGL(k_state_init, dim3(1), dim3(64), 0, st, s, beta1, beta2, loss_scale,
-                       min_loss_scale, dynamic);
+                             double min_loss_scale, uint32_t dynamic, void* ws, size_t ws_bytes,
+                             hipStream_t st) {
+    const int64_t words = (int64_t)(ws_bytes / 8);
+    int64_t grid = (words + kBlock - 1) / kBlock;
+    if (grid < 1) grid = 1;
+    if (grid > 64) grid = 64;
+    hipLaunchKernelGGL(k_state_init, dim3((unsigned)grid), dim3(kBlock), 0, st, s, beta1, beta2,
+                       loss_scale, min_loss_scale, dynamic, static_cast<uint64_t*>(ws), words);
     return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@
 namespace zk {
 
 #ifndef ZERO_GRID_MAX
-#define ZERO_GRID_MAX 8192
+#define ZERO_GRID_MAX 16384
 #endif
 
 constexpr int kBlock = 256;         // threads per workgroup: 4 wave64s
@@ -26,6 +26,10 @@ struct Partial {
     uint32_t bad_buckets;
 };
 static_assert(sizeof(Partial) == 16, "partials are 16 bytes");
+
+// Workspace bytes per workgroup: a 16-byte Partial (host commit), or three
+// tagged 64-bit words (device commit).
+constexpr size_t kPartialBytes = 24;
 
 // fp32 scalars of one update, each rounded once from double on the host.
 struct Scalars {
@@ -69,6 +73,7 @@ int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep);
 hipError_t launch_step(const StepDesc& d, hipStream_t stream);
 hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t stream);
 hipError_t launch_state_init(zero_device_state* s, double beta1, double beta2, double loss_scale,
-                             double min_loss_scale, uint32_t dynamic, hipStream_t stream);
+                             double min_loss_scale, uint32_t dynamic, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 }  // namespace zk

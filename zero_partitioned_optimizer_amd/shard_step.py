@@ -157,7 +157,8 @@ class DeviceShardStep:
         self.stats = torch.zeros(16, dtype=torch.uint8, device=dev)
         self.record = torch.zeros(128, dtype=torch.uint8, device=dev)
         self.ws = torch.empty(B.zero_workspace_bytes(S), dtype=torch.uint8, device=dev)
-        B.zero_device_state_init(self.record, beta1, beta2, loss_scale, min_loss_scale, dynamic)
+        B.zero_device_state_init(self.record, self.ws, beta1, beta2, loss_scale, min_loss_scale,
+                                 dynamic)
         B.zero_gather_slot(self.p[0], S, self.slot)
         self._args = None
         self._args_key = None
