@@ -168,7 +168,7 @@ typedef struct {
 
 /*
  * Bytes of device workspace a reduce, Adam or train-step call needs (per-workgroup
- * fp64 partials; 384 KiB). The same workspace may be reused by
+ * fp64 partials; 3 MiB). The same workspace may be reused by
  * consecutive calls on one stream; calls that run concurrently need their own.
  */
 size_t zero_workspace_bytes(int64_t shard_S);

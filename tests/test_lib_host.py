@@ -250,3 +250,4 @@ def test_train_step_validation(Z):
     assert L.zero_device_state_init(FAKEREC, WS, 4096, 0.9, 1.5, 1.0, 1.0, 0, None) == -1
     assert L.zero_device_state_init(FAKEREC, WS, 4096, 0.9, 0.999, float("inf"), 1.0, 0, None) == -1
     assert L.zero_device_state_init(FAKEREC, FAKEREC - 64, 4096, 0.9, 0.999, 1.0, 1.0, 0, None) == -1
+

@@ -650,9 +650,10 @@ __global__ void k_state_init(zero_device_state* s, double beta1, double beta2, d
 int rows_for(int32_t n_rep) { return n_rep <= 16 ? 2 : 1; }
 
 // Workgroups of the step kernel: many more than the chip holds at once (short
-// workgroups, so faster CUs pick up more of the work and the tail is short), at
-// most 8192 with two rows per lane and kGridMax with one, and balanced so that
-// every workgroup makes the same number of full trips (no ragged last round).
+// workgroups, so faster CUs pick up more of the work and the tail is short;
+// one trip each up to about 134M elements), at most kGridMax / 2 with two rows
+// per lane and kGridMax with one, and balanced so that every workgroup makes
+// the same number of full trips (no ragged last round).
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep) {
     if (n_buckets > 0) return (int)(n_buckets < kGridMax ? n_buckets : kGridMax);
     const int64_t per_trip = (int64_t)rows_for(n_rep) * kBlock * kVec;

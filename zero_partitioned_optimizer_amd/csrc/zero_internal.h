@@ -10,7 +10,7 @@
 namespace zk {
 
 #ifndef ZERO_GRID_MAX
-#define ZERO_GRID_MAX 16384
+#define ZERO_GRID_MAX 131072
 #endif
 
 constexpr int kBlock = 256;         // threads per workgroup: 4 wave64s

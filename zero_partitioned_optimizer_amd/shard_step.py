@@ -35,7 +35,8 @@ class ShardStep:
         assert p0.dtype == torch.float32 and p0.numel() == S and p0.is_contiguous()
         self.S, self.N, self.grad_dtype = S, int(n_replicas), int(grad_dtype)
         self.hyper = dict(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay)
-        self.p = [p0.clone(), torch.zeros_like(p0)]   # zeros: bucket steps skip padding
+        # zeros: bucket-table steps leave padding untouched
+        self.p = [p0.clone(), torch.zeros_like(p0)]
         self.m = [torch.zeros_like(p0), torch.zeros_like(p0)]
         self.v = [torch.zeros_like(p0), torch.zeros_like(p0)]
         self.cur = 0
