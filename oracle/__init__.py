@@ -32,6 +32,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 F32 = 0
 BF16 = 1
+BF16_WIRE = 2      # bf16 replicas, running sum rounded to bf16 after every add
 
 GCC_FLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
              "-fopenmp", "-fPIC", "-shared"]
@@ -75,6 +76,8 @@ def load(path: str) -> ctypes.CDLL:
     for name in ("or_ring_rs", "or_ring_rs_walk"):
         getattr(L, name).argtypes = [vp, i64, i64, vp, vp, vp, vp]
         getattr(L, name).restype = ctypes.c_int
+    L.or_ring_rs_wire.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
+    L.or_ring_rs_wire.restype = ctypes.c_int
     L.or_ring_ag.argtypes = [vp, i64, i64, vp, vp, vp]
     L.or_ring_ag.restype = ctypes.c_int
     L.or_bf16_to_f32.argtypes = [ctypes.c_uint16]
@@ -164,12 +167,13 @@ class Layout:
 # ring collectives (message-passing simulation)
 # ---------------------------------------------------------------------------
 
-def ring_reduce_scatter(bufs: np.ndarray, walk: bool = False):
+def ring_reduce_scatter(bufs: np.ndarray, walk: bool = False, wire: str = "f32"):
     """bufs: (N, N*S) float32, rank k's full local buffer in row k.
 
     Returns (chunks (N, S) float32 -- chunk c as held by its owner c,
     sent (N,), recv (N,), order (N, N) -- order[c] = ranks in the order their
-    data entered chunk c). walk=True runs the literal one-extra-hop walk."""
+    data entered chunk c). walk=True runs the literal one-extra-hop walk.
+    wire="bf16" holds and sends every running partial in bf16 (standard ring)."""
     bufs = np.ascontiguousarray(bufs, dtype=np.float32)
     N = bufs.shape[0]
     S = bufs.shape[1] // N
@@ -178,8 +182,13 @@ def ring_reduce_scatter(bufs: np.ndarray, walk: bool = False):
     sent = np.zeros(N, dtype=np.int64)
     recv = np.zeros(N, dtype=np.int64)
     order = np.full((N, N), -1, dtype=np.int64)
-    fn = lib().or_ring_rs_walk if walk else lib().or_ring_rs
-    if fn(_ptr(bufs), N, S, _ptr(out), _ptr(sent), _ptr(recv), _ptr(order)) != 0:
+    assert wire in ("f32", "bf16") and not (walk and wire != "f32")
+    if walk:
+        rc = lib().or_ring_rs_walk(_ptr(bufs), N, S, _ptr(out), _ptr(sent), _ptr(recv), _ptr(order))
+    else:
+        rc = lib().or_ring_rs_wire(_ptr(bufs), N, S, 1 if wire == "bf16" else 0, _ptr(out),
+                                   _ptr(sent), _ptr(recv), _ptr(order))
+    if rc != 0:
         raise RuntimeError("ring simulation failed")
     return out, sent, recv, order
 
@@ -223,7 +232,8 @@ def adam_scalars(lr, beta1, beta2, eps, wd, t) -> np.ndarray:
     return out
 
 
-def _rep_table(reps):
+def _rep_table(reps, wire: bool = False):
+    """wire=True: bf16 replicas folded as a bf16 ring does (each partial rounded)."""
     reps = [np.ascontiguousarray(r) for r in reps]
     dt = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16}
     kinds = {dt[r.dtype] for r in reps}
@@ -231,15 +241,20 @@ def _rep_table(reps):
     n = reps[0].size
     assert all(r.size == n for r in reps)
     table = (ctypes.c_void_p * len(reps))(*[_ptr(r) for r in reps])
-    return reps, table, kinds.pop(), n
+    kind = kinds.pop()
+    if wire:
+        assert kind == BF16, "the bf16 wire applies to bf16 replicas"
+        kind = BF16_WIRE
+    return reps, table, kind, n
 
 
-def reduce(reps, loss_scale: float = 1.0, nthreads: int = 1):
+def reduce(reps, loss_scale: float = 1.0, nthreads: int = 1, wire: bool = False):
     """Slot-ordered fp32 left fold, times 1/(N*loss_scale).
 
     reps: list of N arrays (float32, or uint16 holding bf16 patterns).
+    wire=True rounds the running sum to bf16 after every add.
     Returns (g float32, overflow flag int, sumsq float)."""
-    reps, table, dtype, n = _rep_table(reps)
+    reps, table, dtype, n = _rep_table(reps, wire)
     g = np.zeros(n, dtype=np.float32)
     flag = ctypes.c_uint32(0)
     sumsq = ctypes.c_double(0.0)
@@ -269,9 +284,10 @@ def adam(g, p, m, v, *, lr, beta1, beta2, eps, wd, t, nthreads: int = 1):
     return po, mo, vo, slot
 
 
-def step(reps, p, m, v, slot, *, loss_scale, lr, beta1, beta2, eps, wd, t, nthreads: int = 1):
+def step(reps, p, m, v, slot, *, loss_scale, lr, beta1, beta2, eps, wd, t, nthreads: int = 1,
+         wire: bool = False):
     """One step with the skip rule, in place on p, m, v, slot. Returns (flag, sumsq)."""
-    reps, table, dtype, n = _rep_table(reps)
+    reps, table, dtype, n = _rep_table(reps, wire)
     for a, want in ((p, np.float32), (m, np.float32), (v, np.float32), (slot, np.uint16)):
         assert a.dtype == want and a.flags["C_CONTIGUOUS"] and a.size == n
     sumsq = ctypes.c_double(0.0)
@@ -289,8 +305,9 @@ class Trainer:
     were and, with a dynamic loss scale, halves the scale (never below 1)."""
 
     def __init__(self, p, m, v, slot, *, lr, beta1, beta2, eps, wd, loss_scale=1.0,
-                 dynamic=False, nthreads=1):
+                 dynamic=False, nthreads=1, wire=False):
         self.p, self.m, self.v, self.slot = p, m, v, slot
+        self.wire = bool(wire)
         self.hyper = dict(lr=lr, beta1=beta1, beta2=beta2, eps=eps, wd=wd)
         self.loss_scale = float(loss_scale)
         self.dynamic = bool(dynamic)
@@ -300,7 +317,7 @@ class Trainer:
 
     def step(self, reps):
         flag, sumsq = step(reps, self.p, self.m, self.v, self.slot, loss_scale=self.loss_scale,
-                           t=self.t + 1, nthreads=self.nthreads, **self.hyper)
+                           t=self.t + 1, nthreads=self.nthreads, wire=self.wire, **self.hyper)
         self.history.append((flag, sumsq, self.loss_scale, self.t))
         if flag:
             if self.dynamic:

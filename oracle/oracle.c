@@ -188,6 +188,8 @@ int or_mem_bytes(int64_t L_pad, int64_t S, int32_t stage, int64_t* out) {
 /* Ring collectives, simulated by message passing between N virtual ranks    */
 /* ------------------------------------------------------------------------ */
 
+static float or_hold(float x, int32_t wire_dtype);
+
 /*
  * Standard ring reduce-scatter. Rank k holds its full local gradient
  * bufs[k*N*S ...], cut into N chunks of S. In step s = 0 .. N-2 every rank k
@@ -196,23 +198,30 @@ int or_mem_bytes(int64_t L_pad, int64_t S, int32_t stage, int64_t* out) {
  * After N-1 steps chunk c sits fully reduced at its owner c:
  *   out[c*S + e]. order[c*N + h] = the rank whose data was the h-th term of
  * chunk c. sent[k] / recv[k] count elements moved by rank k.
+ * wire_dtype: the type the running partials are held and sent in. OR_F32
+ * keeps them in fp32; OR_BF16 rounds every partial to bf16 (round to nearest
+ * even) when it is formed, as a ring whose buffers and messages are bf16 does.
  */
-int or_ring_rs(const float* bufs, int64_t N, int64_t S, float* out, int64_t* sent,
-               int64_t* recv, int64_t* order) {
+int or_ring_rs_wire(const float* bufs, int64_t N, int64_t S, int32_t wire_dtype, float* out,
+                    int64_t* sent, int64_t* recv, int64_t* order) {
     if (N < 1 || S < 0) return OR_EINVAL;
     /* partial[k] = the chunk rank k currently holds a running sum of */
     float* partial = (float*)malloc(sizeof(float) * (size_t)(N * (S > 0 ? S : 1)));
     float* msg = (float*)malloc(sizeof(float) * (size_t)(N * (S > 0 ? S : 1)));
     int64_t* pchunk = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
     int64_t* nterms = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
-    if (!partial || !msg || !pchunk || !nterms) return OR_EINVAL;
+    int64_t* newchunk = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+    if (!partial || !msg || !pchunk || !nterms || !newchunk) {
+        free(partial); free(msg); free(pchunk); free(nterms); free(newchunk);
+        return OR_EINVAL;
+    }
     for (int64_t k = 0; k < N; k++) { sent[k] = 0; recv[k] = 0; }
     for (int64_t c = 0; c < N; c++) nterms[c] = 0;
     /* step "-1": rank k starts chunk (k-1) mod N with its own data */
     for (int64_t k = 0; k < N; k++) {
         int64_t c = ((k - 1) % N + N) % N;
         pchunk[k] = c;
-        memcpy(partial + k * S, bufs + k * N * S + c * S, sizeof(float) * (size_t)S);
+        for (int64_t e = 0; e < S; e++) partial[k * S + e] = or_hold(bufs[k * N * S + c * S + e], wire_dtype);
         order[c * N + nterms[c]++] = k;
     }
     for (int64_t s = 0; s + 1 < N; s++) {
@@ -224,23 +233,28 @@ int or_ring_rs(const float* bufs, int64_t N, int64_t S, float* out, int64_t* sen
             recv[dst] += S;
         }
         /* every rank adds its own copy of the chunk it just received */
-        int64_t* newchunk = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
         for (int64_t k = 0; k < N; k++) newchunk[k] = pchunk[((k - 1) % N + N) % N];
         for (int64_t k = 0; k < N; k++) {
             int64_t c = newchunk[k];
             const float* own = bufs + k * N * S + c * S;
-            for (int64_t e = 0; e < S; e++) partial[k * S + e] = msg[k * S + e] + own[e];
+            for (int64_t e = 0; e < S; e++)
+                partial[k * S + e] = or_hold(msg[k * S + e] + own[e], wire_dtype);
             pchunk[k] = c;
             order[c * N + nterms[c]++] = k;
         }
-        free(newchunk);
     }
+    int rc = OR_OK;
     for (int64_t k = 0; k < N; k++) {
-        if (pchunk[k] != k) { free(partial); free(msg); free(pchunk); free(nterms); return OR_EINVAL; }
+        if (pchunk[k] != k) { rc = OR_EINVAL; break; }
         memcpy(out + k * S, partial + k * S, sizeof(float) * (size_t)S);
     }
-    free(partial); free(msg); free(pchunk); free(nterms);
-    return OR_OK;
+    free(partial); free(msg); free(pchunk); free(nterms); free(newchunk);
+    return rc;
+}
+
+int or_ring_rs(const float* bufs, int64_t N, int64_t S, float* out, int64_t* sent,
+               int64_t* recv, int64_t* order) {
+    return or_ring_rs_wire(bufs, N, S, 0 /* fp32 */, out, sent, recv, order);
 }
 
 /*
@@ -346,16 +360,27 @@ void or_f32_to_bf16_array(const float* x, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; i++) out[i] = or_f32_to_bf16(x[i]);
 }
 
+/* x as held in a buffer of wire_dtype: unchanged for fp32, rounded to bf16 for bf16. */
+static float or_hold(float x, int32_t wire_dtype) {
+    return wire_dtype == 0 ? x : or_bf16_to_f32(or_f32_to_bf16(x));
+}
+
 /* ------------------------------------------------------------------------ */
 /* The step                                                                  */
 /* ------------------------------------------------------------------------ */
 
 #define OR_F32 0
 #define OR_BF16 1
+#define OR_BF16_WIRE 2    /* bf16 replicas summed as a bf16 ring does: each partial rounded */
 
 static float or_load(const void* base, int32_t dtype, int64_t i) {
-    if (dtype == OR_BF16) return or_bf16_to_f32(((const uint16_t*)base)[i]);
+    if (dtype == OR_BF16 || dtype == OR_BF16_WIRE) return or_bf16_to_f32(((const uint16_t*)base)[i]);
     return ((const float*)base)[i];
+}
+
+/* One hop of the fold: the fp32 sum, held in bf16 when the wire is bf16. */
+static float or_fold_add(float acc, float x, int32_t dtype) {
+    return or_hold(acc + x, dtype == OR_BF16_WIRE ? OR_BF16 : OR_F32);
 }
 
 /* 1 / (N * loss_scale), computed in double and rounded once to fp32. */
@@ -371,6 +396,10 @@ float or_inv_scale(int32_t N, double loss_scale) {
  *   flag  = 1 if any g[i] is inf or NaN
  *   sumsq = sum of (double)g[i] * (double)g[i]
  * reps[j] is the j-th slot of the slot table (its own dtype-sized array of n).
+ * dtype OR_BF16_WIRE: bf16 replicas whose running sum is rounded to bf16 after
+ * every add, what each rank of the ring walk in GuanhuaWang's reply ("Why
+ * DeepSpeed ZeRO paper says reduce-scatter ... Psi elements?") holds and sends
+ * on when its buffers are bf16; the pages leave the precision open.
  */
 void or_reduce(const void* const* reps, int32_t N, int32_t dtype, int64_t n,
                double loss_scale, float* g_out, uint32_t* flag_out, double* sumsq_out,
@@ -384,7 +413,7 @@ void or_reduce(const void* const* reps, int32_t N, int32_t dtype, int64_t n,
 #endif
     for (int64_t i = 0; i < n; i++) {
         float acc = or_load(reps[0], dtype, i);
-        for (int32_t j = 1; j < N; j++) acc = acc + or_load(reps[j], dtype, i);
+        for (int32_t j = 1; j < N; j++) acc = or_fold_add(acc, or_load(reps[j], dtype, i), dtype);
         float g = acc * inv;
         if (!isfinite(g)) flag |= 1u;
         sumsq += (double)g * (double)g;

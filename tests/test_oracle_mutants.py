@@ -21,6 +21,7 @@ import test_oracle_memory as TM
 import test_oracle_reduce as TR
 import test_oracle_ring as TG
 import test_oracle_step as TS
+import test_oracle_wire as TW
 
 MUTANTS = {
     "no_bias_correction_1": ("float mh = m1 / bc1;", "float mh = m1;"),
@@ -42,8 +43,12 @@ MUTANTS = {
     "segment_offset_wrong_base": ("out[4 * n + 1] = a - offsets[i];", "out[4 * n + 1] = a - lo;"),
     "shard_not_rounded_to_B": ("int64_t S = or_align_up(per_rank, B);", "int64_t S = per_rank;"),
     "stage2_grads_not_partitioned": ("case 2: par = P;  grd = Pn;", "case 2: par = P;  grd = P;"),
-    "ring_adds_twice": ("partial[k * S + e] = msg[k * S + e] + own[e];",
-                        "partial[k * S + e] = msg[k * S + e] + own[e] + own[e];"),
+    "ring_adds_twice": ("partial[k * S + e] = or_hold(msg[k * S + e] + own[e], wire_dtype);",
+                        "partial[k * S + e] = or_hold(msg[k * S + e] + own[e] + own[e], wire_dtype);"),
+    "wire_not_rounded": ("return or_hold(acc + x, dtype == OR_BF16_WIRE ? OR_BF16 : OR_F32);",
+                         "return acc + x;"),
+    "wire_truncates": ("return wire_dtype == 0 ? x : or_bf16_to_f32(or_f32_to_bf16(x));",
+                       "return wire_dtype == 0 ? x : or_bf16_to_f32((uint16_t)(or_bits(x) >> 16));"),
     "walk_skips_return_hop": ("for (int64_t h = 1; h <= N; h++) {", "for (int64_t h = 1; h < N; h++) {"),
     "bucket_never_cut": ("int cut = (k < S) && bucket_elems > 0 && (k % bucket_elems) == 0;",
                          "int cut = 0;"),
@@ -79,6 +84,12 @@ def all_pins(orc):
         ("bf16", lambda: TB.test_ties_and_edges(orc)),
         ("step_skip", lambda: TS.test_overflow_skips_everything(orc)),
         ("step_trainer", lambda: TS.test_trainer_dynamic_scale_and_counter(orc)),
+        ("wire_ties", lambda: TW.test_hand_computed_ties(orc)),
+        ("wire_torch", lambda: [TW.test_matches_torch_bf16_tensor_adds(orc, n) for n in (2, 8)]),
+        ("wire_ring", lambda: [TW.test_ring_with_bf16_messages_equals_wire_fold(orc, n)
+                               for n in (2, 3)]),
+        ("wire_exact", lambda: TW.test_no_rounding_when_sums_are_bf16_exact(orc)),
+        ("wire_skip", lambda: TW.test_wire_rounding_can_decide_the_skip(orc)),
     ]
     for name, fn in cases:
         try:
