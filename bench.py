@@ -57,7 +57,7 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, host_reps, p0_host, S, seconds: float):
+def cpu_baseline(w, host_reps, p0_host, S, seconds: float, wire: bool = False):
     """The oracle, as it stands, on this host: repeated steps over the shard."""
     import numpy as np
 
@@ -71,7 +71,7 @@ def cpu_baseline(w, host_reps, p0_host, S, seconds: float):
     t0 = time.perf_counter()
     while True:
         oracle.step(host_reps, p, m, v, slot, loss_scale=w.loss_scale, t=n + 1, nthreads=nthreads,
-                    **w.hyper())
+                    wire=wire, **w.hyper())
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -106,6 +106,9 @@ def main() -> int:
     ap.add_argument("--hbm-probe", action="store_true",
                     help="also run the plain-stream HBM probe (read, write, copy, 2:1 and 5:1 "
                          "read:write mixes) and report it beside the roofline")
+    ap.add_argument("--fold", default="f32", choices=["f32", "bf16-wire"],
+                    help="f32: the fold keeps its running sum in fp32; bf16-wire: rounded to "
+                         "bf16 after every add, as a ring with bf16 buffers (bf16 replicas only)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -129,6 +132,12 @@ def main() -> int:
     dev = torch.device("cuda:0")
     w = W.get(args.config)
     gdt = Z.ZERO_BF16 if w.grad_dtype == "bf16" else Z.ZERO_F32
+    wire = args.fold == "bf16-wire"
+    if wire:
+        if w.grad_dtype != "bf16":
+            print("--fold bf16-wire needs bf16 replicas", file=sys.stderr)
+            return 2
+        gdt = Z.ZERO_BF16_WIRE
     h = Z.zero_layout_build(list(w.numels), w.N, w.A, w.B)
     try:
         S = Z.zero_layout_info_get(h).shard_S
@@ -188,7 +197,7 @@ def main() -> int:
     bpe = w.N * w.grad_bytes + 26
     kernel_s = statistics.mean(kms) / 1e3
     achieved = S * bpe / kernel_s / 1e9
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name) if not wire else None
     out = {
         "metric": METRIC,
         "value": S * K / elapsed,
@@ -205,7 +214,7 @@ def main() -> int:
         "config": {"workload": f"{w.name} shard, rank {args.rank} of N={w.N}", "shard_elems": S,
                    "n_replicas": w.N, "grad_dtype": w.grad_dtype, "state_dtype": "f32",
                    "bytes_per_elem": bpe, "bucket_elems": args.bucket_elems,
-                   "commit": args.commit,
+                   "commit": args.commit, "fold": args.fold,
                    "slot": "single" if (args.single_slot or args.commit == "host") else "double"},
         "step_gbps": S * bpe / (elapsed / K) / 1e9,
         "kernel_us_mean": kernel_s * 1e6,
@@ -243,7 +252,8 @@ def main() -> int:
         for r in reps:
             x = r.cpu()
             host_reps.append(x.numpy().view(np.uint16) if w.grad_dtype == "bf16" else x.numpy())
-        out["cpu_baseline"] = cpu_baseline(w, host_reps, p0.cpu().numpy(), S, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, host_reps, p0.cpu().numpy(), S, args.cpu_seconds,
+                                           wire)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -57,7 +57,19 @@ typedef enum {
     ZERO_E_UNSUPPORTED = -6   /* a valid but unsupported combination */
 } zero_status;
 
-typedef enum { ZERO_F32 = 0, ZERO_BF16 = 1 } zero_dtype;
+/*
+ * Element type of the gradient replicas, and how the fold holds its running sum:
+ *   ZERO_F32       fp32 replicas, fp32 running sum;
+ *   ZERO_BF16      bf16 replicas, fp32 running sum (never rounded between adds);
+ *   ZERO_BF16_WIRE bf16 replicas, the running sum rounded to bf16 (nearest,
+ *                  ties to even) after every add: what each GPU of the ring walk
+ *                  in GuanhuaWang's reply ("Why DeepSpeed ZeRO paper says
+ *                  reduce-scatter (or all-gather) has data movement of Psi
+ *                  elements?") holds and passes on when its buffers are bf16.
+ *                  The pages leave that precision open; ZERO_BF16 is the default
+ *                  reading, this one reproduces a bf16 ring bit for bit.
+ */
+typedef enum { ZERO_F32 = 0, ZERO_BF16 = 1, ZERO_BF16_WIRE = 2 } zero_dtype;
 
 /* ------------------------------------------------------------------------ */
 /* Flat layout and shard cut (host only)                                      */
@@ -321,6 +333,26 @@ typedef struct {
 int zero_device_state_init(zero_device_state* state_dev, void* workspace_dev, size_t ws_bytes,
                            double beta1, double beta2, double loss_scale, double min_loss_scale,
                            int32_t dynamic, void* stream);
+
+/*
+ * Resume from a checkpoint. The committed state of a shard is p, m, v of the
+ * current set plus this record; the pages define the per-rank optimizer state
+ * as the fp32 master copy with the two Adam moments ("ZeRO Optimizer", stage 1
+ * memory terms) and nothing else, so saving those and the record is a complete
+ * checkpoint. This enqueues the writing of *saved (a host copy of a record
+ * taken after synchronizing its stream) into state_dev and the clearing of the
+ * workspace, as zero_device_state_init does; seq restarts at 0 and the other
+ * fields are kept bit for bit, so the steps that follow are identical to those
+ * of an uninterrupted run. The caller puts the saved p, m, v into set
+ * saved->cur of the zero_train_args it will pass, and rewrites its slot with
+ * zero_gather_slot from that master (into slot[saved->cur] when the slot is
+ * double-buffered). The host record is read before return.
+ * Errors: ZERO_E_INVAL (NULL, betas or loss scales as for zero_device_state_init,
+ * t or n_skipped negative, cur or last_overflow not 0/1, beta powers outside
+ * [0, 1] or not 1 at t = 0), ZERO_E_ALIGN, ZERO_E_HIP.
+ */
+int zero_device_state_load(zero_device_state* state_dev, void* workspace_dev, size_t ws_bytes,
+                           const zero_device_state* saved, void* stream);
 
 typedef struct {
     const void* const* replicas;   /* host array of n_replicas device pointers, slot order */

@@ -30,10 +30,12 @@ def bucket_table(Z, w, rank, bucket_elems):
     return torch.frombuffer(bytearray(bytes(raw)[: 16 * nb]), dtype=torch.uint8).to("cuda"), nb
 
 
-def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None, double_slot=False):
+def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None, double_slot=False, wire=False):
     lay, covered = layout_of(w, rank)
     S = lay.S
     gdt = Z.ZERO_BF16 if w.grad_dtype == "bf16" else Z.ZERO_F32
+    if wire:
+        gdt = Z.ZERO_BF16_WIRE
     p0 = W.host_params(w, S, covered, rank)
     bt, nb = bucket_table(Z, w, rank, bucket_elems) if bucket_elems else (None, 0)
     step = Z.DeviceShardStep(S, w.N, gdt, to_dev(p0), lr=w.lr, beta1=w.beta1, beta2=w.beta2,
@@ -42,10 +44,10 @@ def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None, double_slot=Fals
                              double_slot=double_slot)
     tr = oracle.Trainer(p0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
                         oracle.f32_to_bf16(p0), loss_scale=w.loss_scale, dynamic=w.dynamic_loss_scale,
-                        nthreads=NTHREADS, **w.hyper())
+                        nthreads=NTHREADS, wire=wire, **w.hyper())
     flags = []
     for s in range(w.steps if steps is None else steps):
-        say(f"device {w.name} rank={rank} step={s} buckets={nb}")
+        say(f"device {w.name} rank={rank} step={s} buckets={nb} wire={wire}")
         reps = W.host_replicas(w, S, covered, rank, s)
         step.step([to_dev(r) for r in reps])
         flag, sumsq = tr.step(reps)
@@ -77,6 +79,13 @@ def test_ragged_injection(Z, rank, bucket_elems, double_slot):
     inj = W.injection(w, lay.S, covered, rank)
     flags = run_device_protocol(Z, w, rank, bucket_elems, double_slot=double_slot)
     assert flags == [1 if s == inj[0] else 0 for s in range(w.steps)]
+
+
+@pytest.mark.parametrize("name,rank,double_slot", [("ragged", 63, True), ("gpt2s", 0, False)])
+def test_wire_device_commit(Z, name, rank, double_slot):
+    w = W.get(name)
+    run_device_protocol(Z, w, rank, double_slot=double_slot, wire=True,
+                        steps=None if name == "ragged" else 2)
 
 
 def test_gpt2_device_equals_host_commit(Z):

@@ -36,12 +36,14 @@ def read_stats(Z, stats_t):
     return Z.stats_from_tensor(stats_t)
 
 
-def run_protocol(Z, w, rank, steps=None, bucket_elems=0, device_gen=False):
+def run_protocol(Z, w, rank, steps=None, bucket_elems=0, device_gen=False, wire=False):
     """Run the workload's steps on the GPU (ShardStep) and in the oracle (Trainer),
-    comparing the committed state after every step."""
+    comparing the committed state after every step. wire: fold on a bf16 wire."""
     lay, covered = layout_of(w, rank)
     S = lay.S
     gdt = Z.ZERO_BF16 if w.grad_dtype == "bf16" else Z.ZERO_F32
+    if wire:
+        gdt = Z.ZERO_BF16_WIRE
     p0 = W.host_params(w, S, covered, rank)
     buckets_t, nb = None, 0
     if bucket_elems:
@@ -54,10 +56,10 @@ def run_protocol(Z, w, rank, steps=None, bucket_elems=0, device_gen=False):
                        buckets=buckets_t, n_buckets=nb)
     tr = oracle.Trainer(p0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
                         oracle.f32_to_bf16(p0), loss_scale=w.loss_scale, dynamic=w.dynamic_loss_scale,
-                        nthreads=NTHREADS, **w.hyper())
+                        nthreads=NTHREADS, wire=wire, **w.hyper())
     flags = []
     for s in range(w.steps if steps is None else steps):
-        say(f"{w.name} rank={rank} step={s} S={S} N={w.N} buckets={nb}")
+        say(f"{w.name} rank={rank} step={s} S={S} N={w.N} buckets={nb} wire={wire}")
         reps = W.host_replicas(w, S, covered, rank, s)
         dreps = [to_dev(r) for r in reps]
         st, verdict = step.step(dreps)
@@ -100,10 +102,17 @@ def test_ragged_inf_injection_and_dynamic_scale(Z, rank, bucket_elems):
 
 
 def single_step_case(Z, S, N, dtype, seed, *, loss_scale=1.0, t=1, wd=0.01, scale=1e-3,
-                     slot=True, fused=True, buckets=None):
-    """One fused (or reduce + unfused) step on random inputs; returns GPU and oracle results."""
+                     slot=True, fused=True, buckets=None, wire=False, reps=None):
+    """One fused (or reduce + unfused) step on random inputs; returns GPU and oracle results.
+    wire: bf16 replicas folded on a bf16 wire; reps: replicas to use instead of random ones."""
     rng = np.random.default_rng(seed)
-    if dtype == "bf16":
+    if reps is not None:
+        pass
+    elif dtype == "bf16" and wire:     # magnitudes spread over 8 decades: the wire rounds
+        reps = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * scale * loss_scale
+                                                 * 10.0 ** rng.uniform(-4, 4, size=S)))
+                for _ in range(N)]
+    elif dtype == "bf16":
         reps = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * scale * loss_scale))
                 for _ in range(N)]
     else:
@@ -112,7 +121,7 @@ def single_step_case(Z, S, N, dtype, seed, *, loss_scale=1.0, t=1, wd=0.01, scal
     m = (rng.standard_normal(S) * 1e-4).astype(np.float32) if t > 1 else np.zeros(S, np.float32)
     v = ((rng.standard_normal(S) * 1e-4) ** 2).astype(np.float32) if t > 1 else np.zeros(S, np.float32)
     hy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
-    g, flag, sumsq = oracle.reduce(reps, loss_scale=loss_scale, nthreads=NTHREADS)
+    g, flag, sumsq = oracle.reduce(reps, loss_scale=loss_scale, nthreads=NTHREADS, wire=wire)
     po, mo, vo, so = oracle.adam(g, p, m, v, t=t, wd=wd, nthreads=NTHREADS, **hy)
     dreps = [to_dev(r) for r in reps]
     P_in, M_in, V_in = to_dev(p), to_dev(m), to_dev(v)
@@ -120,7 +129,7 @@ def single_step_case(Z, S, N, dtype, seed, *, loss_scale=1.0, t=1, wd=0.01, scal
     slot_t = torch.empty(max(S, 1), dtype=torch.int16, device="cuda")[:S] if slot else None
     stats = torch.zeros(16, dtype=torch.uint8, device="cuda")
     ws = torch.empty(Z.zero_workspace_bytes(S), dtype=torch.uint8, device="cuda")
-    gdt = Z.ZERO_BF16 if dtype == "bf16" else Z.ZERO_F32
+    gdt = (Z.ZERO_BF16_WIRE if wire else Z.ZERO_BF16) if dtype == "bf16" else Z.ZERO_F32
     if fused:
         a = Z.make_adam_args(replicas=dreps, grad_dtype=gdt, p_in=P_in, m_in=M_in, v_in=V_in,
                              p_out=P_out, m_out=M_out, v_out=V_out, slot=slot_t, shard_S=S,
@@ -383,3 +392,59 @@ def test_rerun_is_bit_identical(Z):
     ws = torch.empty(Z.zero_workspace_bytes(S), dtype=torch.uint8, device="cuda")
     Z.zero_reduce_shard(dreps, Z.ZERO_BF16, S, stats, ws)
     assert read_stats(Z, stats).sumsq == sums[0]
+
+
+# --- bf16 wire: the running sum rounded to bf16 after every add ---------------
+
+@pytest.mark.parametrize("N,S", [(2, 4099), (3, 1), (8, 100_003), (8, 1_000_003), (17, 5),
+                                 (64, 262_147)])
+def test_wire_fused(Z, N, S):
+    say(f"wire fused N={N} S={S}")
+    single_step_case(Z, S, N, "bf16", seed=9000 + N, wire=True, t=3)
+
+
+@pytest.mark.parametrize("S", [1, 4097, 262_147])
+def test_wire_unfused_g_bit_exact(Z, S):
+    say(f"wire unfused S={S}")
+    single_step_case(Z, S, 8, "bf16", seed=9100 + S, wire=True, fused=False)
+
+
+def test_wire_changes_the_result_and_decides_overflow(Z):
+    """The kernel really takes the wire path: on spread magnitudes its g differs
+    from the fp32 fold's; bf16 max plus half its ulp overflows on the wire only,
+    and the NaN of an inf - inf pair is the same quiet NaN on both sides."""
+    S, N = 4096, 8
+    rng = np.random.default_rng(9200)
+    reps = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S)
+                                             * 10.0 ** rng.uniform(-4, 4, size=S))) for _ in range(N)]
+    g_w = oracle.reduce(reps, wire=True)[0]
+    g_f = oracle.reduce(reps)[0]
+    assert np.sum(g_w != g_f) > S // 4
+    stats = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(Z.zero_workspace_bytes(S), dtype=torch.uint8, device="cuda")
+    G = torch.empty(S, dtype=torch.float32, device="cuda")
+    Z.zero_reduce_shard([to_dev(r) for r in reps], Z.ZERO_BF16_WIRE, S, stats, ws, grad_out=G)
+    assert_bitexact("g wire", to_host(G), g_w)
+    # overflow on the wire only
+    r0 = np.zeros(S, np.uint16)
+    r1 = np.zeros(S, np.uint16)
+    r0[10], r1[10] = 0x7F7F, np.asarray(W._bf16_bits_from_f32(np.array([2.0 ** 119])))[0]
+    r0[20], r1[20] = 0x7F80, 0xFF80            # +inf + -inf -> NaN
+    for wire in (False, True):
+        g, flag, _ = oracle.reduce([r0, r1], wire=wire)
+        gdt = Z.ZERO_BF16_WIRE if wire else Z.ZERO_BF16
+        Z.zero_reduce_shard([to_dev(r0), to_dev(r1)], gdt, S, stats, ws, grad_out=G)
+        st = read_stats(Z, stats)
+        assert st.overflow == flag == 1
+        got = to_host(G)
+        assert np.isfinite(got[10]) == (not wire) and np.isfinite(g[10]) == (not wire)
+        # NaN sign and payload are the hardware's (x86 and gfx950 differ for inf - inf)
+        nan = np.isnan(g)
+        assert np.array_equal(np.isnan(got), nan) and nan[20]
+        assert_bitexact(f"g wire={wire}", got[~nan], g[~nan])
+
+
+@pytest.mark.parametrize("rank,bucket_elems", [(0, 0), (63, 1000)])
+def test_wire_ragged_protocol(Z, rank, bucket_elems):
+    w = W.get("ragged")
+    run_protocol(Z, w, rank, bucket_elems=bucket_elems, wire=True)

@@ -251,3 +251,33 @@ def test_train_step_validation(Z):
     assert L.zero_device_state_init(FAKEREC, WS, 4096, 0.9, 0.999, float("inf"), 1.0, 0, None) == -1
     assert L.zero_device_state_init(FAKEREC, FAKEREC - 64, 4096, 0.9, 0.999, 1.0, 1.0, 0, None) == -1
 
+
+
+def test_device_state_load_validation(Z):
+    """Rejections happen on the host, before anything is enqueued."""
+    L = Z.lib()
+    REC, WS = FAKE + 65536, FAKE + 32768
+    good = dict(beta1=0.9, beta2=0.999, beta1_pow=0.9 ** 3, beta2_pow=0.999 ** 3, loss_scale=1024.0,
+                min_loss_scale=1.0, last_sumsq=0.5, t=3, n_skipped=1, cur=1, dynamic=1,
+                last_overflow=0, seq=4)
+
+    def status(state=REC, ws=WS, **kw):
+        d = dict(good)
+        d.update(kw)
+        rec = Z.zero_device_state(**d)
+        return L.zero_device_state_load(state, ws, 4096, ctypes.byref(rec), None)
+
+    assert L.zero_device_state_load(REC, WS, 4096, None, None) == -1
+    assert status(state=None) == -1
+    assert status(state=REC + 8) == -2
+    assert status(ws=REC - 64) == -1                   # workspace overlaps the record
+    assert status(beta1=1.0) == -1
+    assert status(loss_scale=0.5) == -1                # below min_loss_scale
+    assert status(loss_scale=float("nan")) == -1
+    assert status(t=-1) == -1
+    assert status(n_skipped=-2) == -1
+    assert status(cur=2) == -1
+    assert status(last_overflow=3) == -1
+    assert status(beta2_pow=1.5) == -1
+    assert status(beta1_pow=float("nan")) == -1
+    assert status(t=0) == -1                           # beta^0 must be 1

@@ -10,12 +10,13 @@ plus ``ShardStep``, which owns buffers and applies the commit rule. There is no
 CPU fallback: without the built library every call raises.
 """
 from ._binding import (  # noqa: F401
-    ZERO_BF16, ZERO_COMMIT, ZERO_F32, ZERO_MAX_REPLICAS, ZERO_SKIP, ZeroError, lib,
+    ZERO_BF16, ZERO_BF16_WIRE, ZERO_COMMIT, ZERO_F32, ZERO_MAX_REPLICAS, ZERO_SKIP, ZeroError, lib,
     make_adam_args, stats_from_tensor, zero_adam_args, zero_adam_step, zero_bucket,
     zero_commit_rule, zero_gather_slot, zero_last_error, zero_layout_buckets,
     zero_layout_buckets_raw, zero_layout_build, zero_layout_free, zero_layout_info,
     zero_layout_info_get, zero_layout_mem_bytes, zero_layout_mem_values, zero_layout_offsets,
     zero_layout_segments, zero_reduce_shard, zero_segment, zero_stats, zero_train_state,
     zero_version, zero_workspace_bytes, zero_device_state, zero_device_state_init,
+    zero_device_state_load,
     zero_train_args, zero_train_step, make_train_args, device_state_from_tensor)
 from .shard_step import DeviceShardStep, ShardStep  # noqa: F401

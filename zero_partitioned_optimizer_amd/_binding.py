@@ -21,7 +21,7 @@ i32, i64, u32, f64, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, c
 
 ZERO_OK, ZERO_E_INVAL, ZERO_E_ALIGN, ZERO_E_RANGE, ZERO_E_NOMEM, ZERO_E_HIP, ZERO_E_UNSUPPORTED = \
     0, -1, -2, -3, -4, -5, -6
-ZERO_F32, ZERO_BF16 = 0, 1
+ZERO_F32, ZERO_BF16, ZERO_BF16_WIRE = 0, 1, 2
 ZERO_COMMIT, ZERO_SKIP = 1, 2
 ZERO_MAX_REPLICAS = 256
 
@@ -118,6 +118,7 @@ def lib() -> ctypes.CDLL:
     L.zero_gather_slot.argtypes = [vp, i64, vp, vp]
     L.zero_commit_rule.argtypes = [P(zero_train_state), P(zero_stats)]
     L.zero_device_state_init.argtypes = [vp, vp, sz, f64, f64, f64, f64, i32, vp]
+    L.zero_device_state_load.argtypes = [vp, vp, sz, P(zero_device_state), vp]
     L.zero_train_step.argtypes = [P(zero_train_args), vp]
     L.zero_last_error.argtypes = []
     L.zero_last_error.restype = ctypes.c_char_p
@@ -127,7 +128,7 @@ def lib() -> ctypes.CDLL:
                  "zero_layout_segments", "zero_layout_buckets", "zero_layout_mem_values",
                  "zero_layout_mem_bytes", "zero_reduce_shard", "zero_adam_step",
                  "zero_gather_slot", "zero_commit_rule", "zero_device_state_init",
-                 "zero_train_step"):
+                 "zero_device_state_load", "zero_train_step"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -308,6 +309,12 @@ def zero_device_state_init(state, workspace, beta1: float, beta2: float, loss_sc
     _check(lib().zero_device_state_init(_addr(state), _addr(workspace), ws, float(beta1),
                                         float(beta2), float(loss_scale), float(min_loss_scale),
                                         int(bool(dynamic)), _stream(stream)))
+
+
+def zero_device_state_load(state, workspace, saved: zero_device_state, stream=None) -> None:
+    ws = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    _check(lib().zero_device_state_load(_addr(state), _addr(workspace), ws, ctypes.byref(saved),
+                                        _stream(stream)))
 
 
 def make_train_args(*, replicas, grad_dtype: int, p, m, v, slot=None, shard_S: int, buckets=None,

@@ -92,6 +92,8 @@ zk::Scalars adam_scalars(const zero_adam_args& a, int32_t n, double loss_scale) 
     return s;
 }
 
+int64_t elem_bytes(zero_dtype dt) { return dt == ZERO_F32 ? 4 : 2; }
+
 int check_replicas(const char* fn, const void* const* replicas, int32_t n, zero_dtype dt,
                    int64_t S) {
     if (!replicas) {
@@ -102,8 +104,8 @@ int check_replicas(const char* fn, const void* const* replicas, int32_t n, zero_
         set_error("%s: n_replicas=%d outside [1, %d]", fn, (int)n, ZERO_MAX_REPLICAS);
         return ZERO_E_RANGE;
     }
-    if (dt != ZERO_F32 && dt != ZERO_BF16) {
-        set_error("%s: grad_dtype %d is neither ZERO_F32 nor ZERO_BF16", fn, (int)dt);
+    if (dt != ZERO_F32 && dt != ZERO_BF16 && dt != ZERO_BF16_WIRE) {
+        set_error("%s: grad_dtype %d is not ZERO_F32, ZERO_BF16 or ZERO_BF16_WIRE", fn, (int)dt);
         return ZERO_E_INVAL;
     }
     for (int32_t j = 0; j < n; ++j) {
@@ -186,7 +188,7 @@ int zero_reduce_shard(const void* const* replicas, int32_t n_replicas, zero_dtyp
         set_error("%s: grad_out_dev is not 16-byte aligned", fn);
         return ZERO_E_ALIGN;
     }
-    const int64_t gb = grad_dtype == ZERO_BF16 ? 2 : 4;
+    const int64_t gb = elem_bytes(grad_dtype);
     if (grad_out_dev) {
         const Span out = span("grad_out", grad_out_dev, 4 * shard_S);
         for (int32_t j = 0; j < n_replicas; ++j)
@@ -288,7 +290,7 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
             }
         }
         if (fused) {
-            const int64_t gb = a.grad_dtype == ZERO_BF16 ? 2 : 4;
+            const int64_t gb = elem_bytes(a.grad_dtype);
             for (int32_t j = 0; j < a.n_replicas; ++j)
                 if (overlap(outs[i], span("replica", a.replicas[j], gb * S))) {
                     set_error("%s: output %s overlaps replicas[%d]", fn, outs[i].name, (int)j);
@@ -330,10 +332,8 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
     return hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
 }
 
-int zero_device_state_init(zero_device_state* state_dev, void* workspace_dev, size_t ws_bytes,
-                           double beta1, double beta2, double loss_scale, double min_loss_scale,
-                           int32_t dynamic, void* stream) {
-    static const char* fn = "zero_device_state_init";
+static int check_record_buffers(const char* fn, const zero_device_state* state_dev,
+                                const void* workspace_dev, size_t ws_bytes) {
     if (!state_dev || !workspace_dev) {
         set_error("%s: state_dev or workspace_dev is NULL", fn);
         return ZERO_E_INVAL;
@@ -347,16 +347,69 @@ int zero_device_state_init(zero_device_state* state_dev, void* workspace_dev, si
         set_error("%s: state_dev and workspace_dev overlap", fn);
         return ZERO_E_INVAL;
     }
-    if (!finite_in(beta1, 0.0, 1.0) || !finite_in(beta2, 0.0, 1.0) ||
-        !(isfinite(loss_scale) && loss_scale > 0) ||
-        !(isfinite(min_loss_scale) && min_loss_scale > 0 && min_loss_scale <= loss_scale)) {
+    return ZERO_OK;
+}
+
+static bool scales_ok(double beta1, double beta2, double loss_scale, double min_loss_scale) {
+    return finite_in(beta1, 0.0, 1.0) && finite_in(beta2, 0.0, 1.0) && isfinite(loss_scale) &&
+           loss_scale > 0 && isfinite(min_loss_scale) && min_loss_scale > 0 &&
+           min_loss_scale <= loss_scale;
+}
+
+int zero_device_state_init(zero_device_state* state_dev, void* workspace_dev, size_t ws_bytes,
+                           double beta1, double beta2, double loss_scale, double min_loss_scale,
+                           int32_t dynamic, void* stream) {
+    static const char* fn = "zero_device_state_init";
+    int rc = check_record_buffers(fn, state_dev, workspace_dev, ws_bytes);
+    if (rc) return rc;
+    if (!scales_ok(beta1, beta2, loss_scale, min_loss_scale)) {
         set_error("%s: beta1=%g beta2=%g loss_scale=%g min_loss_scale=%g out of domain", fn, beta1,
                   beta2, loss_scale, min_loss_scale);
         return ZERO_E_INVAL;
     }
-    return hip_status(zk::launch_state_init(state_dev, beta1, beta2, loss_scale, min_loss_scale,
-                                            dynamic ? 1u : 0u, workspace_dev, ws_bytes,
-                                            static_cast<hipStream_t>(stream)),
+    zero_device_state rec{};
+    rec.beta1 = beta1;
+    rec.beta2 = beta2;
+    rec.beta1_pow = 1.0;
+    rec.beta2_pow = 1.0;
+    rec.loss_scale = loss_scale;
+    rec.min_loss_scale = min_loss_scale;
+    rec.dynamic = dynamic ? 1u : 0u;
+    return hip_status(zk::launch_state_write(state_dev, rec, workspace_dev, ws_bytes,
+                                             static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+int zero_device_state_load(zero_device_state* state_dev, void* workspace_dev, size_t ws_bytes,
+                           const zero_device_state* saved, void* stream) {
+    static const char* fn = "zero_device_state_load";
+    int rc = check_record_buffers(fn, state_dev, workspace_dev, ws_bytes);
+    if (rc) return rc;
+    if (!saved) {
+        set_error("%s: saved is NULL", fn);
+        return ZERO_E_INVAL;
+    }
+    const zero_device_state& r = *saved;
+    if (!scales_ok(r.beta1, r.beta2, r.loss_scale, r.min_loss_scale)) {
+        set_error("%s: beta1=%g beta2=%g loss_scale=%g min_loss_scale=%g out of domain", fn,
+                  r.beta1, r.beta2, r.loss_scale, r.min_loss_scale);
+        return ZERO_E_INVAL;
+    }
+    const auto pow_ok = [](double x) { return x >= 0.0 && x <= 1.0; };   // false for NaN
+    if (r.t < 0 || r.n_skipped < 0 || r.cur > 1u || r.last_overflow > 1u ||
+        !pow_ok(r.beta1_pow) || !pow_ok(r.beta2_pow) ||
+        (r.t == 0 && (r.beta1_pow != 1.0 || r.beta2_pow != 1.0))) {
+        set_error("%s: inconsistent record (t=%lld n_skipped=%lld cur=%u last_overflow=%u "
+                  "beta1_pow=%g beta2_pow=%g)",
+                  fn, (long long)r.t, (long long)r.n_skipped, r.cur, r.last_overflow, r.beta1_pow,
+                  r.beta2_pow);
+        return ZERO_E_INVAL;
+    }
+    zero_device_state rec = r;
+    rec.dynamic = r.dynamic ? 1u : 0u;
+    rec.seq = 0u;                    // the cleared workspace holds no tag of an earlier step
+    return hip_status(zk::launch_state_write(state_dev, rec, workspace_dev, ws_bytes,
+                                             static_cast<hipStream_t>(stream)),
                       fn);
 }
 
@@ -421,7 +474,7 @@ int zero_train_step(const zero_train_args* args, void* stream) {
                 set_error("%s: buffers %s and %s overlap", fn, bufs[i].name, bufs[k].name);
                 return ZERO_E_INVAL;
             }
-        const int64_t gb = a.grad_dtype == ZERO_BF16 ? 2 : 4;
+        const int64_t gb = elem_bytes(a.grad_dtype);
         for (int32_t j = 0; j < a.n_replicas; ++j)
             if (overlap(bufs[i], span("replica", a.replicas[j], gb * S))) {
                 set_error("%s: %s overlaps replicas[%d]", fn, bufs[i].name, (int)j);

@@ -123,13 +123,28 @@ __device__ __forceinline__ bool nonfinite(float x) {
     return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u;
 }
 
-// A quad (4 consecutive elements) of one gradient replica, widened to fp32.
+// x as a bf16 buffer holds it: rounded to nearest even, any NaN the quiet NaN.
+__device__ __forceinline__ float hold_bf16(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return __uint_as_float(0x7fc00000u);
+    return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+}
+
+// Replica element type tags: uint16_t (bf16), float, and WireBf16 -- bf16
+// replicas whose running sum is held in bf16 after every add, as in a ring whose
+// buffers and messages are bf16.
+struct WireBf16 {};
+
+// A quad (4 consecutive elements) of one gradient replica, widened to fp32, and
+// one hop of the fold (add is fp32 except on the bf16 wire).
 template <typename RT>
 struct Quad;
 
 template <>
 struct Quad<uint16_t> {
     using V = u32x2;
+    static __device__ __forceinline__ f32x4 add(f32x4 acc, f32x4 x) { return acc + x; }
+    static __device__ __forceinline__ float add1(float acc, float x) { return acc + x; }
     static __device__ __forceinline__ V load(const void* base, int64_t q) {
         return ld(reinterpret_cast<const u32x2*>(base) + q);
     }
@@ -147,8 +162,19 @@ struct Quad<uint16_t> {
 };
 
 template <>
+struct Quad<WireBf16> : Quad<uint16_t> {
+    static __device__ __forceinline__ f32x4 add(f32x4 acc, f32x4 x) {
+        const f32x4 s = acc + x;
+        return f32x4{hold_bf16(s.x), hold_bf16(s.y), hold_bf16(s.z), hold_bf16(s.w)};
+    }
+    static __device__ __forceinline__ float add1(float acc, float x) { return hold_bf16(acc + x); }
+};
+
+template <>
 struct Quad<float> {
     using V = f32x4;
+    static __device__ __forceinline__ f32x4 add(f32x4 acc, f32x4 x) { return acc + x; }
+    static __device__ __forceinline__ float add1(float acc, float x) { return acc + x; }
     static __device__ __forceinline__ V load(const void* base, int64_t q) {
         return ld(reinterpret_cast<const f32x4*>(base) + q);
     }
@@ -195,7 +221,7 @@ __device__ __forceinline__ void fold_batch(const KParams& a, int j, int64_t q0, 
 #pragma unroll
     for (int k = 0; k < K; ++k) {
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) acc[r] = acc[r] + Quad<RT>::widen(buf[k][r]);
+        for (int r = 0; r < ROWS; ++r) acc[r] = Quad<RT>::add(acc[r], Quad<RT>::widen(buf[k][r]));
     }
 }
 
@@ -346,7 +372,7 @@ template <typename RT, bool ADAM, bool WRITE_G>
 __device__ __forceinline__ void one_elem(const KParams& a, const Res& rs, int64_t e, double& sq,
                                          uint32_t& bad) {
     float acc = Quad<RT>::one(a.rep[0], e);
-    for (int j = 1; j < a.n_rep; ++j) acc = acc + Quad<RT>::one(a.rep[j], e);
+    for (int j = 1; j < a.n_rep; ++j) acc = Quad<RT>::add1(acc, Quad<RT>::one(a.rep[j], e));
     const float g = acc * rs.sc.inv;
     bad |= nonfinite(g) ? 1u : 0u;
     const double gd = (double)g;
@@ -616,28 +642,14 @@ __global__ void __launch_bounds__(kBlock) k_restore(const zero_device_state* ctr
     cast_range((ctrl->cur & 1u) ? set_p1 : set_p0, S, slot);
 }
 
-// Record initialisation, and the clearing of the workspace its steps will use
-// (no partial may carry a tag before the record's first step).
-__global__ void k_state_init(zero_device_state* s, double beta1, double beta2, double loss_scale,
-                             double min_loss_scale, uint32_t dynamic, uint64_t* ws, int64_t ws_words) {
+// Writing a whole record (initial or restored), and clearing the workspace its
+// steps will use (no partial may carry a tag before the record's next step).
+__global__ void k_state_write(zero_device_state* s, zero_device_state rec, uint64_t* ws,
+                              int64_t ws_words) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ws_words; i += stride)
         ws[i] = 0ull;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        s->beta1 = beta1;
-        s->beta2 = beta2;
-        s->beta1_pow = 1.0;
-        s->beta2_pow = 1.0;
-        s->loss_scale = loss_scale;
-        s->min_loss_scale = min_loss_scale;
-        s->last_sumsq = 0.0;
-        s->t = 0;
-        s->n_skipped = 0;
-        s->cur = 0u;
-        s->dynamic = dynamic;
-        s->last_overflow = 0u;
-        s->seq = 0u;
-    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *s = rec;
 }
 
 // ---------------------------------------------------------------------------
@@ -727,6 +739,9 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     if (d.dtype == ZERO_BF16) {
         if (buckets) launch_typed<uint16_t, true>(d, k, grid, st);
         else launch_typed<uint16_t, false>(d, k, grid, st);
+    } else if (d.dtype == ZERO_BF16_WIRE) {
+        if (buckets) launch_typed<WireBf16, true>(d, k, grid, st);
+        else launch_typed<WireBf16, false>(d, k, grid, st);
     } else {
         if (buckets) launch_typed<float, true>(d, k, grid, st);
         else launch_typed<float, false>(d, k, grid, st);
@@ -754,15 +769,14 @@ hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_state_init(zero_device_state* s, double beta1, double beta2, double loss_scale,
-                             double min_loss_scale, uint32_t dynamic, void* ws, size_t ws_bytes,
-                             hipStream_t st) {
+hipError_t launch_state_write(zero_device_state* s, const zero_device_state& rec, void* ws,
+                              size_t ws_bytes, hipStream_t st) {
     const int64_t words = (int64_t)(ws_bytes / 8);
     int64_t grid = (words + kBlock - 1) / kBlock;
     if (grid < 1) grid = 1;
     if (grid > 64) grid = 64;
-    hipLaunchKernelGGL(k_state_init, dim3((unsigned)grid), dim3(kBlock), 0, st, s, beta1, beta2,
-                       loss_scale, min_loss_scale, dynamic, static_cast<uint64_t*>(ws), words);
+    hipLaunchKernelGGL(k_state_write, dim3((unsigned)grid), dim3(kBlock), 0, st, s, rec,
+                       static_cast<uint64_t*>(ws), words);
     return hipGetLastError();
 }
 

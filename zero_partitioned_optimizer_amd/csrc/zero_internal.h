@@ -72,8 +72,8 @@ int rows_for(int32_t n_rep);
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep);
 hipError_t launch_step(const StepDesc& d, hipStream_t stream);
 hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t stream);
-hipError_t launch_state_init(zero_device_state* s, double beta1, double beta2, double loss_scale,
-                             double min_loss_scale, uint32_t dynamic, void* ws, size_t ws_bytes,
-                             hipStream_t stream);
+// Write rec to *s and clear the workspace (ws_bytes / 8 words), on st.
+hipError_t launch_state_write(zero_device_state* s, const zero_device_state& rec, void* ws,
+                              size_t ws_bytes, hipStream_t st);
 
 }  // namespace zk

@@ -119,6 +119,25 @@ class ShardStep:
             B.zero_gather_slot(self.p[self.cur], self.S, self.slot, stream)
         return verdict
 
+    def state_dict(self) -> dict:
+        """The committed state on the host: master copy, moments and the commit
+        record (t, skips, loss scale). Hyperparameters are the caller's."""
+        st = self.state
+        return {"p": self.master.cpu(), "m": self.exp_avg.cpu(), "v": self.exp_avg_sq.cpu(),
+                "t": int(st.t), "n_skipped": int(st.n_skipped), "loss_scale": float(st.loss_scale),
+                "min_loss_scale": float(st.min_loss_scale), "dynamic": int(st.dynamic)}
+
+    def load_state_dict(self, sd: dict) -> None:
+        """Resume from ``state_dict()``: the next step continues the saved run."""
+        c = self.cur
+        for dst, key in ((self.p[c], "p"), (self.m[c], "m"), (self.v[c], "v")):
+            assert sd[key].numel() == self.S and sd[key].dtype == torch.float32
+            dst.copy_(sd[key])
+        self.state = B.zero_train_state(t=sd["t"], n_skipped=sd["n_skipped"],
+                                        loss_scale=sd["loss_scale"],
+                                        min_loss_scale=sd["min_loss_scale"], dynamic=sd["dynamic"])
+        B.zero_gather_slot(self.p[c], self.S, self.slot)
+
     def step(self, replicas: Sequence[torch.Tensor], stream=None, events=None):
         """One full step: fused kernel, read the 16-byte stats, apply the commit rule."""
         self.launch(replicas, stream, events)
@@ -200,6 +219,27 @@ class DeviceShardStep:
         """(master, m, v) of the committed state (synchronizes)."""
         c = self.state().cur & 1
         return self.p[c], self.m[c], self.v[c]
+
+    def state_dict(self) -> dict:
+        """The committed state on the host (synchronizes): the record's bytes and
+        the master copy and moments of its current set."""
+        rec = self.state()
+        c = rec.cur & 1
+        return {"record": bytes(rec), "p": self.p[c].cpu(), "m": self.m[c].cpu(),
+                "v": self.v[c].cpu()}
+
+    def load_state_dict(self, sd: dict) -> None:
+        """Resume from ``state_dict()``: the saved set goes back into the set the
+        record names, libzero rewrites the record (clearing the workspace) and
+        the slot is cast again from the master copy."""
+        rec = B.zero_device_state.from_buffer_copy(sd["record"])
+        c = rec.cur & 1
+        for dst, key in ((self.p[c], "p"), (self.m[c], "m"), (self.v[c], "v")):
+            assert sd[key].numel() == self.S and sd[key].dtype == torch.float32
+            dst.copy_(sd[key])
+        B.zero_device_state_load(self.record, self.ws, rec)
+        slot = self.slot_alt if (self.double_slot and c) else self.slot
+        B.zero_gather_slot(self.p[c], self.S, slot)
 
     def current_slot(self) -> torch.Tensor:
         """The slot buffer holding the committed bf16 parameters (synchronizes)."""
