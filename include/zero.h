@@ -401,6 +401,33 @@ typedef struct {
  */
 int zero_train_step(const zero_train_args* args, void* stream);
 
+/*
+ * One part of a device-committed step split into consecutive element ranges,
+ * so that each range can be stepped as soon as its gradients are ready while
+ * the rest are still being produced. The pages list overlap with computation
+ * and bucketing of small gradient groups among ZeRO's communication
+ * optimizations ("ZeRO Optimizer", "Communication Optimization" and
+ * "Communication Patterns", all-reduce for gradients) without fixing a
+ * mechanism; stepping each range once its gradients are in place is this
+ * library's reading of that overlap for the fused step.
+ * part_ends: host array of n_parts non-decreasing shard offsets; part k covers
+ * [part_ends[k-1], part_ends[k]) with part_ends[-1] = 0; inner ends are multiples
+ * of 8 elements and part_ends[n_parts - 1] == shard_S (empty parts are allowed).
+ * Call part = 0, 1, ..., n_parts - 1 in that order on ONE stream: every part reads
+ * the same committed record and leaves tagged partials, and the last part's
+ * workgroup 0 collects the partials of all parts (in part, then workgroup order)
+ * and commits, as zero_train_step does; with a single slot the restore kernel
+ * follows the last part. p, m, v and the slot come out bit-identical to
+ * zero_train_step's; the squared norm is summed in another grouping (equal
+ * within rounding). Each part takes at most kGridMax / n_parts workgroups, so the
+ * workspace of zero_workspace_bytes(shard_S) suffices. args must carry no
+ * bucket table (ZERO_E_UNSUPPORTED); parts cover padding like a whole-shard step.
+ * Errors: as zero_train_step; ZERO_E_INVAL for a NULL part_ends; ZERO_E_RANGE for
+ * n_parts outside [1, 131072], part outside [0, n_parts) or a bad boundary.
+ */
+int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, int32_t n_parts,
+                         int32_t part, void* stream);
+
 /* Thread-local text for the last non-OK return on this thread ("" if none). */
 const char* zero_last_error(void);
 

@@ -227,7 +227,7 @@ def test_train_step_validation(Z):
         d = dict(base)
         d.update(kw)
         a = Z.make_train_args(**d)
-        a.ws_bytes = Z.zero_workspace_bytes(64)
+        a.ws_bytes = 4096                   # enough for S = 64; ends below the replica
         with pytest.raises(Z.ZeroError) as e:
             Z.zero_train_step(a, stream=0)
         return e.value.status
@@ -281,3 +281,38 @@ def test_device_state_load_validation(Z):
     assert status(beta2_pow=1.5) == -1
     assert status(beta1_pow=float("nan")) == -1
     assert status(t=0) == -1                           # beta^0 must be 1
+
+
+def test_train_step_part_validation(Z):
+    """Part tables are checked on the host before anything is enqueued."""
+    FAKEREC = FAKE + 65536
+    S = 64
+    a = Z.make_train_args(replicas=[FAKE + 45056], grad_dtype=1, p=(FAKE, FAKE + 4096),
+                          m=(FAKE + 8192, FAKE + 12288), v=(FAKE + 16384, FAKE + 20480),
+                          slot=FAKE + 24576, shard_S=S, lr=1e-3, eps=1e-8, weight_decay=0.0,
+                          state=FAKEREC, stats=FAKE + 28672, workspace=FAKE + 32768)
+    a.ws_bytes = 4096
+
+    def status(ends, part=0, n=None, args=a):
+        tbl, cnt = Z.part_table(ends)
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_train_step_part(args, tbl, cnt if n is None else n, part, stream=0)
+        return e.value.status
+
+    assert status([32, 60]) == -3            # last end is not shard_S
+    assert status([12, 64]) == -3            # inner end not a multiple of 8
+    assert status([40, 32, 64]) == -3        # decreasing
+    assert status([-8, 64]) == -3
+    assert status([32, 64], part=2) == -3    # part out of range
+    assert status([32, 64], part=-1) == -3
+    assert status([32, 64], n=0) == -3
+    assert Z.lib().zero_train_step_part(ctypes.byref(a), None, 2, 0, None) == -1
+    b = Z.make_train_args(replicas=[FAKE + 45056], grad_dtype=1, p=(FAKE, FAKE + 4096),
+                          m=(FAKE + 8192, FAKE + 12288), v=(FAKE + 16384, FAKE + 20480),
+                          slot=FAKE + 24576, shard_S=S, lr=1e-3, eps=1e-8, weight_decay=0.0,
+                          state=FAKEREC, stats=FAKE + 28672, workspace=FAKE + 32768,
+                          buckets=FAKE + 50000 - 50000 % 16, n_buckets=2)
+    b.ws_bytes = 4096
+    assert status([32, 64], args=b) == -6    # bucket tables are not split into parts
+    a.lr = -1.0
+    assert status([32, 64]) == -1            # the whole-step checks apply too

@@ -120,6 +120,7 @@ def lib() -> ctypes.CDLL:
     L.zero_device_state_init.argtypes = [vp, vp, sz, f64, f64, f64, f64, i32, vp]
     L.zero_device_state_load.argtypes = [vp, vp, sz, P(zero_device_state), vp]
     L.zero_train_step.argtypes = [P(zero_train_args), vp]
+    L.zero_train_step_part.argtypes = [P(zero_train_args), vp, i32, i32, vp]
     L.zero_last_error.argtypes = []
     L.zero_last_error.restype = ctypes.c_char_p
     L.zero_version.argtypes = []
@@ -128,7 +129,7 @@ def lib() -> ctypes.CDLL:
                  "zero_layout_segments", "zero_layout_buckets", "zero_layout_mem_values",
                  "zero_layout_mem_bytes", "zero_reduce_shard", "zero_adam_step",
                  "zero_gather_slot", "zero_commit_rule", "zero_device_state_init",
-                 "zero_device_state_load", "zero_train_step"):
+                 "zero_device_state_load", "zero_train_step", "zero_train_step_part"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -347,6 +348,17 @@ def make_train_args(*, replicas, grad_dtype: int, p, m, v, slot=None, shard_S: i
 
 def zero_train_step(args: zero_train_args, stream=None) -> None:
     _check(lib().zero_train_step(ctypes.byref(args), _stream(stream)))
+
+
+def part_table(part_ends):
+    """A host int64 array of part boundaries for zero_train_step_part."""
+    ends = [int(e) for e in part_ends]
+    return (ctypes.c_int64 * len(ends))(*ends), len(ends)
+
+
+def zero_train_step_part(args: zero_train_args, table, n_parts: int, part: int, stream=None) -> None:
+    _check(lib().zero_train_step_part(ctypes.byref(args), ctypes.addressof(table), int(n_parts),
+                                      int(part), _stream(stream)))
 
 
 def device_state_from_tensor(t) -> zero_device_state:

@@ -413,8 +413,8 @@ int zero_device_state_load(zero_device_state* state_dev, void* workspace_dev, si
                       fn);
 }
 
-int zero_train_step(const zero_train_args* args, void* stream) {
-    static const char* fn = "zero_train_step";
+// Every check of zero_train_step, shared with zero_train_step_part.
+static int check_train_args(const char* fn, const zero_train_args* args) {
     if (!args) {
         set_error("%s: args is NULL", fn);
         return ZERO_E_INVAL;
@@ -485,11 +485,16 @@ int zero_train_step(const zero_train_args* args, void* stream) {
             return ZERO_E_INVAL;
         }
     }
+    return ZERO_OK;
+}
+
+// The step descriptor of a whole-shard device-commit launch.
+static zk::StepDesc train_desc(const zero_train_args& a) {
     zk::StepDesc d{};
     d.replicas = a.replicas;
     d.n_rep = a.n_replicas;
     d.dtype = a.grad_dtype;
-    d.S = S;
+    d.S = a.shard_S;
     d.buckets = a.n_buckets > 0 ? a.buckets_dev : nullptr;
     d.n_buckets = a.n_buckets;
     d.adam = true;
@@ -512,7 +517,85 @@ int zero_train_step(const zero_train_args* args, void* stream) {
     d.partials = static_cast<zk::Partial*>(a.workspace_dev);
     d.ev_begin = static_cast<hipEvent_t>(a.event_begin);
     d.ev_end = static_cast<hipEvent_t>(a.event_end);
+    return d;
+}
+
+int zero_train_step(const zero_train_args* args, void* stream) {
+    static const char* fn = "zero_train_step";
+    const int rc = check_train_args(fn, args);
+    if (rc) return rc;
+    const zk::StepDesc d = train_desc(*args);
     return hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
+}
+
+int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, int32_t n_parts,
+                         int32_t part, void* stream) {
+    static const char* fn = "zero_train_step_part";
+    int rc = check_train_args(fn, args);
+    if (rc) return rc;
+    const zero_train_args& a = *args;
+    const int64_t S = a.shard_S;
+    if (a.n_buckets > 0) {
+        set_error("%s: parts cover element ranges; a bucket table is not supported", fn);
+        return ZERO_E_UNSUPPORTED;
+    }
+    if (!part_ends) {
+        set_error("%s: part_ends is NULL", fn);
+        return ZERO_E_INVAL;
+    }
+    if (n_parts < 1 || n_parts > zk::kGridMax || part < 0 || part >= n_parts) {
+        set_error("%s: part %d of n_parts=%d out of range", fn, (int)part, (int)n_parts);
+        return ZERO_E_RANGE;
+    }
+    // boundaries: non-decreasing, multiples of 8 elements (16 bytes), the last one S;
+    // every part gets at most kGridMax / n_parts workgroups, so the partial slots
+    // of all parts fit the workspace of a whole-shard step
+    const int part_cap = zk::kGridMax / n_parts;
+    int64_t prev = 0, total = 0, base = 0;
+    for (int32_t k = 0; k < n_parts; ++k) {
+        const int64_t e = part_ends[k];
+        const bool last = k == n_parts - 1;
+        if (e < prev || e > S || (last ? e != S : (e % 8) != 0)) {
+            set_error("%s: part_ends[%d]=%lld invalid (previous %lld, shard_S %lld; inner ends "
+                      "must be multiples of 8, the last must equal shard_S)",
+                      fn, (int)k, (long long)e, (long long)prev, (long long)S);
+            return ZERO_E_RANGE;
+        }
+        const int64_t g = zk::grid_for(e - prev, 0, a.n_replicas, part_cap);
+        if (k == part) base = total;
+        total += g;
+        prev = e;
+    }
+    if (total * (int64_t)zk::kPartialBytes > (int64_t)a.ws_bytes || total > INT32_MAX) {
+        set_error("%s: the %d parts need %lld workspace bytes, ws_bytes=%zu", fn, (int)n_parts,
+                  (long long)(total * (int64_t)zk::kPartialBytes), a.ws_bytes);
+        return ZERO_E_RANGE;
+    }
+    const int64_t lo = part == 0 ? 0 : part_ends[part - 1], hi = part_ends[part];
+    const bool last = part == n_parts - 1;
+    zk::StepDesc d = train_desc(a);
+    const int64_t gb = elem_bytes(a.grad_dtype);
+    const void* shifted[ZERO_MAX_REPLICAS];
+    for (int32_t j = 0; j < a.n_replicas; ++j)
+        shifted[j] = static_cast<const char*>(a.replicas[j]) + lo * gb;
+    d.replicas = shifted;
+    d.S = hi - lo;
+    for (int i = 0; i < 2; ++i) {
+        d.set_p[i] = a.p[i] + lo;
+        d.set_m[i] = a.m[i] + lo;
+        d.set_v[i] = a.v[i] + lo;
+        if (d.set_slot[i]) d.set_slot[i] = d.set_slot[i] + lo;
+    }
+    if (d.slot) d.slot = d.slot + lo;
+    d.part_base = (int32_t)base;
+    d.max_grid = part_cap;
+    d.collect_n = last ? (int32_t)total : -1;
+    d.no_restore = true;
+    rc = hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
+    if (rc || !last || !a.slot[0] || a.slot[1]) return rc;
+    return hip_status(zk::launch_restore(a.state_dev, a.p[0], a.p[1], a.slot[0], S,
+                                         static_cast<hipStream_t>(stream)),
+                      fn);
 }
 
 int zero_gather_slot(const float* master_dev, int64_t shard_S, uint16_t* slot_bf16_dev,

@@ -2,11 +2,13 @@
 // context beside the step kernel's roofline: read-only, write-only, copy, and
 // k:1 read:write mixes (2:1 is the step's mix at N = 8 with bf16 replicas,
 // 28 B read : 14 B written per element; 5:1 is near its mix at N = 32).
-// Every kernel streams dwordx4 with nontemporal hints over 1 GiB buffers from a
+// Every kernel streams dwordx4 with nontemporal hints over 1 GiB buffers (or the
+// size in MiB given as the argument) from a
 // grid-stride loop with a bounds check on every access. Prints one JSON object.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <algorithm>
 #include <vector>
@@ -56,8 +58,12 @@ __global__ void __launch_bounds__(kB) k_write(f4* __restrict__ dst, int64_t n4) 
         }                                                                                  \
     } while (0)
 
-int main() {
-    const int64_t bytes = int64_t(1) << 30;
+int main(int argc, char** argv) {
+    // optional argument: MiB per buffer (default 1024; six buffers are allocated)
+    int64_t mib = argc > 1 ? atoll(argv[1]) : 1024;
+    if (mib < 16) mib = 16;
+    if (mib > 16384) mib = 16384;
+    const int64_t bytes = mib << 20;
     const int64_t n4 = bytes / 16;
     const int kMaxK = 5;
     f4* buf[kMaxK + 1];

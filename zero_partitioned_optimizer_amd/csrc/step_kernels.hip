@@ -52,6 +52,8 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 struct KParams {
     const void* rep[ZERO_MAX_REPLICAS];
     int32_t n_rep;
+    int32_t part_base;                      // device commit: partial slot of workgroup 0
+    int32_t collect_n;                      // device commit: slots workgroup 0 collects (0: none)
     int32_t reserved;
     int64_t S;
     const zero_bucket* buckets;
@@ -470,17 +472,17 @@ __device__ __forceinline__ void commit_record(zero_device_state* c, zero_stats* 
     }
 }
 
-// Workgroup 0 of a device-commit launch: wait for every workgroup's tagged
-// partial, fold them in workgroup order (thread t takes partials t, t + 256, ...,
+// Workgroup 0 of a device-commit launch: wait for the n tagged partials (this
+// launch's, or those of every part of a step split over several launches on one
+// stream), fold them in slot order (thread t takes partials t, t + 256, ...,
 // then the fixed tree of block_reduce) and commit. The wait is bounded by
 // kCollectTimeout ticks of the 100 MHz real-time counter; if it runs out (which a
 // correct launch never does) nothing is committed and the stats carry the marker
 // bad_buckets = 0xFFFFFFFF.
 constexpr uint64_t kCollectTimeout = 200000000ull;   // 2 s
 
-__device__ __noinline__ void collect_and_commit(const uint64_t* base, zero_stats* stats,
+__device__ __noinline__ void collect_and_commit(const uint64_t* base, int n, zero_stats* stats,
                                                zero_device_state* c, uint32_t tag) {
-    const int n = (int)gridDim.x;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     bool timed_out = false;
     double sq = 0.0;
@@ -577,16 +579,17 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
         if (threadIdx.x == 0) {
             const uint64_t tag = (uint64_t)rs.tag << 32;
             const uint64_t sqb = (uint64_t)__double_as_longlong(sq);
-            uint64_t* w = reinterpret_cast<uint64_t*>(a.partials) + 3 * (int64_t)blockIdx.x;
+            uint64_t* w = reinterpret_cast<uint64_t*>(a.partials) +
+                          3 * ((int64_t)a.part_base + blockIdx.x);
             __hip_atomic_store(w + 0, tag | (sqb >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(w + 1, tag | (sqb & 0xffffffffull), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(w + 2, tag | (uint64_t)((bad ? 1u : 0u) | (badb << 1)), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (blockIdx.x == 0)
-            collect_and_commit(reinterpret_cast<const uint64_t*>(a.partials), a.stats, a.ctrl_rw,
-                               rs.tag);
+        if (blockIdx.x == 0 && a.collect_n > 0)
+            collect_and_commit(reinterpret_cast<const uint64_t*>(a.partials), a.collect_n, a.stats,
+                               a.ctrl_rw, rs.tag);
     }
 }
 
@@ -666,12 +669,13 @@ int rows_for(int32_t n_rep) { return n_rep <= 16 ? 2 : 1; }
 // one trip each up to about 134M elements), at most kGridMax / 2 with two rows
 // per lane and kGridMax with one, and balanced so that every workgroup makes
 // the same number of full trips (no ragged last round).
-int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep) {
-    if (n_buckets > 0) return (int)(n_buckets < kGridMax ? n_buckets : kGridMax);
+int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid) {
+    if (max_grid <= 0 || max_grid > kGridMax) max_grid = kGridMax;
+    if (n_buckets > 0) return (int)(n_buckets < max_grid ? n_buckets : max_grid);
     const int64_t per_trip = (int64_t)rows_for(n_rep) * kBlock * kVec;
     const int64_t trips = S / per_trip;
     if (trips < 1) return 1;
-    const int64_t cap = rows_for(n_rep) == 2 ? kGridMax / 2 : kGridMax;
+    const int64_t cap = rows_for(n_rep) == 2 ? (max_grid > 1 ? max_grid / 2 : 1) : max_grid;
     const int64_t rounds = (trips + cap - 1) / cap;
     return (int)((trips + rounds - 1) / rounds);
 }
@@ -731,7 +735,9 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     k.partials = d.partials;
     k.sc = d.sc;
     const bool buckets = d.n_buckets > 0;
-    const int grid = grid_for(d.S, d.n_buckets, d.n_rep);
+    const int grid = grid_for(d.S, d.n_buckets, d.n_rep, d.max_grid);
+    k.part_base = d.part_base;
+    k.collect_n = d.collect_n == 0 ? grid : (d.collect_n > 0 ? d.collect_n : 0);
     if (d.ev_begin) {
         hipError_t e = hipEventRecord(d.ev_begin, st);
         if (e != hipSuccess) return e;
@@ -753,14 +759,19 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     if (d.ctrl) {
-        if (d.slot && !d.set_slot[1])
-            hipLaunchKernelGGL(k_restore, dim3(grid_stream(d.S)), dim3(kBlock), 0, st,
-                               (const zero_device_state*)d.ctrl, (const float*)d.set_p[0],
-                               (const float*)d.set_p[1], d.slot, d.S);
+        if (d.slot && !d.set_slot[1] && !d.no_restore)
+            return launch_restore(d.ctrl, d.set_p[0], d.set_p[1], d.slot, d.S, st);
     } else {
         hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kFinalizeBlock), 0, st,
                            (const Partial*)d.partials, grid, d.stats);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_restore(const zero_device_state* ctrl, const float* set_p0, const float* set_p1,
+                          uint16_t* slot, int64_t S, hipStream_t st) {
+    hipLaunchKernelGGL(k_restore, dim3(grid_stream(S)), dim3(kBlock), 0, st, ctrl, set_p0, set_p1,
+                       slot, S);
     return hipGetLastError();
 }
 

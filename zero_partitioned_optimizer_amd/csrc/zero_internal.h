@@ -66,12 +66,23 @@ struct StepDesc {
     Partial* partials;              // workspace, >= grid_for() entries
     hipEvent_t ev_begin;            // optional, around the main kernel only
     hipEvent_t ev_end;
+    // device commit split over several launches (parts of one step):
+    int32_t part_base;              // partial slot of this launch's workgroup 0
+    int32_t collect_n;              // 0: collect this launch's own partials and commit (a
+                                    // whole step); > 0: collect slots [0, n) and commit;
+                                    // < 0: publish only (a part before the last)
+    bool no_restore;                // single slot: leave the restore kernel to the caller
+    int max_grid;                   // cap on the workgroups (0: kGridMax)
 };
 
 int rows_for(int32_t n_rep);
-int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep);
+int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid = 0);
 hipError_t launch_step(const StepDesc& d, hipStream_t stream);
 hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t stream);
+// After a device-committed step with a single slot: recast the slot from the
+// current master if the step was skipped (no-op kernel otherwise).
+hipError_t launch_restore(const zero_device_state* ctrl, const float* set_p0, const float* set_p1,
+                          uint16_t* slot, int64_t S, hipStream_t stream);
 // Write rec to *s and clear the workspace (ws_bytes / 8 words), on st.
 hipError_t launch_state_write(zero_device_state* s, const zero_device_state& rec, void* ws,
                               size_t ws_bytes, hipStream_t st);

@@ -208,6 +208,27 @@ class DeviceShardStep:
             a.event_begin = a.event_end = None
         B.zero_train_step(a, stream)
 
+    def step_parts(self, replicas: Sequence[torch.Tensor], part_ends: Sequence[int],
+                   ready=None, stream=None, events=None) -> None:
+        """Enqueue one step as consecutive element ranges (``zero_train_step_part``),
+        all on one stream; ``ready[k]`` (a torch.cuda.Event, optional) is waited on
+        before part k, so each range is stepped as soon as its gradients are
+        written. ``events[k]`` (optional pair) times part k's kernel."""
+        a = self._args_for(replicas)
+        key = tuple(int(e) for e in part_ends)
+        if getattr(self, "_parts_key", None) != key:
+            self._parts, self._parts_n = B.part_table(key)
+            self._parts_key = key
+        st = stream if stream is not None else torch.cuda.current_stream()
+        for k in range(self._parts_n):
+            if ready is not None and ready[k] is not None:
+                st.wait_event(ready[k])
+            ev = events[k] if events is not None else None
+            a.event_begin = B._event(ev[0]) if ev is not None else None
+            a.event_end = B._event(ev[1]) if ev is not None else None
+            B.zero_train_step_part(a, self._parts, self._parts_n, k, st)
+        a.event_begin = a.event_end = None
+
     def state(self) -> B.zero_device_state:
         """Copy the committed-state record back (synchronizes)."""
         return B.device_state_from_tensor(self.record)
