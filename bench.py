@@ -156,6 +156,70 @@ def overlap_bench(args, Z, w, S, pool, p0, kw, gdt) -> int:
     return 0
 
 
+def offload_bench(args, Z, w, S, reps, p0, gdt) -> int:
+    """The offloaded step: GPU fold and check, the fp32 gradient to the host in
+    chunks, host Adam on each chunk as it lands, bf16 back into the slot. Beside
+    it, the parts on their own: the gradient's device-to-host copy, the slot's
+    host-to-device copy (both pinned, one transfer each) and the host Adam over
+    the whole shard with the same threads."""
+    import numpy as np
+    import torch
+    nthreads = len(os.sched_getaffinity(0))
+    step = Z.OffloadShardStep(S, w.N, gdt, p0.cpu(), lr=w.lr, beta1=w.beta1, beta2=w.beta2,
+                              eps=w.eps, weight_decay=w.wd, loss_scale=w.loss_scale,
+                              dynamic=w.dynamic_loss_scale, chunk_elems=args.chunk_elems,
+                              nthreads=nthreads)
+    for _ in range(args.warmup):
+        step.step(reps)
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    skipped = 0
+    for _ in range(K):
+        st, verdict = step.step(reps)
+        skipped += verdict == Z.ZERO_SKIP
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    def best_of(fn, n=5):
+        ts = []
+        for _ in range(n):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - a)
+        return min(ts)
+    t_d2h = best_of(lambda: step.g_host.copy_(step.g_dev, non_blocking=True))
+    t_h2d = best_of(lambda: step.slot.copy_(step.slot_host, non_blocking=True))
+    g = np.ones(S, np.float32) * 1e-3
+    pp, mm, vv = (np.zeros(S, np.float32) for _ in range(3))
+    sl = np.zeros(S, np.uint16)
+    t_adam = best_of(lambda: Z.zero_host_adam(g, pp, mm, vv, S, lr=w.lr, beta1=w.beta1,
+                                              beta2=w.beta2, eps=w.eps, weight_decay=w.wd,
+                                              step_t=1, slot=sl, nthreads=nthreads), 3)
+    ms = elapsed / K * 1e3
+    log(f"offload: {ms:.3f} ms/step; D2H {S * 4 / t_d2h / 1e9:.1f} GB/s, H2D "
+        f"{S * 2 / t_h2d / 1e9:.1f} GB/s, host Adam {S / t_adam / 1e9:.2f} G elem/s "
+        f"({nthreads} threads)")
+    out = {
+        "metric": "offloaded shard step: elements/s (state in host memory)",
+        "value": S * K / elapsed, "unit": "elements/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name} shard, rank {args.rank} of N={w.N}", "shard_elems": S,
+                   "n_replicas": w.N, "grad_dtype": w.grad_dtype, "state": "host",
+                   "chunk_elems": args.chunk_elems or 1 << 18, "host_threads": nthreads},
+        "parts_alone_ms": {"d2h_gradient": t_d2h * 1e3, "h2d_slot": t_h2d * 1e3,
+                           "host_adam": t_adam * 1e3},
+        "pcie_gbs": {"d2h": S * 4 / t_d2h / 1e9, "h2d": S * 2 / t_h2d / 1e9},
+        "host_adam_elems_per_s": S / t_adam,
+        "skipped_steps": skipped, "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +255,11 @@ def main() -> int:
                          "their gradients land (device commit)")
     ap.add_argument("--gemm", type=int, default=4096,
                     help="--overlap: the stand-in backward's GEMM is (M x M) @ (M x M) per part")
+    ap.add_argument("--offload", action="store_true",
+                    help="instead of the default line: time the offloaded step (fp32 master, m, "
+                         "v in host memory; host Adam on chunks as they cross)")
+    ap.add_argument("--chunk-elems", type=int, default=0,
+                    help="--offload: elements per host chunk (0: the library's default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -251,6 +320,8 @@ def main() -> int:
     torch.cuda.synchronize()
     if args.overlap:
         return overlap_bench(args, Z, w, S, reps, p0, kw, gdt)
+    if args.offload:
+        return offload_bench(args, Z, w, S, reps, p0, gdt)
     log("inputs resident; warmup", args.warmup)
 
     for _ in range(args.warmup):

@@ -428,6 +428,91 @@ int zero_train_step(const zero_train_args* args, void* stream);
 int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, int32_t n_parts,
                          int32_t part, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Optimizer state offloaded to host memory                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The "ZeRO Optimizer" page ("Advanced Optimizations", ZeRO-Offload) moves the
+ * optimizer states to CPU memory and balances the GPU-CPU transfers against the
+ * work; it gives no algorithm. Read plainly: the shard's fp32 master, m and v
+ * live in host memory, the GPU folds and checks the gradients as in
+ * zero_reduce_shard, the averaged fp32 gradient crosses to the host, the host
+ * runs the same Adam/AdamW (one fp32 operation per source operation, correctly
+ * rounded division and square root, no contraction, so the result is bit for
+ * bit that of zero_adam_step), and the bf16 result crosses back into the
+ * rank's slot.
+ */
+
+/*
+ * Adam/AdamW on the host, in place on p, m, v over n elements, optionally
+ * writing bf16 (nearest even) into slot_bf16. Same operation sequence and fp32
+ * scalars as zero_adam_step (step_t >= 1; beta^t as a t-fold product in double).
+ * All pointers are host memory, non-overlapping except that nothing aliases.
+ * nthreads: worker threads (0: one per CPU in the calling process's affinity mask,
+ * at most 256). Synchronous.
+ * Errors: ZERO_E_INVAL (NULL pointer with n > 0, a parameter out of domain),
+ * ZERO_E_RANGE (n < 0).
+ */
+typedef struct {
+    const float* g;
+    float* p;
+    float* m;
+    float* v;
+    uint16_t* slot_bf16;           /* may be NULL */
+    int64_t n;
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t step_t;
+    int32_t nthreads;
+    int32_t reserved;
+} zero_host_adam_args;
+
+int zero_host_adam(const zero_host_adam_args* args);
+
+/*
+ * One offloaded step of this rank's shard, synchronous on the host:
+ *  1. on `stream`: fold the replicas into g_dev (fp32 [shard_S], device),
+ *     ×1/(N·loss_scale), overflow flag and squared norm into stats_dev
+ *     (zero_reduce_shard); copy the 16-byte stats back and wait for them;
+ *  2. overflow: nothing is touched, the commit rule skips (state->n_skipped += 1,
+ *     dynamic loss scale halved), return ZERO_SKIP;
+ *  3. clean: g_dev is copied to g_host in chunks of chunk_elems elements, one
+ *     event per chunk; host threads take the chunks in order, run zero_host_adam
+ *     on each as soon as it has landed (update number state->t + 1), and upload
+ *     each chunk's bf16 values from slot_host to slot_dev on stream_h2d (or on
+ *     `stream` if NULL) while later chunks are still crossing; after both
+ *     streams are synchronized, state->t += 1 and ZERO_COMMIT is returned.
+ * *stats_out (may be NULL) gets the step's stats. Host buffers: p_host, m_host,
+ * v_host any host memory; g_host and slot_host pinned (hipHostMalloc) for
+ * asynchronous copies, and not reused by the caller until the call returns.
+ * The library creates its chunk events per call and frees them. Errors: as
+ * zero_reduce_shard and zero_host_adam; ZERO_E_RANGE for chunk_elems < 0.
+ */
+typedef struct {
+    const void* const* replicas;   /* host array of n_replicas device pointers, slot order */
+    int32_t n_replicas;
+    zero_dtype grad_dtype;
+    int64_t shard_S;
+    float* g_dev;                  /* device [shard_S] */
+    float* g_host;                 /* pinned host [shard_S] */
+    float* p_host;                 /* host [shard_S], the committed state, updated in place */
+    float* m_host;
+    float* v_host;
+    uint16_t* slot_host;           /* pinned host [shard_S] staging */
+    uint16_t* slot_dev;            /* device [shard_S], this rank's slot */
+    double lr, beta1, beta2, eps, weight_decay;
+    zero_train_state* state;       /* host: t, skips, loss scale; the commit rule updates it */
+    zero_stats* stats_dev;
+    void* workspace_dev;
+    size_t ws_bytes;
+    int64_t chunk_elems;           /* 0: 262,144 */
+    int32_t nthreads;              /* host worker threads, 0: one per CPU of the affinity mask */
+    int32_t reserved;
+    void* stream_h2d;              /* optional second stream for the slot uploads */
+} zero_offload_args;
+
+int zero_offload_step(const zero_offload_args* args, void* stream, zero_stats* stats_out);
+
 /* Thread-local text for the last non-OK return on this thread ("" if none). */
 const char* zero_last_error(void);
 

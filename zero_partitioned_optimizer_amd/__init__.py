@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     zero_layout_info_get, zero_layout_mem_bytes, zero_layout_mem_values, zero_layout_offsets,
     zero_layout_segments, zero_reduce_shard, zero_segment, zero_stats, zero_train_state,
     zero_version, zero_workspace_bytes, zero_device_state, zero_device_state_init,
-    zero_device_state_load, zero_train_step_part, part_table,
+    zero_device_state_load, zero_train_step_part, part_table, zero_host_adam,
+    zero_offload_step, zero_offload_args, zero_host_adam_args,
     zero_train_args, zero_train_step, make_train_args, device_state_from_tensor)
-from .shard_step import DeviceShardStep, ShardStep  # noqa: F401
+from .shard_step import DeviceShardStep, OffloadShardStep, ShardStep  # noqa: F401

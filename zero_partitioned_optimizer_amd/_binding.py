@@ -85,6 +85,22 @@ class zero_train_args(ctypes.Structure):
                 ("workspace_dev", vp), ("ws_bytes", sz), ("event_begin", vp), ("event_end", vp)]
 
 
+class zero_host_adam_args(ctypes.Structure):
+    _fields_ = [("g", vp), ("p", vp), ("m", vp), ("v", vp), ("slot_bf16", vp), ("n", i64),
+                ("lr", f64), ("beta1", f64), ("beta2", f64), ("eps", f64), ("weight_decay", f64),
+                ("step_t", i64), ("nthreads", i32), ("reserved", i32)]
+
+
+class zero_offload_args(ctypes.Structure):
+    _fields_ = [("replicas", ctypes.POINTER(vp)), ("n_replicas", i32), ("grad_dtype", i32),
+                ("shard_S", i64), ("g_dev", vp), ("g_host", vp), ("p_host", vp), ("m_host", vp),
+                ("v_host", vp), ("slot_host", vp), ("slot_dev", vp), ("lr", f64), ("beta1", f64),
+                ("beta2", f64), ("eps", f64), ("weight_decay", f64),
+                ("state", ctypes.POINTER(zero_train_state)), ("stats_dev", vp),
+                ("workspace_dev", vp), ("ws_bytes", sz), ("chunk_elems", i64), ("nthreads", i32),
+                ("reserved", i32), ("stream_h2d", vp)]
+
+
 assert ctypes.sizeof(zero_device_state) == 88
 assert ctypes.sizeof(zero_bucket) == 16 and ctypes.sizeof(zero_stats) == 16
 assert ctypes.sizeof(zero_segment) == 32
@@ -121,6 +137,8 @@ def lib() -> ctypes.CDLL:
     L.zero_device_state_load.argtypes = [vp, vp, sz, P(zero_device_state), vp]
     L.zero_train_step.argtypes = [P(zero_train_args), vp]
     L.zero_train_step_part.argtypes = [P(zero_train_args), vp, i32, i32, vp]
+    L.zero_host_adam.argtypes = [P(zero_host_adam_args)]
+    L.zero_offload_step.argtypes = [P(zero_offload_args), vp, P(zero_stats)]
     L.zero_last_error.argtypes = []
     L.zero_last_error.restype = ctypes.c_char_p
     L.zero_version.argtypes = []
@@ -129,7 +147,8 @@ def lib() -> ctypes.CDLL:
                  "zero_layout_segments", "zero_layout_buckets", "zero_layout_mem_values",
                  "zero_layout_mem_bytes", "zero_reduce_shard", "zero_adam_step",
                  "zero_gather_slot", "zero_commit_rule", "zero_device_state_init",
-                 "zero_device_state_load", "zero_train_step", "zero_train_step_part"):
+                 "zero_device_state_load", "zero_train_step", "zero_train_step_part",
+                 "zero_host_adam", "zero_offload_step"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -348,6 +367,36 @@ def make_train_args(*, replicas, grad_dtype: int, p, m, v, slot=None, shard_S: i
 
 def zero_train_step(args: zero_train_args, stream=None) -> None:
     _check(lib().zero_train_step(ctypes.byref(args), _stream(stream)))
+
+
+def _host_addr(x) -> int:
+    """Address of a host buffer: a CPU torch tensor, a numpy array, an int or None."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        assert not x.is_cuda, "host buffer expected"
+        return x.data_ptr()
+    return x.ctypes.data
+
+
+def zero_host_adam(g, p, m, v, n: int, *, lr: float, beta1: float, beta2: float, eps: float,
+                   weight_decay: float, step_t: int, slot=None, nthreads: int = 0) -> None:
+    """Adam/AdamW on host buffers (in place on p, m, v)."""
+    a = zero_host_adam_args(g=_host_addr(g), p=_host_addr(p), m=_host_addr(m), v=_host_addr(v),
+                            slot_bf16=_host_addr(slot) or None, n=int(n), lr=float(lr),
+                            beta1=float(beta1), beta2=float(beta2), eps=float(eps),
+                            weight_decay=float(weight_decay), step_t=int(step_t),
+                            nthreads=int(nthreads))
+    _check(lib().zero_host_adam(ctypes.byref(a)))
+
+
+def zero_offload_step(args: zero_offload_args, stream=None) -> tuple:
+    """Returns (ZERO_COMMIT or ZERO_SKIP, zero_stats)."""
+    st = zero_stats()
+    rc = _check(lib().zero_offload_step(ctypes.byref(args), _stream(stream), ctypes.byref(st)))
+    return rc, st
 
 
 def part_table(part_ends):

@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -9,6 +10,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libzero.so")
 SOURCES = ["abi.cpp", "layout.cpp", "step_kernels.hip"]
+# host-only C++ (no device pass), compiled to an object and linked in
+HOST_SOURCES = ["offload.cpp"]
+HOST_FLAGS = ["-x", "c++", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-c"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -37,8 +41,17 @@ def _run(cmd):
 def build(out: str = LIB, extra=(), probe: bool = True) -> str:
     """Compile every source into ``out`` (always recompiles), and the HBM probe."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    _run([hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs,
-          "-o", out + ".tmp"])
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs = []
+    for h in HOST_SOURCES:
+        obj = out + "." + os.path.splitext(h)[0] + ".o"
+        rocm = os.path.dirname(os.path.dirname(os.path.realpath(shutil.which(hipcc()) or hipcc())))
+        _run([hipcc(), *HOST_FLAGS, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+              *inc, os.path.join(CSRC, h), "-o", obj])
+        objs.append(obj)
+    _run([hipcc(), *HIPCC_FLAGS, *extra, *inc, *srcs, "-x", "none", *objs, "-o", out + ".tmp"])
+    for obj in objs:
+        os.remove(obj)
     os.replace(out + ".tmp", out)
     if probe:
         flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]

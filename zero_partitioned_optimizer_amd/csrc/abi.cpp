@@ -159,6 +159,24 @@ bool finite_in(double x, double lo, double hi) { return isfinite(x) && x >= lo &
 
 }  // namespace
 
+namespace zl {
+
+int hip_error(hipError_t e, const char* where) { return hip_status(e, where); }
+
+zk::Scalars update_scalars(double lr, double beta1, double beta2, double eps, double wd,
+                           int64_t t) {
+    zero_adam_args a{};
+    a.lr = lr;
+    a.beta1 = beta1;
+    a.beta2 = beta2;
+    a.eps = eps;
+    a.weight_decay = wd;
+    a.step_t = t;
+    return adam_scalars(a, 1, 1.0);
+}
+
+}  // namespace zl
+
 extern "C" {
 
 const char* zero_last_error(void) { return zl::g_err.c_str(); }

@@ -88,3 +88,12 @@ hipError_t launch_state_write(zero_device_state* s, const zero_device_state& rec
                               size_t ws_bytes, hipStream_t st);
 
 }  // namespace zk
+
+namespace zl {
+// Thread-local error text of the last failing call (zero_last_error).
+void set_error(const char* fmt, ...);
+// ZERO_OK, or ZERO_E_HIP with the error text set.
+int hip_error(hipError_t e, const char* where);
+// The fp32 scalars of update number t (inv = 1), as the device steps use them.
+zk::Scalars update_scalars(double lr, double beta1, double beta2, double eps, double wd, int64_t t);
+}  // namespace zl

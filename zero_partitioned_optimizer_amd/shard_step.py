@@ -267,3 +267,99 @@ class DeviceShardStep:
         if not self.double_slot:
             return self.slot
         return self.slot_alt if self.state().cur & 1 else self.slot
+
+
+class OffloadShardStep:
+    """The step with the shard's fp32 master, m and v in host memory
+    (``zero_offload_step``): the GPU folds and checks the replicas, the averaged
+    gradient crosses to the host in chunks, host threads run Adam on each chunk
+    as it lands, and the bf16 values go back into the slot on the GPU. The
+    commit rule runs on the host, as in ``ShardStep``; a skipped step touches
+    nothing. Only the replicas, one fp32 gradient buffer and the slot stay in
+    device memory."""
+
+    def __init__(self, shard_S: int, n_replicas: int, grad_dtype: int, p0: torch.Tensor, *,
+                 lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+                 loss_scale: float = 1.0, dynamic: bool = False, min_loss_scale: float = 1.0,
+                 slot: Optional[torch.Tensor] = None, chunk_elems: int = 0, nthreads: int = 0,
+                 upload_stream: bool = True, device=None):
+        S = int(shard_S)
+        assert p0.dtype == torch.float32 and p0.numel() == S
+        dev = torch.device(device) if device is not None else torch.device(
+            "cuda", torch.cuda.current_device())
+        self.S, self.N, self.grad_dtype = S, int(n_replicas), int(grad_dtype)
+        self.hyper = dict(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay)
+        self.p = p0.detach().to("cpu", copy=True).contiguous()
+        self.m = torch.zeros(S, dtype=torch.float32)
+        self.v = torch.zeros(S, dtype=torch.float32)
+        self.g_dev = torch.empty(S, dtype=torch.float32, device=dev)
+        self.g_host = torch.empty(S, dtype=torch.float32, pin_memory=True)
+        self.slot_host = torch.empty(S, dtype=torch.int16, pin_memory=True)
+        self.slot = slot if slot is not None else torch.empty(S, dtype=torch.int16, device=dev)
+        assert self.slot.numel() == S and self.slot.element_size() == 2 and self.slot.is_cuda
+        self.stats = torch.zeros(16, dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(B.zero_workspace_bytes(S), dtype=torch.uint8, device=dev)
+        self.state = B.zero_train_state(t=0, n_skipped=0, loss_scale=float(loss_scale),
+                                        min_loss_scale=float(min_loss_scale), dynamic=int(dynamic))
+        self.chunk_elems, self.nthreads = int(chunk_elems), int(nthreads)
+        self.upload = torch.cuda.Stream(device=dev) if upload_stream else None
+        self._args = None
+        self._args_key = None
+        self._recast_slot()
+
+    def _recast_slot(self):
+        master = self.p.to(self.g_dev.device)
+        B.zero_gather_slot(master, self.S, self.slot)
+        torch.cuda.current_stream().synchronize()
+
+    @property
+    def t(self) -> int:
+        return int(self.state.t)
+
+    @property
+    def loss_scale(self) -> float:
+        return float(self.state.loss_scale)
+
+    def _args_for(self, replicas: Sequence[torch.Tensor]) -> B.zero_offload_args:
+        key = tuple(r.data_ptr() for r in replicas)
+        if self._args_key != key:
+            table = B._replica_table(list(replicas))
+            a = B.zero_offload_args()
+            a.replicas = ctypes.cast(table, ctypes.POINTER(ctypes.c_void_p))
+            a.n_replicas = len(replicas)
+            a.grad_dtype = self.grad_dtype
+            a.shard_S = self.S
+            a.g_dev, a.g_host = self.g_dev.data_ptr(), self.g_host.data_ptr()
+            a.p_host, a.m_host, a.v_host = self.p.data_ptr(), self.m.data_ptr(), self.v.data_ptr()
+            a.slot_host, a.slot_dev = self.slot_host.data_ptr(), self.slot.data_ptr()
+            a.state = ctypes.pointer(self.state)
+            a.stats_dev = self.stats.data_ptr()
+            a.workspace_dev = self.ws.data_ptr()
+            a.ws_bytes = self.ws.numel()
+            a.chunk_elems, a.nthreads = self.chunk_elems, self.nthreads
+            a.stream_h2d = self.upload.cuda_stream if self.upload is not None else None
+            self._args, self._table, self._args_key = a, table, key
+        a = self._args
+        a.lr, a.beta1, a.beta2 = self.hyper["lr"], self.hyper["beta1"], self.hyper["beta2"]
+        a.eps, a.weight_decay = self.hyper["eps"], self.hyper["weight_decay"]
+        return a
+
+    def step(self, replicas: Sequence[torch.Tensor], stream=None):
+        """One offloaded step (synchronous). Returns (stats, ZERO_COMMIT or ZERO_SKIP)."""
+        verdict, st = B.zero_offload_step(self._args_for(replicas), stream)
+        return st, verdict
+
+    def state_dict(self) -> dict:
+        st = self.state
+        return {"p": self.p.clone(), "m": self.m.clone(), "v": self.v.clone(), "t": int(st.t),
+                "n_skipped": int(st.n_skipped), "loss_scale": float(st.loss_scale),
+                "min_loss_scale": float(st.min_loss_scale), "dynamic": int(st.dynamic)}
+
+    def load_state_dict(self, sd: dict) -> None:
+        for dst, key in ((self.p, "p"), (self.m, "m"), (self.v, "v")):
+            assert sd[key].numel() == self.S and sd[key].dtype == torch.float32
+            dst.copy_(sd[key])
+        self.state.t, self.state.n_skipped = sd["t"], sd["n_skipped"]
+        self.state.loss_scale, self.state.min_loss_scale = sd["loss_scale"], sd["min_loss_scale"]
+        self.state.dynamic = sd["dynamic"]
+        self._recast_slot()
