@@ -209,7 +209,7 @@ def offload_bench(args, Z, w, S, reps, p0, gdt) -> int:
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{w.name} shard, rank {args.rank} of N={w.N}", "shard_elems": S,
                    "n_replicas": w.N, "grad_dtype": w.grad_dtype, "state": "host",
-                   "chunk_elems": args.chunk_elems or 1 << 18, "host_threads": nthreads},
+                   "chunk_elems": args.chunk_elems or 1 << 20, "host_threads": nthreads},
         "parts_alone_ms": {"d2h_gradient": t_d2h * 1e3, "h2d_slot": t_h2d * 1e3,
                            "host_adam": t_adam * 1e3},
         "pcie_gbs": {"d2h": S * 4 / t_d2h / 1e9, "h2d": S * 2 / t_h2d / 1e9},

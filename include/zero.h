@@ -477,11 +477,12 @@ int zero_host_adam(const zero_host_adam_args* args);
  *  2. overflow: nothing is touched, the commit rule skips (state->n_skipped += 1,
  *     dynamic loss scale halved), return ZERO_SKIP;
  *  3. clean: g_dev is copied to g_host in chunks of chunk_elems elements, one
- *     event per chunk; host threads take the chunks in order, run zero_host_adam
- *     on each as soon as it has landed (update number state->t + 1), and upload
- *     each chunk's bf16 values from slot_host to slot_dev on stream_h2d (or on
- *     `stream` if NULL) while later chunks are still crossing; after both
- *     streams are synchronized, state->t += 1 and ZERO_COMMIT is returned.
+ *     event per chunk; as soon as a chunk has landed every host thread updates
+ *     its stripe of it (the zero_host_adam arithmetic, update number
+ *     state->t + 1), and the thread that finishes the chunk uploads its bf16
+ *     values from slot_host to slot_dev on stream_h2d (or on `stream` if NULL)
+ *     while later chunks are still crossing; after both streams are
+ *     synchronized, state->t += 1 and ZERO_COMMIT is returned.
  * *stats_out (may be NULL) gets the step's stats. Host buffers: p_host, m_host,
  * v_host any host memory; g_host and slot_host pinned (hipHostMalloc) for
  * asynchronous copies, and not reused by the caller until the call returns.
@@ -505,7 +506,7 @@ typedef struct {
     zero_stats* stats_dev;
     void* workspace_dev;
     size_t ws_bytes;
-    int64_t chunk_elems;           /* 0: 262,144 */
+    int64_t chunk_elems;           /* 0: 1,048,576 */
     int32_t nthreads;              /* host worker threads, 0: one per CPU of the affinity mask */
     int32_t reserved;
     void* stream_h2d;              /* optional second stream for the slot uploads */

@@ -28,7 +28,7 @@ namespace {
 using zl::set_error;
 
 constexpr int kMaxThreads = 256;
-constexpr int64_t kDefaultChunk = int64_t(1) << 18;
+constexpr int64_t kDefaultChunk = int64_t(1) << 20;
 
 // Adam / AdamW over n elements, in place, optionally with the bf16 slot.
 __attribute__((target_clones("avx512f", "avx2", "default"))) void adam_span(
@@ -184,9 +184,7 @@ int zero_offload_step(const zero_offload_args* args, void* stream, zero_stats* s
     int err = ZERO_OK;
     for (int64_t c = 0; c < n_chunks && !err; ++c) {
         const int64_t lo = c * C, len = (S - lo) < C ? (S - lo) : C;
-        err = zl::hip_error(hipEventCreateWithFlags(&ev[c], hipEventDisableTiming |
-                                                                hipEventBlockingSync),
-                            fn);
+        err = zl::hip_error(hipEventCreateWithFlags(&ev[c], hipEventDisableTiming), fn);
         if (!err)
             err = zl::hip_error(hipMemcpyAsync(a.g_host + lo, a.g_dev + lo, (size_t)len * 4,
                                                hipMemcpyDeviceToHost, st),
@@ -196,21 +194,29 @@ int zero_offload_step(const zero_offload_args* args, void* stream, zero_stats* s
     if (!err) {
         const zk::Scalars s = zl::update_scalars(a.lr, a.beta1, a.beta2, a.eps, a.weight_decay,
                                                  a.state->t + 1);
-        const int T = thread_count(a.nthreads, n_chunks);
-        std::atomic<int64_t> next{0};
+        // Every thread takes its stripe of every chunk, chunk after chunk; the
+        // thread that finishes a chunk's last stripe sends that chunk's bf16 values
+        // up. A chunk is thus updated by all threads as soon as it lands, and its
+        // upload overlaps the next chunks' copies and updates.
+        const int T = thread_count(a.nthreads, (C + 16383) / 16384);
+        std::vector<std::atomic<int>> left((size_t)n_chunks);
+        for (auto& x : left) x.store(T);
         std::atomic<int> first_err{(int)hipSuccess};   // a hipError_t; the text is set below
-        auto worker = [&] {
-            for (;;) {
-                const int64_t c = next.fetch_add(1);
-                if (c >= n_chunks || first_err.load() != (int)hipSuccess) return;
+        auto worker = [&](int k) {
+            for (int64_t c = 0; c < n_chunks; ++c) {
+                if (first_err.load() != (int)hipSuccess) return;
                 const int64_t lo = c * C, len = (S - lo) < C ? (S - lo) : C;
+                // stripes of whole 16-element groups, so stripes never split a cache line
+                const int64_t groups = (len + 15) / 16;
+                const int64_t a0 = lo + 16 * (groups * k / T);
+                const int64_t a1 = k == T - 1 ? lo + len : lo + 16 * (groups * (k + 1) / T);
                 hipError_t e = hipEventSynchronize(ev[c]);
-                if (e == hipSuccess) {
-                    adam_span(a.g_host + lo, a.p_host + lo, a.m_host + lo, a.v_host + lo,
-                              a.slot_host + lo, len, s);
+                if (e == hipSuccess && a1 > a0)
+                    adam_span(a.g_host + a0, a.p_host + a0, a.m_host + a0, a.v_host + a0,
+                              a.slot_host + a0, a1 - a0, s);
+                if (e == hipSuccess && left[c].fetch_sub(1) == 1)
                     e = hipMemcpyAsync(a.slot_dev + lo, a.slot_host + lo, (size_t)len * 2,
                                        hipMemcpyHostToDevice, up);
-                }
                 if (e != hipSuccess) {
                     int expected = (int)hipSuccess;
                     first_err.compare_exchange_strong(expected, (int)e);
@@ -219,8 +225,8 @@ int zero_offload_step(const zero_offload_args* args, void* stream, zero_stats* s
             }
         };
         std::vector<std::thread> pool;
-        for (int k = 0; k + 1 < T; ++k) pool.emplace_back(worker);
-        worker();
+        for (int k = 0; k + 1 < T; ++k) pool.emplace_back(worker, k);
+        worker(T - 1);
         for (auto& th : pool) th.join();
         err = zl::hip_error((hipError_t)first_err.load(), fn);
     }
