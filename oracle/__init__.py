@@ -78,6 +78,8 @@ def load(path: str) -> ctypes.CDLL:
         getattr(L, name).restype = ctypes.c_int
     L.or_ring_rs_wire.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
     L.or_ring_rs_wire.restype = ctypes.c_int
+    L.or_gather_tensor.argtypes = [vp, i64, i64, i32, i64, i64, vp]
+    L.or_gather_tensor.restype = ctypes.c_int
     L.or_ring_ag.argtypes = [vp, i64, i64, vp, vp, vp]
     L.or_ring_ag.restype = ctypes.c_int
     L.or_bf16_to_f32.argtypes = [ctypes.c_uint16]
@@ -203,6 +205,20 @@ def ring_all_gather(chunks: np.ndarray):
     if lib().or_ring_ag(_ptr(chunks), N, S, _ptr(gathered), _ptr(sent), _ptr(recv)) != 0:
         raise RuntimeError("ring all-gather simulation failed")
     return gathered, sent, recv
+
+
+def gather_tensor(shards, offset: int, n: int) -> np.ndarray:
+    """Stage-3 fetch: tensor elements [offset, offset + n) of the flat buffer,
+    read from the N rank shards (arrays of S uint16 or float32 each)."""
+    shards = [np.ascontiguousarray(x) for x in shards]
+    N, S = len(shards), shards[0].size
+    assert all(x.size == S and x.dtype == shards[0].dtype for x in shards)
+    eb = shards[0].dtype.itemsize
+    out = np.zeros(int(n), dtype=shards[0].dtype)
+    table = (ctypes.c_void_p * N)(*[_ptr(x) for x in shards])
+    if lib().or_gather_tensor(table, N, S, eb, int(offset), int(n), _ptr(out)) != 0:
+        raise ValueError("gather_tensor: bad arguments")
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -321,6 +321,29 @@ int or_ring_ag(const float* chunks, int64_t N, int64_t S, float* gathered, int64
     return OR_OK;
 }
 
+/*
+ * Stage-3 fetch of one tensor: the parameters are partitioned like the flat
+ * buffer (rank r owns [r*S, (r+1)*S)) and gathered before the layer that uses
+ * them ("ZeRO Optimizer", "ZeRO Stages" stage 3 and "Communication Patterns",
+ * all-gather of only the required parameter subset). Element e of the tensor at
+ * flat offset `offset` is element (offset + e) - r*S of rank r's shard, with
+ * r = (offset + e) / S. elem_bytes is 2 (bf16 parameters) or 4; the copy is
+ * bitwise.
+ */
+int or_gather_tensor(const void* const* shards, int64_t N, int64_t S, int32_t elem_bytes,
+                     int64_t offset, int64_t n, void* out) {
+    if (N < 1 || S < 1 || n < 0 || offset < 0 || offset + n > N * S ||
+        (elem_bytes != 2 && elem_bytes != 4))
+        return OR_EINVAL;
+    for (int64_t e = 0; e < n; e++) {
+        int64_t f = offset + e;
+        int64_t r = f / S;
+        const char* src = (const char*)shards[r] + (size_t)(f - r * S) * (size_t)elem_bytes;
+        memcpy((char*)out + (size_t)e * (size_t)elem_bytes, src, (size_t)elem_bytes);
+    }
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* bfloat16                                                                  */
 /* ------------------------------------------------------------------------ */

@@ -21,6 +21,7 @@ import test_oracle_memory as TM
 import test_oracle_reduce as TR
 import test_oracle_ring as TG
 import test_oracle_step as TS
+import test_oracle_gather as TGA
 import test_oracle_wire as TW
 
 MUTANTS = {
@@ -45,6 +46,8 @@ MUTANTS = {
     "stage2_grads_not_partitioned": ("case 2: par = P;  grd = Pn;", "case 2: par = P;  grd = P;"),
     "ring_adds_twice": ("partial[k * S + e] = or_hold(msg[k * S + e] + own[e], wire_dtype);",
                         "partial[k * S + e] = or_hold(msg[k * S + e] + own[e] + own[e], wire_dtype);"),
+    "gather_uses_first_rank": ("        int64_t r = f / S;\n", "        int64_t r = offset / S;\n"),
+    "gather_off_by_one": ("(size_t)(f - r * S) * (size_t)elem_bytes", "(size_t)(f - r * S + (e > 0)) * (size_t)elem_bytes"),
     "wire_not_rounded": ("return or_hold(acc + x, dtype == OR_BF16_WIRE ? OR_BF16 : OR_F32);",
                          "return acc + x;"),
     "wire_truncates": ("return wire_dtype == 0 ? x : or_bf16_to_f32(or_f32_to_bf16(x));",
@@ -90,6 +93,10 @@ def all_pins(orc):
                                for n in (2, 3)]),
         ("wire_exact", lambda: TW.test_no_rounding_when_sums_are_bf16_exact(orc)),
         ("wire_skip", lambda: TW.test_wire_rounding_can_decide_the_skip(orc)),
+        ("gather_ring", lambda: [TGA.test_gather_equals_ring_all_gather_slices(orc, n)
+                                 for n in (2, 3)]),
+        ("gather_round_trip", lambda: TGA.test_round_trip_through_segments(orc, 1, 1)),
+        ("gather_edges", lambda: TGA.test_tensor_spanning_every_rank_and_edges(orc)),
     ]
     for name, fn in cases:
         try:
