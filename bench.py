@@ -220,6 +220,63 @@ def offload_bench(args, Z, w, S, reps, p0, gdt) -> int:
     return 0
 
 
+def gather_bench(args, Z, W, w, S) -> int:
+    """Stage-3 fetch: the model's tensors copied out of the N bf16 rank shards
+    (the gathered parameter buffer's slots) into temporaries, one layer at a time
+    and all at once. Algorithmic bytes: 2 bytes read + 2 written per element."""
+    import torch
+    dev = torch.device("cuda:0")
+    h = Z.zero_layout_build(list(w.numels), w.N, w.A, w.B)
+    try:
+        offsets = Z.zero_layout_offsets(h)
+    finally:
+        Z.zero_layout_free(h)
+    shards = [torch.randint(-32768, 32767, (S,), dtype=torch.int16, device=dev) for _ in range(w.N)]
+    numels = list(w.numels)
+    per_layer = W.layer_tensor_count(w.name)
+    first = W.first_layer_tensor(w.name)
+    layer = list(range(first, first + per_layer))
+    outs_all = [torch.empty(n, dtype=torch.int16, device=dev) for n in numels]
+
+    def timed(idx, reps):
+        nums = [numels[t] for t in idx]
+        plan = Z.GatherPlan(shards, S, [offsets[t] for t in idx], nums, [outs_all[t] for t in idx])
+        for _ in range(args.warmup):
+            plan()
+        # back to back, one event pair around all calls: the host's call overhead
+        # overlaps the copies of the calls before it
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            plan()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps, sum(nums)
+
+    t_layer, n_layer = timed(layer, args.steps)
+    t_all, n_all = timed(list(range(len(numels))), max(5, args.steps // 10))
+    gbs_all = 4 * n_all / t_all / 1e9
+    log(f"gather: layer ({per_layer} tensors, {n_layer} elements) {t_layer * 1e6:.1f} us "
+        f"= {4 * n_layer / t_layer / 1e9:.0f} GB/s; model ({len(numels)} tensors) "
+        f"{t_all * 1e3:.3f} ms = {gbs_all:.0f} GB/s")
+    out = {
+        "metric": "stage-3 fetch: achieved HBM GB/s (bf16 tensors out of the rank shards)",
+        "value": gbs_all, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_all * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (bit copy)", "data": "synthetic",
+        "config": {"workload": f"{w.name} parameters, N={w.N} shards of S={S}",
+                   "n_tensors": len(numels), "elements": n_all},
+        "layer": {"tensors": per_layer, "elements": n_layer, "us": t_layer * 1e6,
+                  "gbs": 4 * n_layer / t_layer / 1e9},
+        "roofline": {"bound": "hbm", "achieved": gbs_all, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs_all / HBM_PEAK_GBS, "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +317,9 @@ def main() -> int:
                          "v in host memory; host Adam on chunks as they cross)")
     ap.add_argument("--chunk-elems", type=int, default=0,
                     help="--offload: elements per host chunk (0: the library's default)")
+    ap.add_argument("--gather", action="store_true",
+                    help="instead of the default line: time the stage-3 fetch (whole tensors out "
+                         "of the N bf16 rank shards) for one transformer layer and for the model")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -300,6 +360,8 @@ def main() -> int:
     finally:
         Z.zero_layout_free(h)
     log(f"workload {w.name}: S={S} N={w.N} grad={w.grad_dtype} buckets={nb}")
+    if args.gather:
+        return gather_bench(args, Z, W, w, S)
 
     tdt = torch.int16 if w.grad_dtype == "bf16" else torch.float32
     reps = []

@@ -429,6 +429,32 @@ int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, 
                          int32_t part, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Stage-3 fetch: whole tensors out of the rank shards                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Stage 3 partitions the parameters like the gradients and optimizer state and
+ * gathers the ones a layer needs just before it runs, freeing them afterwards
+ * ("ZeRO Optimizer", "ZeRO Stages" stage 3 and "Communication Patterns",
+ * all-gather of the required parameter subset; "Why does not the stage 3
+ * implementation use broadcast and reduce-scatter?": all-gather rather than
+ * broadcast). Tensor k occupies flat elements [offsets[k], offsets[k] + numels[k])
+ * (zero_layout_offsets) and rank r's shard holds flat elements [r*shard_S,
+ * (r+1)*shard_S); this copies every listed tensor, bit for bit, from the
+ * n_shards device shards into outs[k] (device, numels[k] contiguous elements),
+ * on `stream`. elem_bytes: 2 (bf16 parameters) or 4. The caller owns outs and
+ * frees them after the layer. shards and outs must be element-aligned; outs must
+ * not overlap the shards or each other. Empty tensors are skipped.
+ * Errors: ZERO_E_INVAL (NULL pointer, elem_bytes not 2 or 4, overlap),
+ * ZERO_E_ALIGN, ZERO_E_RANGE (n_shards outside [1, 256], shard_S outside
+ * [1, 2^40], n_tensors < 0, a tensor leaving the n_shards * shard_S buffer),
+ * ZERO_E_HIP.
+ */
+int zero_gather_tensors(const void* const* shards, int32_t n_shards, int64_t shard_S,
+                        int32_t elem_bytes, const int64_t* offsets, const int64_t* numels,
+                        void* const* outs, int32_t n_tensors, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Optimizer state offloaded to host memory                                   */
 /* ------------------------------------------------------------------------ */
 

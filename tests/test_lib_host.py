@@ -316,3 +316,29 @@ def test_train_step_part_validation(Z):
     assert status([32, 64], args=b) == -6    # bucket tables are not split into parts
     a.lr = -1.0
     assert status([32, 64]) == -1            # the whole-step checks apply too
+
+
+def test_gather_tensors_validation(Z):
+    L = Z.lib()
+    sh = (ctypes.c_void_p * 2)(FAKE, FAKE + 4096)
+    offs = (ctypes.c_int64 * 2)(0, 10)
+    nums = (ctypes.c_int64 * 2)(10, 20)
+    outs = (ctypes.c_void_p * 2)(FAKE + 8192, FAKE + 12288)
+
+    def call(shards=sh, n_shards=2, S=64, eb=2, o=offs, n=nums, out=outs, k=2):
+        return L.zero_gather_tensors(shards, n_shards, S, eb, o, n, out, k, None)
+
+    assert call(shards=None) == -1
+    assert call(n_shards=0) == -3
+    assert call(n_shards=300) == -3
+    assert call(S=0) == -3
+    assert call(eb=3) == -1
+    assert call(k=-1) == -3
+    assert call(o=None) == -1
+    assert call(o=(ctypes.c_int64 * 2)(0, 120)) == -3           # 120 + 20 > 2 * 64
+    assert call(n=(ctypes.c_int64 * 2)(10, -1)) == -3
+    assert call(out=(ctypes.c_void_p * 2)(FAKE + 8192, FAKE + 12289)) == -2
+    assert call(out=(ctypes.c_void_p * 2)(FAKE + 8192, FAKE + 8200)) == -1     # outs overlap
+    assert call(out=(ctypes.c_void_p * 2)(FAKE + 8192, FAKE + 4100)) == -1     # out in a shard
+    assert call(shards=(ctypes.c_void_p * 2)(FAKE, FAKE + 4097)) == -2
+    assert call(k=0) == 0                                                      # nothing to do

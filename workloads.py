@@ -59,6 +59,16 @@ def llama_numels(layers: int, d: int, ffn: int, vocab: int, kv_dim: Optional[int
     return out
 
 
+def layer_tensor_count(name: str) -> int:
+    """Tensors per transformer layer in the lists above (1 for the other lists)."""
+    return {"gpt2s": 12, "llama7b": 9, "llama70b": 9}.get(name, 1)
+
+
+def first_layer_tensor(name: str) -> int:
+    """Index of the first tensor of layer 0 (after the embeddings)."""
+    return {"gpt2s": 2, "llama7b": 1, "llama70b": 1}.get(name, 0)
+
+
 def ragged_numels(seed: int = 1234, count: int = 10_000, hi: int = 65536, N: int = 64) -> List[int]:
     """Log-uniform sizes in [1, hi]; the raw total is kept non-divisible by N."""
     rng = np.random.default_rng(seed)

@@ -18,6 +18,6 @@ from ._binding import (  # noqa: F401
     zero_layout_segments, zero_reduce_shard, zero_segment, zero_stats, zero_train_state,
     zero_version, zero_workspace_bytes, zero_device_state, zero_device_state_init,
     zero_device_state_load, zero_train_step_part, part_table, zero_host_adam,
-    zero_offload_step, zero_offload_args, zero_host_adam_args,
+    zero_offload_step, zero_offload_args, zero_host_adam_args, zero_gather_tensors, GatherPlan,
     zero_train_args, zero_train_step, make_train_args, device_state_from_tensor)
 from .shard_step import DeviceShardStep, OffloadShardStep, ShardStep  # noqa: F401

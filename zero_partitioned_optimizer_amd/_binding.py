@@ -137,6 +137,7 @@ def lib() -> ctypes.CDLL:
     L.zero_device_state_load.argtypes = [vp, vp, sz, P(zero_device_state), vp]
     L.zero_train_step.argtypes = [P(zero_train_args), vp]
     L.zero_train_step_part.argtypes = [P(zero_train_args), vp, i32, i32, vp]
+    L.zero_gather_tensors.argtypes = [P(vp), i32, i64, i32, P(i64), P(i64), P(vp), i32, vp]
     L.zero_host_adam.argtypes = [P(zero_host_adam_args)]
     L.zero_offload_step.argtypes = [P(zero_offload_args), vp, P(zero_stats)]
     L.zero_last_error.argtypes = []
@@ -148,7 +149,7 @@ def lib() -> ctypes.CDLL:
                  "zero_layout_mem_bytes", "zero_reduce_shard", "zero_adam_step",
                  "zero_gather_slot", "zero_commit_rule", "zero_device_state_init",
                  "zero_device_state_load", "zero_train_step", "zero_train_step_part",
-                 "zero_host_adam", "zero_offload_step"):
+                 "zero_host_adam", "zero_offload_step", "zero_gather_tensors"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -397,6 +398,34 @@ def zero_offload_step(args: zero_offload_args, stream=None) -> tuple:
     st = zero_stats()
     rc = _check(lib().zero_offload_step(ctypes.byref(args), _stream(stream), ctypes.byref(st)))
     return rc, st
+
+
+class GatherPlan:
+    """The marshalled arguments of one zero_gather_tensors call, reusable: calling
+    the plan enqueues the copies again (same shards, tensors and outputs)."""
+
+    def __init__(self, shards, shard_S: int, offsets, numels, outs):
+        self.k = len(numels)
+        self.outs = outs
+        self._keep = (shards, outs)
+        self.args = (_replica_table(shards), len(shards), int(shard_S), shards[0].element_size(),
+                     (i64 * max(self.k, 1))(*[int(o) for o in offsets]),
+                     (i64 * max(self.k, 1))(*[int(n) for n in numels]),
+                     (vp * max(self.k, 1))(*[_addr(o) for o in outs]), self.k)
+
+    def __call__(self, stream=None):
+        _check(lib().zero_gather_tensors(*self.args, _stream(stream)))
+        return self.outs
+
+
+def zero_gather_tensors(shards, shard_S: int, offsets, numels, outs=None, stream=None):
+    """Copy whole tensors out of the rank shards (device tensors of shard_S elements,
+    2- or 4-byte elements). outs: device tensors to fill, or None to allocate them
+    (same dtype as the shards). Returns the outputs."""
+    numels = [int(n) for n in numels]
+    if outs is None:
+        outs = [torch.empty(n, dtype=shards[0].dtype, device=shards[0].device) for n in numels]
+    return GatherPlan(shards, shard_S, offsets, numels, outs)(stream)
 
 
 def part_table(part_ends):

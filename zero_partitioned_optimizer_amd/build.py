@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libzero.so")
-SOURCES = ["abi.cpp", "layout.cpp", "step_kernels.hip"]
+SOURCES = ["abi.cpp", "layout.cpp", "step_kernels.hip", "gather_kernels.hip"]
 # host-only C++ (no device pass), compiled to an object and linked in
 HOST_SOURCES = ["offload.cpp"]
 HOST_FLAGS = ["-x", "c++", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-c"]

@@ -616,6 +616,68 @@ int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, 
                       fn);
 }
 
+int zero_gather_tensors(const void* const* shards, int32_t n_shards, int64_t shard_S,
+                        int32_t elem_bytes, const int64_t* offsets, const int64_t* numels,
+                        void* const* outs, int32_t n_tensors, void* stream) {
+    static const char* fn = "zero_gather_tensors";
+    if (n_tensors < 0) {
+        set_error("%s: n_tensors=%d is negative", fn, (int)n_tensors);
+        return ZERO_E_RANGE;
+    }
+    if (!shards || (n_tensors > 0 && (!offsets || !numels || !outs))) {
+        set_error("%s: shards, offsets, numels or outs is NULL", fn);
+        return ZERO_E_INVAL;
+    }
+    if (n_shards < 1 || n_shards > ZERO_MAX_REPLICAS || shard_S < 1 ||
+        shard_S > (int64_t(1) << 40)) {
+        set_error("%s: n_shards=%d shard_S=%lld out of range", fn, (int)n_shards,
+                  (long long)shard_S);
+        return ZERO_E_RANGE;
+    }
+    if (elem_bytes != 2 && elem_bytes != 4) {
+        set_error("%s: elem_bytes=%d is neither 2 nor 4", fn, (int)elem_bytes);
+        return ZERO_E_INVAL;
+    }
+    const int64_t L_pad = (int64_t)n_shards * shard_S;
+    const uintptr_t eb = (uintptr_t)elem_bytes;
+    for (int32_t r = 0; r < n_shards; ++r) {
+        if (!shards[r] || (reinterpret_cast<uintptr_t>(shards[r]) % eb) != 0) {
+            set_error("%s: shards[%d]=%p is NULL or not element-aligned", fn, (int)r, shards[r]);
+            return shards[r] ? ZERO_E_ALIGN : ZERO_E_INVAL;
+        }
+    }
+    for (int32_t k = 0; k < n_tensors; ++k) {
+        const int64_t o = offsets[k], n = numels[k];
+        if (o < 0 || n < 0 || o > L_pad || n > L_pad - o) {
+            set_error("%s: tensor %d at offset %lld with %lld elements leaves the %lld-element "
+                      "buffer", fn, (int)k, (long long)o, (long long)n, (long long)L_pad);
+            return ZERO_E_RANGE;
+        }
+        if (n > 0 && !outs[k]) {
+            set_error("%s: outs[%d] is NULL", fn, (int)k);
+            return ZERO_E_INVAL;
+        }
+        if ((reinterpret_cast<uintptr_t>(outs[k]) % eb) != 0) {
+            set_error("%s: outs[%d]=%p is not element-aligned", fn, (int)k, outs[k]);
+            return ZERO_E_ALIGN;
+        }
+        const Span sk = span("out", outs[k], n * elem_bytes);
+        for (int32_t r = 0; r < n_shards; ++r)
+            if (overlap(sk, span("shard", shards[r], shard_S * elem_bytes))) {
+                set_error("%s: outs[%d] overlaps shards[%d]", fn, (int)k, (int)r);
+                return ZERO_E_INVAL;
+            }
+        for (int32_t j = 0; j < k; ++j)
+            if (overlap(sk, span("out", outs[j], numels[j] * elem_bytes))) {
+                set_error("%s: outs[%d] overlaps outs[%d]", fn, (int)k, (int)j);
+                return ZERO_E_INVAL;
+            }
+    }
+    return hip_status(zk::launch_gather(shards, n_shards, shard_S, elem_bytes, offsets, numels, outs,
+                                        n_tensors, static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
 int zero_gather_slot(const float* master_dev, int64_t shard_S, uint16_t* slot_bf16_dev,
                      void* stream) {
     static const char* fn = "zero_gather_slot";
