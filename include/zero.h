@@ -179,9 +179,12 @@ typedef struct {
 } zero_stats;
 
 /*
- * Bytes of device workspace a reduce, Adam or train-step call needs (per-workgroup
- * fp64 partials; 3 MiB). The same workspace may be reused by
- * consecutive calls on one stream; calls that run concurrently need their own.
+ * Bytes of device workspace a reduce, Adam or train-step call on a shard of
+ * shard_S elements needs: 24 bytes of fp64 partials per workgroup, for one
+ * workgroup per 1,024 elements plus one per part of a split step (at most
+ * 4,096), capped at 4,194,304 workgroups (about 20 MB for a 842M-element shard).
+ * The same workspace may be reused by consecutive calls on one stream; calls
+ * that run concurrently need their own.
  */
 size_t zero_workspace_bytes(int64_t shard_S);
 
@@ -419,11 +422,10 @@ int zero_train_step(const zero_train_args* args, void* stream);
  * and commits, as zero_train_step does; with a single slot the restore kernel
  * follows the last part. p, m, v and the slot come out bit-identical to
  * zero_train_step's; the squared norm is summed in another grouping (equal
- * within rounding). Each part takes at most kGridMax / n_parts workgroups, so the
- * workspace of zero_workspace_bytes(shard_S) suffices. args must carry no
+ * within rounding). The workspace of zero_workspace_bytes(shard_S) suffices. args must carry no
  * bucket table (ZERO_E_UNSUPPORTED); parts cover padding like a whole-shard step.
  * Errors: as zero_train_step; ZERO_E_INVAL for a NULL part_ends; ZERO_E_RANGE for
- * n_parts outside [1, 131072], part outside [0, n_parts) or a bad boundary.
+ * n_parts outside [1, 4096], part outside [0, n_parts) or a bad boundary.
  */
 int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, int32_t n_parts,
                          int32_t part, void* stream);

@@ -184,8 +184,7 @@ const char* zero_last_error(void) { return zl::g_err.c_str(); }
 const char* zero_version(void) { return "libzero 1.0 (gfx950)"; }
 
 size_t zero_workspace_bytes(int64_t shard_S) {
-    (void)shard_S;
-    return (size_t)zk::kGridMax * zk::kPartialBytes;
+    return (size_t)zk::grid_bound(shard_S) * zk::kPartialBytes;
 }
 
 int zero_reduce_shard(const void* const* replicas, int32_t n_replicas, zero_dtype grad_dtype,
@@ -561,7 +560,7 @@ int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, 
         set_error("%s: part_ends is NULL", fn);
         return ZERO_E_INVAL;
     }
-    if (n_parts < 1 || n_parts > zk::kGridMax || part < 0 || part >= n_parts) {
+    if (n_parts < 1 || n_parts > zk::kMaxParts || part < 0 || part >= n_parts) {
         set_error("%s: part %d of n_parts=%d out of range", fn, (int)part, (int)n_parts);
         return ZERO_E_RANGE;
     }

@@ -487,14 +487,30 @@ __device__ __noinline__ void collect_and_commit(const uint64_t* base, int n, zer
     bool timed_out = false;
     double sq = 0.0;
     uint32_t bad = 0u, badb = 0u;
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-        uint64_t w0, w1, w2;
+    // thread t takes partials t, t + kBlock, t + 2 kBlock, ... in that order, kBatch
+    // at a time: their loads are all in flight before the tags are checked
+    constexpr int kBatch = 4;
+    for (int b = threadIdx.x; b < n; b += kBatch * kBlock) {
+        uint64_t w[kBatch][3];
+        uint32_t want = 0u, have = 0u;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (b + k * kBlock < n) want |= 1u << k;
         for (;;) {
-            w0 = __hip_atomic_load(base + 3 * (int64_t)i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            w1 = __hip_atomic_load(base + 3 * (int64_t)i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            w2 = __hip_atomic_load(base + 3 * (int64_t)i + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((uint32_t)(w0 >> 32) == tag && (uint32_t)(w1 >> 32) == tag && (uint32_t)(w2 >> 32) == tag)
-                break;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                if (!((want & ~have) >> k & 1u)) continue;
+                const uint64_t* q = base + 3 * (int64_t)(b + k * kBlock);
+                w[k][0] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                w[k][1] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                w[k][2] = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                if ((uint32_t)(w[k][0] >> 32) == tag && (uint32_t)(w[k][1] >> 32) == tag &&
+                    (uint32_t)(w[k][2] >> 32) == tag)
+                    have |= (want >> k & 1u) << k;
+            if (have == want) break;
             if (__builtin_amdgcn_s_memrealtime() - t0 > kCollectTimeout) {
                 timed_out = true;
                 break;
@@ -502,10 +518,14 @@ __device__ __noinline__ void collect_and_commit(const uint64_t* base, int n, zer
             __builtin_amdgcn_s_sleep(8);
         }
         if (timed_out) break;
-        const uint64_t bits = ((w0 & 0xffffffffull) << 32) | (w1 & 0xffffffffull);
-        sq += __longlong_as_double((long long)bits);
-        bad |= (uint32_t)(w2 & 1u);
-        badb += (uint32_t)(w2 & 0xffffffffull) >> 1;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (!(want >> k & 1u)) continue;
+            const uint64_t bits = ((w[k][0] & 0xffffffffull) << 32) | (w[k][1] & 0xffffffffull);
+            sq += __longlong_as_double((long long)bits);
+            bad |= (uint32_t)(w[k][2] & 1u);
+            badb += (uint32_t)(w[k][2] & 0xffffffffull) >> 1;
+        }
     }
     uint32_t tmo = timed_out ? 1u : 0u;
     block_reduce(sq, bad, badb);
@@ -662,7 +682,10 @@ __global__ void k_state_write(zero_device_state* s, zero_device_state rec, uint6
 // Quads per lane per trip: two rows keep more bytes in flight when few replica
 // streams are open; with many replicas one row keeps the register budget (and so
 // the occupancy) up.
-int rows_for(int32_t n_rep) { return n_rep <= 16 ? 2 : 1; }
+#ifndef ZERO_ROWS_FEW
+#define ZERO_ROWS_FEW 1
+#endif
+int rows_for(int32_t n_rep) { return n_rep <= 16 ? ZERO_ROWS_FEW : 1; }
 
 // Workgroups of the step kernel: many more than the chip holds at once (short
 // workgroups, so faster CUs pick up more of the work and the tail is short;
@@ -671,7 +694,11 @@ int rows_for(int32_t n_rep) { return n_rep <= 16 ? 2 : 1; }
 // the same number of full trips (no ragged last round).
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid) {
     if (max_grid <= 0 || max_grid > kGridMax) max_grid = kGridMax;
-    if (n_buckets > 0) return (int)(n_buckets < max_grid ? n_buckets : max_grid);
+    if (n_buckets > 0) {
+        // bucket launches stride over the table; at most grid_bound(S) workgroups
+        int64_t g = n_buckets < max_grid ? n_buckets : max_grid;
+        return (int)(g < grid_bound(S) ? g : grid_bound(S));
+    }
     const int64_t per_trip = (int64_t)rows_for(n_rep) * kBlock * kVec;
     const int64_t trips = S / per_trip;
     if (trips < 1) return 1;
@@ -702,8 +729,10 @@ static void launch_rows(const StepDesc& d, const KParams& k, int grid, hipStream
 
 template <typename RT, bool BUCKETS>
 static void launch_typed(const StepDesc& d, const KParams& k, int grid, hipStream_t st) {
-    if (rows_for(d.n_rep) == 2) launch_rows<RT, BUCKETS, 2>(d, k, grid, st);
-    else launch_rows<RT, BUCKETS, 1>(d, k, grid, st);
+    if constexpr (ZERO_ROWS_FEW == 2) {
+        if (rows_for(d.n_rep) == 2) return launch_rows<RT, BUCKETS, 2>(d, k, grid, st);
+    }
+    launch_rows<RT, BUCKETS, 1>(d, k, grid, st);
 }
 
 hipError_t launch_step(const StepDesc& d, hipStream_t st) {

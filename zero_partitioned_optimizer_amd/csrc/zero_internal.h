@@ -10,12 +10,26 @@
 namespace zk {
 
 #ifndef ZERO_GRID_MAX
-#define ZERO_GRID_MAX 131072
+#define ZERO_GRID_MAX 4194304
 #endif
 
-constexpr int kBlock = 256;         // threads per workgroup: 4 wave64s
+#ifndef ZERO_BLOCK
+#define ZERO_BLOCK 256
+#endif
+
+constexpr int kBlock = ZERO_BLOCK;  // threads per workgroup: 4 wave64s
 constexpr int kVec = 4;             // elements per lane per row (one quad)
 constexpr int kGridMax = ZERO_GRID_MAX;  // workgroups of the grid-stride step kernel
+constexpr int kMaxParts = 4096;          // parts of one step split over launches
+
+// Upper bound on the workgroups of any step launch over a shard of S elements
+// (one trip of kBlock * kVec elements each, plus one per part of a split step),
+// which sizes the workspace of partials.
+inline int64_t grid_bound(int64_t S) {
+    const int64_t trips = S > 0 ? (S + (int64_t)kBlock * kVec - 1) / ((int64_t)kBlock * kVec) : 1;
+    const int64_t g = trips + kMaxParts;
+    return g < kGridMax ? g : kGridMax;
+}
 constexpr int kCommitGrid = 512;    // workgroups of the commit / cast kernels
 constexpr int kFinalizeBlock = 256;
 
