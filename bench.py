@@ -392,6 +392,11 @@ def main() -> int:
     every = max(1, args.event_every)
     ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for k in range(0, K, every)}
+    # record every event once before the timed region: the HIP runtime grows its
+    # event pool on first use, a one-time stall of tens of milliseconds
+    for e0, e1 in ev.values():
+        e0.record()
+        e1.record()
     skipped = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
