@@ -22,6 +22,7 @@ import test_oracle_reduce as TR
 import test_oracle_ring as TG
 import test_oracle_step as TS
 import test_oracle_gather as TGA
+import test_oracle_golden as TGO
 import test_oracle_wire as TW
 
 MUTANTS = {
@@ -97,6 +98,9 @@ def all_pins(orc):
                                  for n in (2, 3)]),
         ("gather_round_trip", lambda: TGA.test_round_trip_through_segments(orc, 1, 1)),
         ("gather_edges", lambda: TGA.test_tensor_spanning_every_rank_and_edges(orc)),
+        ("golden_memory", lambda: [TGO.test_memory_per_device_matches_page(orc, n) for n in (2, 8)]),
+        ("golden_reduction", lambda: TGO.test_stated_reductions_are_byte_model_limits(orc)),
+        ("golden_ring", lambda: TGO.test_ring_fractions_for_eight_ranks(orc)),
     ]
     for name, fn in cases:
         try:
