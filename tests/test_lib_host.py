@@ -342,3 +342,37 @@ def test_gather_tensors_validation(Z):
     assert call(out=(ctypes.c_void_p * 2)(FAKE + 8192, FAKE + 4100)) == -1     # out in a shard
     assert call(shards=(ctypes.c_void_p * 2)(FAKE, FAKE + 4097)) == -2
     assert call(k=0) == 0                                                      # nothing to do
+
+
+def test_offload_step_validation(Z):
+    """Checks that reject an offloaded step before any device work is enqueued."""
+    L = Z.lib()
+    st = Z.zero_train_state(t=0, n_skipped=0, loss_scale=1.0, min_loss_scale=1.0, dynamic=0)
+    tbl = (ctypes.c_void_p * 1)(FAKE + 45056)
+
+    def args(**kw):
+        a = Z.zero_offload_args()
+        a.replicas = ctypes.cast(tbl, ctypes.POINTER(ctypes.c_void_p))
+        a.n_replicas, a.grad_dtype, a.shard_S = 1, 1, 64
+        a.g_dev, a.g_host, a.p_host, a.m_host, a.v_host = FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, FAKE + 16384
+        a.slot_host, a.slot_dev = FAKE + 20480, FAKE + 24576
+        a.lr, a.beta1, a.beta2, a.eps, a.weight_decay = 1e-3, 0.9, 0.999, 1e-8, 0.0
+        a.state = ctypes.pointer(st)
+        a.stats_dev, a.workspace_dev, a.ws_bytes = FAKE + 28672, FAKE + 32768, 4096
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    def status(**kw):
+        return L.zero_offload_step(ctypes.byref(args(**kw)), None, None)
+
+    assert L.zero_offload_step(None, None, None) == -1
+    assert status(state=None) == -1
+    assert status(stats_dev=None) == -1
+    assert status(g_host=None) == -1
+    assert status(slot_dev=None) == -1
+    assert status(chunk_elems=-5) == -3
+    assert status(beta1=1.5) == -1
+    assert status(lr=float("nan")) == -1
+    assert status(n_replicas=0) == -3          # from the reduce's own checks
+    assert st.t == 0 and st.n_skipped == 0      # nothing was committed
