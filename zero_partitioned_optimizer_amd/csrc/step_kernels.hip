@@ -373,8 +373,22 @@ __device__ __forceinline__ void quads(const KParams& a, const Res& rs, int64_t q
 template <typename RT, bool ADAM, bool WRITE_G>
 __device__ __forceinline__ void one_elem(const KParams& a, const Res& rs, int64_t e, double& sq,
                                          uint32_t& bad) {
+    // replica loads in batches of 8, all in flight before their adds (a spare load
+    // repeats the batch's first slot and is dropped): a lane on a bucket edge
+    // makes N / 8 memory round trips, not N
+    const int n = a.n_rep;
     float acc = Quad<RT>::one(a.rep[0], e);
-    for (int j = 1; j < a.n_rep; ++j) acc = Quad<RT>::add1(acc, Quad<RT>::one(a.rep[j], e));
+    for (int j = 1; j < n; j += 8) {
+        const int cnt = n - j < 8 ? n - j : 8;
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = Quad<RT>::one(a.rep[k < cnt ? j + k : j], e);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float s = Quad<RT>::add1(acc, x[k]);
+            acc = k < cnt ? s : acc;
+        }
+    }
     const float g = acc * rs.sc.inv;
     bad |= nonfinite(g) ? 1u : 0u;
     const double gd = (double)g;
