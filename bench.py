@@ -320,6 +320,10 @@ def main() -> int:
     ap.add_argument("--gather", action="store_true",
                     help="instead of the default line: time the stage-3 fetch (whole tensors out "
                          "of the N bf16 rank shards) for one transformer layer and for the model")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="write a 1 GiB buffer before every timed step so no step finds its data "
+                         "in the 256 MB Infinity Cache; `value` then comes from the step kernels' "
+                         "own event times (every step timed), not the wall clock")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -389,7 +393,8 @@ def main() -> int:
     for _ in range(args.warmup):
         step.step(reps)
     K = args.steps
-    every = max(1, args.event_every)
+    every = 1 if args.flush_mall else max(1, args.event_every)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush_mall else None
     ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for k in range(0, K, every)}
     # record every event once before the timed region: the HIP runtime grows its
@@ -402,17 +407,23 @@ def main() -> int:
     t0 = time.perf_counter()
     if args.commit == "device":
         for k in range(K):
+            if flush is not None:
+                flush.fill_(float(k))
             step.step(reps, events=ev.get(k))
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         skipped = int(step.state().n_skipped)
     else:
         for k in range(K):
+            if flush is not None:
+                flush.fill_(float(k))
             st, verdict = step.step(reps, events=ev.get(k))
             skipped += verdict == Z.ZERO_SKIP
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
     kms = [a.elapsed_time(b) for a, b in ev.values()]
+    if flush is not None:                  # the flushes are not part of the step
+        elapsed = sum(kms) / 1e3
     log(f"timed {K} steps in {elapsed:.4f} s; kernel mean {statistics.mean(kms) * 1e3:.1f} us, "
         f"median {statistics.median(kms) * 1e3:.1f} us, skipped {skipped}")
 
@@ -436,7 +447,7 @@ def main() -> int:
         "config": {"workload": f"{w.name} shard, rank {args.rank} of N={w.N}", "shard_elems": S,
                    "n_replicas": w.N, "grad_dtype": w.grad_dtype, "state_dtype": "f32",
                    "bytes_per_elem": bpe, "bucket_elems": args.bucket_elems,
-                   "commit": args.commit, "fold": args.fold,
+                   "commit": args.commit, "fold": args.fold, "mall_flushed": bool(args.flush_mall),
                    "slot": "single" if (args.single_slot or args.commit == "host") else "double"},
         "step_gbps": S * bpe / (elapsed / K) / 1e9,
         "kernel_us_mean": kernel_s * 1e6,
