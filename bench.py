@@ -301,7 +301,8 @@ def main() -> int:
                          "(the known-size reference for HBM byte counters under rocprofv3)")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="also run the plain-stream HBM probe (read, write, copy, 2:1 and 5:1 "
-                         "read:write mixes) and report it beside the roofline")
+                         "read:write mixes, and a stream of the step's own shape at this shard's "
+                         "size) and report it beside the roofline")
     ap.add_argument("--fold", default="f32", choices=["f32", "bf16-wire"],
                     help="f32: the fold keeps its running sum in fp32; bf16-wire: rounded to "
                          "bf16 after every add, as a ring with bf16 buffers (bf16 replicas only)")
@@ -463,12 +464,19 @@ def main() -> int:
         import subprocess
         probe = os.path.join(ROOT, "zero_partitioned_optimizer_amd", "hbm_probe")
         log("hbm probe ...")
-        res = subprocess.run([probe], capture_output=True, text=True, timeout=300)
+        cmd = [probe]
+        # the step-shaped stream at this shard's size, where a second copy of the
+        # step's buffers fits beside the bench's own
+        if w.grad_dtype == "bf16" and S % 4 == 0 and S * bpe <= 80e9:
+            cmd += ["1024", str(S), str(w.N)]
+        res = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
         if res.returncode != 0:
             raise RuntimeError("hbm_probe failed: " + res.stderr)
         hp = json.loads(res.stdout.strip().splitlines()[-1])
         mix = "mix_2to1" if bpe - 26 <= 2 * 14 else "mix_5to1"
         hp["step_kernel_vs_" + mix] = achieved / hp[mix]
+        if "step_shape" in hp:
+            hp["step_kernel_vs_step_shape"] = achieved / hp["step_shape"]["gbps"]
         out["hbm_probe"] = hp
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)

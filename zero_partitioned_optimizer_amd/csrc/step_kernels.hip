@@ -495,8 +495,8 @@ __device__ __forceinline__ void commit_record(zero_device_state* c, zero_stats* 
 // bad_buckets = 0xFFFFFFFF.
 constexpr uint64_t kCollectTimeout = 200000000ull;   // 2 s
 
-__device__ __noinline__ void collect_and_commit(const uint64_t* base, int n, zero_stats* stats,
-                                               zero_device_state* c, uint32_t tag) {
+__device__ __forceinline__ void collect_and_commit(const uint64_t* base, int n, zero_stats* stats,
+                                                  zero_device_state* c, uint32_t tag) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     bool timed_out = false;
     double sq = 0.0;
