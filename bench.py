@@ -76,9 +76,33 @@ def cpu_baseline(w, host_reps, p0_host, S, seconds: float, wire: bool = False):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    # the same oracle on one thread, for a quarter of the time
+    n1 = 0
+    t1 = time.perf_counter()
+    while True:
+        oracle.step(host_reps, p, m, v, slot, loss_scale=w.loss_scale, t=n + n1 + 1, nthreads=1,
+                    wire=wire, **w.hyper())
+        n1 += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= seconds / 4:
+            break
     return {"value": n * S / el, "unit": "elements/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{w.name} rank-0 shard, S={S} elements, N={w.N} replicas, {n} oracle "
-                      f"steps in {el:.1f} s, OpenMP threads={nthreads}"}
+                      f"steps in {el:.1f} s, OpenMP threads={nthreads}",
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": n1 * S / el1, "unit": "elements/s",
+                              "sample": f"{n1} oracle steps in {el1:.1f} s, 1 thread"}}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def overlap_bench(args, Z, w, S, pool, p0, kw, gdt) -> int:

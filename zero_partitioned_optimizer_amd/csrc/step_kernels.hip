@@ -16,14 +16,18 @@
 //  - wave64 lanes each own one quad (4 consecutive elements) per row: bf16
 //    replicas come in as dwordx2, fp32 state as dwordx4, so a wave reads 512 B
 //    (bf16) or 1 KiB (fp32) contiguous per instruction;
-//  - every lane issues its p/m/v loads and a whole batch of up to 8 replica
-//    loads before the first add, for bytes in flight;
-//  - a fixed grid of at most kGridMax workgroups strides over the shard, so the
-//    working front stays compact in HBM and the per-workgroup partials stay few;
+//  - every lane issues its p/m/v loads and the first batch of up to 8 replica
+//    loads (slots 0 .. 7) before the first add, then the remaining replicas in
+//    batches of 8, each batch all in flight before its adds;
+//  - one short workgroup per 1,024 elements (one quad per lane, one trip),
+//    far more workgroups than are resident, so faster CUs take more of them
+//    and the tail is one short workgroup; beyond kGridMax workgroups the grid
+//    strides over the shard with the same number of trips per workgroup;
 //  - the flag and the fp64 squared norm are reduced with wave shuffles, then
-//    LDS, then one partial per workgroup; a one-workgroup finalize sums the
-//    partials in workgroup order, so the norm is bit-reproducible and no
-//    atomics or memsets are needed;
+//    LDS, then one partial per workgroup, summed in workgroup order (by a
+//    one-workgroup finalize kernel, or, with the device commit, by workgroup 0
+//    of the same launch), so the norm is bit-reproducible; there are no float
+//    atomics and no memsets;
 //  - loads of data read once use the nontemporal hint, and so do the stores.
 // Arithmetic is one IEEE fp32 operation per source operation, built with
 // -ffp-contract=off; division and sqrt are the correctly rounded forms.
@@ -227,16 +231,44 @@ __device__ __forceinline__ void fold_batch(const KParams& a, int j, int64_t q0, 
     }
 }
 
-// acc = R_0 + R_1 + ... + R_{N-1}, left to right, for ROWS quads.
+// Slots 0 .. K-1 as the first batch: all K loads in flight, then acc = R_0 and
+// R_1 .. R_{K-1} added in slot order.
+template <typename RT, int ROWS, int K>
+__device__ __forceinline__ void fold_head(const KParams& a, int64_t q0, int64_t qs,
+                                          f32x4 (&acc)[ROWS]) {
+    typename Quad<RT>::V buf[K][ROWS];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const void* base = a.rep[k];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) buf[k][r] = Quad<RT>::load(base, q0 + r * qs);
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) acc[r] = Quad<RT>::widen(buf[0][r]);
+#pragma unroll
+    for (int k = 1; k < K; ++k) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) acc[r] = Quad<RT>::add(acc[r], Quad<RT>::widen(buf[k][r]));
+    }
+}
+
+// acc = R_0 + R_1 + ... + R_{N-1}, left to right, for ROWS quads: slots 0 .. 7
+// in one batch (with the state loads already issued, a lane's first memory
+// round trip carries up to eight replica loads), then batches of 8 and the rest.
 template <typename RT, int ROWS>
 __device__ __forceinline__ void fold(const KParams& a, int64_t q0, int64_t qs, f32x4 (&acc)[ROWS]) {
-    {
-        const void* base = a.rep[0];
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) acc[r] = Quad<RT>::widen(Quad<RT>::load(base, q0 + r * qs));
-    }
     const int n = a.n_rep;
-    int j = 1;
+    switch (n < 8 ? n : 8) {
+        case 8: fold_head<RT, ROWS, 8>(a, q0, qs, acc); break;
+        case 7: fold_head<RT, ROWS, 7>(a, q0, qs, acc); break;
+        case 6: fold_head<RT, ROWS, 6>(a, q0, qs, acc); break;
+        case 5: fold_head<RT, ROWS, 5>(a, q0, qs, acc); break;
+        case 4: fold_head<RT, ROWS, 4>(a, q0, qs, acc); break;
+        case 3: fold_head<RT, ROWS, 3>(a, q0, qs, acc); break;
+        case 2: fold_head<RT, ROWS, 2>(a, q0, qs, acc); break;
+        default: fold_head<RT, ROWS, 1>(a, q0, qs, acc); break;
+    }
+    int j = 8;
     for (; j + 8 <= n; j += 8) fold_batch<RT, ROWS, 8>(a, j, q0, qs, acc);
     switch (n - j) {
         case 7: fold_batch<RT, ROWS, 7>(a, j, q0, qs, acc); break;
