@@ -1,0 +1,35 @@
+"""bench.py's command line on a machine without a GPU: more than one GPU is refused
+with a message before anything touches a device, and the help text lists the
+measurement modes."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run(*args, env=None):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=120, cwd=ROOT, env=env)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = run("--gpus", "8", "--steps", "1", "--warmup", "0")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 8" in r.stderr
+    assert r.stdout == ""
+
+
+def test_world_size_above_one_is_refused():
+    env = dict(os.environ, WORLD_SIZE="2", RANK="0", LOCAL_RANK="0")
+    r = run("--gpus", "1", env=env)
+    assert r.returncode == 2
+    assert "WORLD_SIZE=2" in r.stderr
+
+
+def test_help_lists_the_modes():
+    r = run("--help")
+    assert r.returncode == 0
+    for flag in ("--config", "--commit", "--hbm-probe", "--fold", "--overlap", "--offload",
+                 "--gather", "--flush-mall", "--cpu-seconds", "--calibrate-copy"):
+        assert flag in r.stdout
