@@ -204,6 +204,8 @@ size_t zero_workspace_bytes(int64_t shard_S);
  *   one that leaves [0, shard_S) is skipped and counted in stats->bad_buckets.
  * grad_out_dev: fp32 [shard_S] output of g, or NULL.
  * stats_dev: device zero_stats. workspace_dev/ws_bytes: >= zero_workspace_bytes.
+ * The outputs (grad_out, stats, workspace) must not overlap one another, a
+ * replica or the bucket table (ZERO_E_INVAL).
  * Errors: ZERO_E_INVAL, ZERO_E_ALIGN, ZERO_E_RANGE, ZERO_E_HIP.
  */
 int zero_reduce_shard(const void* const* replicas, int32_t n_replicas, zero_dtype grad_dtype,

@@ -194,6 +194,12 @@ def test_reduce_and_gather_validation(Z):
     assert L.zero_reduce_shard(tbl, 2, 1, 64, None, 0, -1.0, None, FAKE + 4096, FAKE + 8192, ws, None) == -1
     assert L.zero_reduce_shard(tbl, 2, 1, 64, None, 0, 1.0, FAKE + 64, FAKE + 4096, FAKE + 8192, ws, None) == -1
     assert L.zero_reduce_shard(tbl, 2, 1, 64, None, 0, 1.0, None, None, FAKE + 8192, ws, None) == -1
+    # stats inside a replica, workspace over stats, workspace over the bucket table
+    assert L.zero_reduce_shard(tbl, 2, 1, 64, None, 0, 1.0, None, FAKE + 16, FAKE + 8192, ws, None) == -1
+    assert L.zero_reduce_shard(tbl, 2, 1, 64, None, 0, 1.0, None, FAKE + 8192, FAKE + 8192 - 16, ws,
+                               None) == -1
+    assert L.zero_reduce_shard(tbl, 2, 1, 64, FAKE + 8192 + 64, 2, 1.0, None, FAKE + 4096, FAKE + 8192,
+                               ws, None) == -1
     assert L.zero_gather_slot(FAKE, 64, FAKE + 8, None) == -2
     assert L.zero_gather_slot(FAKE, 64, FAKE + 64, None) == -1
     assert L.zero_gather_slot(None, 64, FAKE, None) == -1

@@ -205,17 +205,26 @@ int zero_reduce_shard(const void* const* replicas, int32_t n_replicas, zero_dtyp
         set_error("%s: grad_out_dev is not 16-byte aligned", fn);
         return ZERO_E_ALIGN;
     }
+    // Aliasing: the outputs (grad_out, stats, workspace) must be pairwise disjoint
+    // and disjoint from every replica and from the bucket table.
     const int64_t gb = elem_bytes(grad_dtype);
-    if (grad_out_dev) {
-        const Span out = span("grad_out", grad_out_dev, 4 * shard_S);
-        for (int32_t j = 0; j < n_replicas; ++j)
-            if (overlap(out, span("replica", replicas[j], gb * shard_S))) {
-                set_error("%s: grad_out overlaps replicas[%d]", fn, (int)j);
+    const Span outs[] = {span("grad_out", grad_out_dev, grad_out_dev ? 4 * shard_S : 0),
+                         span("stats", stats_dev, 16),
+                         span("workspace", workspace_dev, (int64_t)ws_bytes)};
+    const int n_outs = 3;
+    for (int i = 0; i < n_outs; ++i) {
+        for (int k = i + 1; k < n_outs; ++k)
+            if (overlap(outs[i], outs[k])) {
+                set_error("%s: outputs %s and %s overlap", fn, outs[i].name, outs[k].name);
                 return ZERO_E_INVAL;
             }
-        if (overlap(out, span("stats", stats_dev, 16)) ||
-            overlap(out, span("workspace", workspace_dev, (int64_t)ws_bytes))) {
-            set_error("%s: grad_out overlaps stats or workspace", fn);
+        for (int32_t j = 0; j < n_replicas; ++j)
+            if (overlap(outs[i], span("replica", replicas[j], gb * shard_S))) {
+                set_error("%s: %s overlaps replicas[%d]", fn, outs[i].name, (int)j);
+                return ZERO_E_INVAL;
+            }
+        if (n_buckets > 0 && overlap(outs[i], span("buckets", buckets_dev, 16 * n_buckets))) {
+            set_error("%s: %s overlaps the bucket table", fn, outs[i].name);
             return ZERO_E_INVAL;
         }
     }

@@ -30,6 +30,7 @@ struct GatherParams {
     int64_t numel[kGatherTensors];
     void* out[kGatherTensors];
     int64_t first_task[kGatherTensors + 1];   // prefix sums of the tensors' task counts
+    int64_t task_base;                        // task of workgroup 0 of this launch
 };
 
 // len elements from src to dst by the whole workgroup. Each lane issues up to
@@ -67,7 +68,7 @@ __device__ __forceinline__ void copy_piece(const E* __restrict__ src, E* __restr
 
 template <typename E>
 __global__ void __launch_bounds__(kBlock) k_gather(const GatherParams g) {
-    const int64_t task = blockIdx.x;
+    const int64_t task = g.task_base + blockIdx.x;
     int t = 0;
     while (t + 1 < g.n_tensors && g.first_task[t + 1] <= task) ++t;
     const int64_t n = g.numel[t];
@@ -102,13 +103,18 @@ hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S,
             g.first_task[i + 1] = g.first_task[i] + (g.numel[i] + kGatherChunk - 1) / kGatherChunk;
         }
         const int64_t tasks = g.first_task[k];
-        if (tasks == 0) continue;
-        if (elem_bytes == 2)
-            hipLaunchKernelGGL(k_gather<uint16_t>, dim3((unsigned)tasks), dim3(kBlock), 0, st, g);
-        else
-            hipLaunchKernelGGL(k_gather<uint32_t>, dim3((unsigned)tasks), dim3(kBlock), 0, st, g);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        // at most kGridMax workgroups per launch; a group with more tasks takes
+        // several launches over consecutive task ranges
+        for (int64_t t0 = 0; t0 < tasks; t0 += kGridMax) {
+            const int64_t n = tasks - t0 < kGridMax ? tasks - t0 : kGridMax;
+            g.task_base = t0;
+            if (elem_bytes == 2)
+                hipLaunchKernelGGL(k_gather<uint16_t>, dim3((unsigned)n), dim3(kBlock), 0, st, g);
+            else
+                hipLaunchKernelGGL(k_gather<uint32_t>, dim3((unsigned)n), dim3(kBlock), 0, st, g);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }

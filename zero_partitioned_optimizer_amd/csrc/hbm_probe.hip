@@ -130,8 +130,9 @@ int main(int argc, char** argv) {
     int64_t mib = argc > 1 ? atoll(argv[1]) : 1024;
     const int64_t shape_S = argc > 3 ? atoll(argv[2]) : 0;
     const int shape_N = argc > 3 ? atoi(argv[3]) : 0;
-    if (argc > 3 && (shape_S < 4 || shape_S % 4 != 0 || shape_N < 1 || shape_N > 256)) {
-        fprintf(stderr, "hbm_probe: S must be a positive multiple of 4 and N in [1, 256]\n");
+    if (argc > 3 && (shape_S < 4 || shape_S % 4 != 0 || shape_S > (int64_t(1) << 32) ||
+                     shape_N < 1 || shape_N > 256)) {
+        fprintf(stderr, "hbm_probe: S must be a positive multiple of 4 up to 2^32 and N in [1, 256]\n");
         return 1;
     }
     if (mib < 16) mib = 16;
