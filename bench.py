@@ -31,7 +31,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "fused shard step: elements/s and achieved HBM GB/s (% of MI355X peak)"
-KERNEL_SRC = os.path.join(ROOT, "zero_partitioned_optimizer_amd", "csrc", "step_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "zero_partitioned_optimizer_amd", "csrc", f)
+                  for f in ("step_kernels.hip", "zero_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -40,8 +41,18 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the step kernel's code: step_kernels.hip and zero_internal.h
+    with comments and whitespace removed, so that a comment edit does not count
+    as a kernel change."""
+    import re
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):

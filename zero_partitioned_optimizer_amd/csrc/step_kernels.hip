@@ -72,7 +72,7 @@ struct KParams {
     float* set_m[2];
     float* set_v[2];
     const zero_device_state* ctrl;          // device-commit path: committed t, scale, set
-    zero_device_state* ctrl_rw;             // the same record, written by the last workgroup
+    zero_device_state* ctrl_rw;             // the same record, written by workgroup 0 (commit)
     zero_stats* stats;
     uint16_t* set_slot[2];                  // device-commit path with a double-buffered slot
     uint16_t* slot;
@@ -493,7 +493,8 @@ __device__ __forceinline__ void block_reduce(double& sq, uint32_t& bad, uint32_t
 // kernels
 // ---------------------------------------------------------------------------
 
-// The commit of a device-resident step (thread 0 of the last workgroup):
+// The commit of a device-resident step (thread 0 of workgroup 0, after it has
+// collected every partial):
 //   clean:    t += 1, beta^t *= beta, the written state set becomes current;
 //   overflow: skipped += 1, a dynamic loss scale halves (not below its floor).
 __device__ __forceinline__ void commit_record(zero_device_state* c, zero_stats* stats, double sq,
@@ -702,8 +703,8 @@ __global__ void __launch_bounds__(kBlock) k_cast_slot(const float* master, int64
 
 // After a device-resident step: if it overflowed, restore the slot from the
 // committed master (the current set, which a skipped step leaves current).
-// Every workgroup reads the verdict the step's last workgroup wrote and, on a
-// clean step, exits at once.
+// Every workgroup reads the verdict the step's commit wrote into the record and,
+// on a clean step, exits at once.
 __global__ void __launch_bounds__(kBlock) k_restore(const zero_device_state* ctrl,
                                                    const float* set_p0, const float* set_p1,
                                                    uint16_t* slot, int64_t S) {
@@ -725,9 +726,10 @@ __global__ void k_state_write(zero_device_state* s, zero_device_state rec, uint6
 // launchers
 // ---------------------------------------------------------------------------
 
-// Quads per lane per trip: two rows keep more bytes in flight when few replica
-// streams are open; with many replicas one row keeps the register budget (and so
-// the occupancy) up.
+// Quads per lane per trip: one row (one quad per lane per trip) by default; a
+// build with ZERO_ROWS_FEW=2 gives launches with up to 16 replicas two rows,
+// more bytes in flight per lane at a higher register count (one row measured
+// faster with one trip per workgroup).
 #ifndef ZERO_ROWS_FEW
 #define ZERO_ROWS_FEW 1
 #endif
