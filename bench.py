@@ -11,8 +11,9 @@ and resident in HBM before the timed region starts.
 
 Prints one JSON line. ``roofline`` is for the dominant kernel (the fused step
 kernel): algorithmic bytes per launch, S * (N * 2 + 26), over its mean duration
-measured with HIP events recorded around that kernel on its own stream (on every
-tenth timed step by default: an event pair costs the stream more than 10 us).
+measured with HIP events that the kernel's own launch carries on its stream
+(hipExtLaunchKernel: they take the kernel's start and end), on every tenth timed
+step by default (timed launches cost the stream a few microseconds each).
 ``cpu_baseline`` is the CPU oracle timed on this host on the same shard.
 """
 from __future__ import annotations
@@ -329,8 +330,8 @@ def main() -> int:
                     help="device commit with one slot buffer (restore kernel after an overflow) "
                          "instead of a double-buffered slot")
     ap.add_argument("--event-every", type=int, default=10,
-                    help="record HIP events around the step kernel of every k-th timed step "
-                         "(an event pair costs the stream more than 10 us)")
+                    help="time the step kernel of every k-th timed step with HIP events its "
+                         "launch carries (a timed launch costs the stream a few us)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain device copy of 1 GiB three times "
                          "(the known-size reference for HBM byte counters under rocprofv3)")

@@ -236,8 +236,9 @@ typedef struct {
     zero_stats* stats_dev;
     void* workspace_dev;
     size_t ws_bytes;
-    /* optional hipEvent_t handles (NULL: none), recorded on `stream` right before
-       and right after the main step kernel, to time it apart from the finalize */
+    /* optional hipEvent_t handles (NULL: none), created by the caller: the main
+       step kernel's launch carries them (hipExtLaunchKernel), so they take that
+       kernel's own start and end time on `stream`, apart from the finalize */
     void* event_begin;
     void* event_end;
 } zero_adam_args;
@@ -377,8 +378,8 @@ typedef struct {
     zero_stats* stats_dev;
     void* workspace_dev;
     size_t ws_bytes;
-    void* event_begin;             /* optional hipEvent_t around the main kernel */
-    void* event_end;
+    void* event_begin;             /* optional hipEvent_t handles: the start and end */
+    void* event_end;               /* time of the step kernel itself, as above */
 } zero_train_args;
 
 /*

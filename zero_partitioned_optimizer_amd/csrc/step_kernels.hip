@@ -31,6 +31,7 @@
 //  - loads of data read once use the nontemporal hint, and so do the stores.
 // Arithmetic is one IEEE fp32 operation per source operation, built with
 // -ffp-contract=off; division and sqrt are the correctly rounded forms.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -763,16 +764,29 @@ static int grid_stream(int64_t S) {
     return (int)g;
 }
 
+// One launch of the step kernel. With timing events the launch carries them
+// (hipExtLaunchKernelGGL), so they take the kernel's own start and end and their
+// interval is the kernel alone, not the stream's gaps around it.
+template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL, int ROWS>
+static void launch_one(const StepDesc& d, const KParams& k, int grid, hipStream_t st) {
+    if (d.ev_begin || d.ev_end)
+        hipExtLaunchKernelGGL((k_step<RT, BUCKETS, ADAM, WRITE_G, CTRL, ROWS>), dim3(grid),
+                              dim3(kBlock), 0, st, d.ev_begin, d.ev_end, 0, k);
+    else
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, ADAM, WRITE_G, CTRL, ROWS>), dim3(grid), dim3(kBlock),
+                           0, st, k);
+}
+
 template <typename RT, bool BUCKETS, int ROWS>
 static void launch_rows(const StepDesc& d, const KParams& k, int grid, hipStream_t st) {
     if (d.ctrl)
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, true, false, true, ROWS>), dim3(grid), dim3(kBlock), 0, st, k);
+        launch_one<RT, BUCKETS, true, false, true, ROWS>(d, k, grid, st);
     else if (d.adam)
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, true, false, false, ROWS>), dim3(grid), dim3(kBlock), 0, st, k);
+        launch_one<RT, BUCKETS, true, false, false, ROWS>(d, k, grid, st);
     else if (d.g_out)
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, true, false, ROWS>), dim3(grid), dim3(kBlock), 0, st, k);
+        launch_one<RT, BUCKETS, false, true, false, ROWS>(d, k, grid, st);
     else
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, false, false, false, ROWS>), dim3(grid), dim3(kBlock), 0, st, k);
+        launch_one<RT, BUCKETS, false, false, false, ROWS>(d, k, grid, st);
 }
 
 template <typename RT, bool BUCKETS>
@@ -815,10 +829,6 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     const int grid = grid_for(d.S, d.n_buckets, d.n_rep, d.max_grid);
     k.part_base = d.part_base;
     k.collect_n = d.collect_n == 0 ? grid : (d.collect_n > 0 ? d.collect_n : 0);
-    if (d.ev_begin) {
-        hipError_t e = hipEventRecord(d.ev_begin, st);
-        if (e != hipSuccess) return e;
-    }
     if (d.dtype == ZERO_BF16) {
         if (buckets) launch_typed<uint16_t, true>(d, k, grid, st);
         else launch_typed<uint16_t, false>(d, k, grid, st);
@@ -831,10 +841,6 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (d.ev_end) {
-        e = hipEventRecord(d.ev_end, st);
-        if (e != hipSuccess) return e;
-    }
     if (d.ctrl) {
         if (d.slot && !d.set_slot[1] && !d.no_restore)
             return launch_restore(d.ctrl, d.set_p[0], d.set_p[1], d.slot, d.S, st);
