@@ -313,6 +313,69 @@ def gather_bench(args, Z, W, w, S) -> int:
     return 0
 
 
+def graph_bench(args, w, S, step, reps) -> int:
+    """G device-commit steps captured in one HIP graph, replayed back to back: the
+    step rate with no host work per step. Every step reads the committed-state
+    record, so a replayed step is the next step. HIP events on the replay stream
+    bracket every replay."""
+    import torch
+    G = args.graph
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        step._args_for(reps)               # the argument block exists before the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(G):
+                step.step(reps)
+    torch.cuda.synchronize()
+    t_before = int(step.state().t)
+    for _ in range(2):
+        graph.replay()
+    R = max(1, args.steps // G)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(R)]
+    for e0, e1 in ev:
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record()
+        graph.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = step.state()
+    steps_run = int(st.t) + int(st.n_skipped) - t_before
+    K = R * G
+    assert steps_run == K + 2 * G, (steps_run, K)
+    per_step = [a.elapsed_time(b) / 1e3 / G for a, b in ev]
+    kernel_s = statistics.mean(per_step)
+    bpe = w.N * w.grad_bytes + 26
+    achieved = S * bpe / kernel_s / 1e9
+    log(f"graph of {G} steps, {R} replays: {elapsed / K * 1e6:.2f} us per step (wall), "
+        f"{kernel_s * 1e6:.2f} us per step (replay events)")
+    out = {
+        "metric": METRIC, "value": S * K / elapsed, "unit": "elements/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": elapsed / K * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} shard, rank {args.rank} of N={w.N}", "shard_elems": S,
+                   "n_replicas": w.N, "grad_dtype": w.grad_dtype, "bytes_per_elem": bpe,
+                   "commit": "device", "graph_steps": G},
+        "step_us_replay_events": kernel_s * 1e6,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "note": "per step of a replayed graph (kernels plus the gaps between them)"},
+        "cpu_baseline": None,
+        "skipped_steps": int(st.n_skipped),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,9 +424,16 @@ def main() -> int:
                     help="write a 1 GiB buffer before every timed step so no step finds its data "
                          "in the 256 MB Infinity Cache; `value` then comes from the step kernels' "
                          "own event times (every step timed), not the wall clock")
+    ap.add_argument("--graph", type=int, default=0, metavar="G",
+                    help="device commit: capture G consecutive steps in one HIP graph and time "
+                         "its replays (no host work per step; for launch-bound shards)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    if args.graph and (args.commit != "device" or args.flush_mall or args.overlap or args.offload
+                       or args.gather):
+        print("--graph times device-commit steps alone", file=sys.stderr)
+        return 2
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -429,6 +499,8 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step.step(reps)
+    if args.graph:
+        return graph_bench(args, w, S, step, reps)
     K = args.steps
     every = 1 if args.flush_mall else max(1, args.event_every)
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush_mall else None

@@ -97,7 +97,7 @@ class ShardStep:
 
     def launch(self, replicas: Sequence[torch.Tensor], stream=None, events=None) -> None:
         """Enqueue the fused step (no synchronization). ``events`` = optional pair of
-        torch.cuda.Event recorded around the main kernel."""
+        torch.cuda.Event that the main kernel's launch carries (its start and end)."""
         a = self._args_for(replicas)
         if events is not None:
             a.event_begin = B._event(events[0])
@@ -148,9 +148,10 @@ class ShardStep:
 
 class DeviceShardStep:
     """The same step with the commit on the device (``zero_train_step``): the fused
-    kernel reads the committed-state record, and a commit kernel applies the skip
-    rule to it, so steps queue back to back with no host synchronization. The host
-    reads the record (t, loss scale, current set) only when it wants to."""
+    kernel reads the committed-state record, and its workgroup 0 folds every
+    workgroup's partial and applies the skip rule to the record, so steps queue
+    back to back with no host synchronization. The host reads the record (t, loss
+    scale, current set) only when it wants to."""
 
     def __init__(self, shard_S: int, n_replicas: int, grad_dtype: int, p0: torch.Tensor, *,
                  lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
