@@ -31,5 +31,11 @@ def test_help_lists_the_modes():
     r = run("--help")
     assert r.returncode == 0
     for flag in ("--config", "--commit", "--hbm-probe", "--fold", "--overlap", "--offload",
-                 "--gather", "--flush-mall", "--cpu-seconds", "--calibrate-copy"):
+                 "--gather", "--flush-mall", "--cpu-seconds", "--calibrate-copy", "--graph"):
         assert flag in r.stdout
+
+
+def test_graph_mode_needs_the_device_commit():
+    r = run("--graph", "4", "--commit", "host")
+    assert r.returncode == 2
+    assert "--graph" in r.stderr
