@@ -76,3 +76,24 @@ def test_guard_bands_and_empty(Z):
         assert g.intact(), t
         assert_bitexact(f"guarded {t}", to_host(g.t), oracle.gather_tensor(shards_h, int(lay.offsets[t]), numels[t]))
     assert Z.zero_gather_tensors(shards, lay.S, [], []) == []
+
+
+@pytest.mark.slow
+def test_tensor_beyond_one_launch(Z):
+    """One bf16 tensor of 2^33 + 12,345 elements (17 GB) over two shards: its
+    8192-element tasks outnumber one launch's 2^20 workgroups, so the copy takes
+    two launches over consecutive task ranges. The output must equal the two
+    shard slices, compared on the device (the oracle's gather is that same
+    concatenation; at this size it is checked as a property)."""
+    n = (1 << 33) + 12_345
+    S = (n + 1) // 2 + 8
+    say(f"gather one tensor of {n} elements over 2 shards of {S}")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    shards = [torch.randint(-32768, 32767, (S,), dtype=torch.int16, device="cuda", generator=g)
+              for _ in range(2)]
+    out = Z.zero_gather_tensors(shards, S, [5], [n])[0]
+    torch.cuda.synchronize()
+    assert torch.equal(out[: S - 5], shards[0][5:])
+    assert torch.equal(out[S - 5:], shards[1][: n - (S - 5)])
+    del out, shards
+    torch.cuda.empty_cache()

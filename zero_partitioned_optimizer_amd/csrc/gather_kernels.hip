@@ -103,10 +103,10 @@ hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S,
             g.first_task[i + 1] = g.first_task[i] + (g.numel[i] + kGatherChunk - 1) / kGatherChunk;
         }
         const int64_t tasks = g.first_task[k];
-        // at most kGridMax workgroups per launch; a group with more tasks takes
-        // several launches over consecutive task ranges
-        for (int64_t t0 = 0; t0 < tasks; t0 += kGridMax) {
-            const int64_t n = tasks - t0 < kGridMax ? tasks - t0 : kGridMax;
+        // at most kGatherMaxTasks workgroups (8G elements) per launch; a group
+        // with more tasks takes several launches over consecutive task ranges
+        for (int64_t t0 = 0; t0 < tasks; t0 += kGatherMaxTasks) {
+            const int64_t n = tasks - t0 < kGatherMaxTasks ? tasks - t0 : kGatherMaxTasks;
             g.task_base = t0;
             if (elem_bytes == 2)
                 hipLaunchKernelGGL(k_gather<uint16_t>, dim3((unsigned)n), dim3(kBlock), 0, st, g);
