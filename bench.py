@@ -377,6 +377,91 @@ def graph_bench(args, w, S, step, reps) -> int:
     return 0
 
 
+def unfused_bench(args, Z, w, S, reps, p0, gdt) -> int:
+    """The unfused step: the reduce kernel writes the fp32 gradient (fold, average,
+    unscale, flag, norm), the host reads the 16-byte stats and applies the commit
+    rule, and on a clean step the Adam kernel updates p, m, v in place from that
+    gradient and writes the slot. 8 more bytes per element than the fused step
+    (the gradient written and read back) and a host round trip inside every
+    step. HIP events bracket each of the two kernels' calls on the stream."""
+    import torch
+    dev = p0.device
+    g = torch.empty(S, dtype=torch.float32, device=dev)
+    stats = torch.zeros(16, dtype=torch.uint8, device=dev)
+    stats_host = torch.zeros(16, dtype=torch.uint8, pin_memory=True)
+    ws = torch.empty(Z.zero_workspace_bytes(S), dtype=torch.uint8, device=dev)
+    p = p0.clone()
+    m = torch.zeros_like(p0)
+    v = torch.zeros_like(p0)
+    slot = torch.empty(S, dtype=torch.int16, device=dev)
+    state = Z.zero_train_state(t=0, n_skipped=0, loss_scale=w.loss_scale, min_loss_scale=1.0,
+                               dynamic=int(w.dynamic_loss_scale))
+    hy = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.wd)
+    stream = torch.cuda.current_stream()
+
+    def one(evs=None):
+        if evs:
+            evs[0].record()
+        Z.zero_reduce_shard(reps, gdt, S, stats, ws, loss_scale=state.loss_scale, grad_out=g)
+        if evs:
+            evs[1].record()
+        stats_host.copy_(stats, non_blocking=True)
+        stream.synchronize()
+        st = Z.zero_stats.from_buffer_copy(stats_host.numpy().tobytes())
+        if Z.zero_commit_rule(state, st) != Z.ZERO_COMMIT:
+            return 1
+        a = Z.make_adam_args(grad_f32=g, p_in=p, m_in=m, v_in=v, p_out=p, m_out=m, v_out=v,
+                             slot=slot, shard_S=S, step_t=int(state.t), stats=stats, workspace=ws,
+                             event_begin=evs[2] if evs else None, event_end=evs[3] if evs else None,
+                             **hy)
+        Z.zero_adam_step(a)
+        return 0
+
+    for _ in range(args.warmup):
+        one()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for e in evs:
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    skips = []
+    t0 = time.perf_counter()
+    for k in range(K):
+        skips.append(one(evs[k]))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    skipped = sum(skips)
+    clean = [e for e, sk in zip(evs, skips) if not sk]
+    assert clean, "every timed step overflowed"
+    t_red = statistics.mean(e[0].elapsed_time(e[1]) for e in evs) / 1e3
+    t_adam = statistics.mean(e[2].elapsed_time(e[3]) for e in clean) / 1e3
+    red_b = S * (w.N * w.grad_bytes + 4)
+    adam_b = S * 30
+    bpe = w.N * w.grad_bytes + 34
+    achieved = S * bpe / (t_red + t_adam) / 1e9
+    log(f"unfused: reduce {t_red * 1e6:.1f} us ({red_b / t_red / 1e9:.0f} GB/s), adam "
+        f"{t_adam * 1e6:.1f} us ({adam_b / t_adam / 1e9:.0f} GB/s), {elapsed / K * 1e6:.1f} us "
+        f"per step (wall)")
+    out = {
+        "metric": METRIC, "value": S * K / elapsed, "unit": "elements/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": elapsed / K * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name} shard, rank {args.rank} of N={w.N}", "shard_elems": S,
+                   "n_replicas": w.N, "grad_dtype": w.grad_dtype, "bytes_per_elem": bpe,
+                   "commit": "host", "path": "unfused"},
+        "reduce_kernel": {"us": t_red * 1e6, "bytes": red_b, "gbps": red_b / t_red / 1e9},
+        "adam_kernel": {"us": t_adam * 1e6, "bytes": adam_b, "gbps": adam_b / t_adam / 1e9},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "note": "S * (2N + 34) bytes over the two kernels' times"},
+        "cpu_baseline": None,
+        "skipped_steps": skipped,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -425,6 +510,9 @@ def main() -> int:
                     help="write a 1 GiB buffer before every timed step so no step finds its data "
                          "in the 256 MB Infinity Cache; `value` then comes from the step kernels' "
                          "own event times (every step timed), not the wall clock")
+    ap.add_argument("--unfused", action="store_true",
+                    help="instead of the default line: time the unfused step (reduce kernel to "
+                         "an fp32 gradient, host commit rule, Adam kernel from the gradient)")
     ap.add_argument("--graph", type=int, default=0, metavar="G",
                     help="device commit: capture G consecutive steps in one HIP graph and time "
                          "its replays (no host work per step; for launch-bound shards)")
@@ -496,6 +584,11 @@ def main() -> int:
         return overlap_bench(args, Z, w, S, reps, p0, kw, gdt)
     if args.offload:
         return offload_bench(args, Z, w, S, reps, p0, gdt)
+    if args.unfused:
+        if nb:
+            print("--unfused runs the whole shard (no bucket table)", file=sys.stderr)
+            return 2
+        return unfused_bench(args, Z, w, S, reps, p0, gdt)
     log("inputs resident; warmup", args.warmup)
 
     for _ in range(args.warmup):

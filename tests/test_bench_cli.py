@@ -31,7 +31,8 @@ def test_help_lists_the_modes():
     r = run("--help")
     assert r.returncode == 0
     for flag in ("--config", "--commit", "--hbm-probe", "--fold", "--overlap", "--offload",
-                 "--gather", "--flush-mall", "--cpu-seconds", "--calibrate-copy", "--graph"):
+                 "--gather", "--flush-mall", "--cpu-seconds", "--calibrate-copy", "--graph",
+                 "--unfused"):
         assert flag in r.stdout
 
 
