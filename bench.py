@@ -470,6 +470,9 @@ def main() -> int:
     ap.add_argument("--config", default="gpt2s",
                     choices=["tiny", "gpt2s", "llama7b", "ragged", "llama70b"])
     ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=None,
+                    help="base seed of the synthetic replicas and parameters (default: the "
+                         "workload's own)")
     ap.add_argument("--bucket-elems", type=int, default=0,
                     help="launch over the layout's bucket table cut at this size (0: whole shard)")
     ap.add_argument("--commit", default="device", choices=["device", "host"],
@@ -542,6 +545,9 @@ def main() -> int:
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     w = W.get(args.config)
+    if args.seed is not None:
+        import dataclasses
+        w = dataclasses.replace(w, seed=int(args.seed))
     gdt = Z.ZERO_BF16 if w.grad_dtype == "bf16" else Z.ZERO_F32
     wire = args.fold == "bf16-wire"
     if wire:
@@ -651,7 +657,8 @@ def main() -> int:
                    "n_replicas": w.N, "grad_dtype": w.grad_dtype, "state_dtype": "f32",
                    "bytes_per_elem": bpe, "bucket_elems": args.bucket_elems,
                    "commit": args.commit, "fold": args.fold, "mall_flushed": bool(args.flush_mall),
-                   "slot": "single" if (args.single_slot or args.commit == "host") else "double"},
+                   "slot": "single" if (args.single_slot or args.commit == "host") else "double",
+                   "seed": w.seed},
         "step_gbps": S * bpe / (elapsed / K) / 1e9,
         "kernel_us_mean": kernel_s * 1e6,
         "kernel_us_median": statistics.median(kms) * 1e3,
