@@ -19,6 +19,8 @@
 
 namespace zk {
 
+constexpr int64_t kGatherMaxTasks = int64_t(1) << 20;   // workgroups per gather launch
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct GatherParams {

@@ -97,7 +97,6 @@ hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipS
 // workgroup task.
 constexpr int kGatherTensors = 32;
 constexpr int64_t kGatherChunk = 8192;
-constexpr int64_t kGatherMaxTasks = int64_t(1) << 20;   // workgroups per gather launch
 hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S, int32_t elem_bytes,
                          const int64_t* offsets, const int64_t* numels, void* const* outs,
                          int32_t n_tensors, hipStream_t stream);
