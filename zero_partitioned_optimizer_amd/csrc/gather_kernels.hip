@@ -9,7 +9,7 @@
 //
 // Pure copy, HBM-bound (2 x element bytes per element): workgroups take fixed
 // tasks of kGatherChunk output elements, so a launch has about one task per
-// 16 KB of output whatever the tensor sizes; pieces whose source and
+// 16 KB of bf16 output whatever the tensor sizes; pieces whose source and
 // destination share their 16-byte alignment move as 16-byte vectors, others
 // element by element (still coalesced).
 #include <hip/hip_runtime.h>
@@ -19,6 +19,8 @@
 
 namespace zk {
 
+constexpr int kGatherTensors = 32;                      // tensors per launch
+constexpr int64_t kGatherChunk = 8192;                  // output elements per task
 constexpr int64_t kGatherMaxTasks = int64_t(1) << 20;   // workgroups per gather launch
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

@@ -93,10 +93,7 @@ int rows_for(int32_t n_rep);
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid = 0);
 hipError_t launch_step(const StepDesc& d, hipStream_t stream);
 hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t stream);
-// Stage-3 fetch (gather_kernels.hip): tensors per launch and output elements per
-// workgroup task.
-constexpr int kGatherTensors = 32;
-constexpr int64_t kGatherChunk = 8192;
+// Stage-3 fetch (gather_kernels.hip).
 hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S, int32_t elem_bytes,
                          const int64_t* offsets, const int64_t* numels, void* const* outs,
                          int32_t n_tensors, hipStream_t stream);
