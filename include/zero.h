@@ -30,8 +30,10 @@
  *    happen before any launch; no C++ exception crosses the ABI. On a non-OK
  *    return, zero_last_error() gives a thread-local description.
  *  - Kernels are enqueued on `stream` (a hipStream_t passed as void*; NULL is
- *    the default stream). No entry point synchronizes. zero_layout_* and
- *    zero_commit_rule are host-only and synchronous.
+ *    the default stream). No entry point synchronizes, except the offloaded
+ *    step zero_offload_step, which waits for its own copies and host updates.
+ *    zero_layout_*, zero_commit_rule and zero_host_adam are host-only and
+ *    synchronous.
  *  - Device buffers must be 16-byte aligned (dwordx4 access).
  */
 #ifndef ZERO_SHARD_STEP_H
@@ -308,8 +310,9 @@ int zero_commit_rule(zero_train_state* state, const zero_stats* stats_host);
 /*
  * The committed-state record of one rank's shard, in device memory (88 bytes,
  * 16-byte aligned, caller-owned). zero_train_step reads it to pick the current
- * state set, t, the loss scale and beta^t, and its commit kernel updates it, so
- * consecutive steps need no host synchronization (and can be graph-captured).
+ * state set, t, the loss scale and beta^t, and the step's own commit (workgroup
+ * 0 of the step kernel, after every partial is in) updates it, so consecutive
+ * steps need no host synchronization (and can be graph-captured).
  * The host may copy it back at any time after synchronizing the stream.
  */
 typedef struct {
@@ -393,8 +396,9 @@ typedef struct {
  * committed, dynamic loss scale halved). The wait is bounded (2 s); should it run
  * out, which a correct launch never does, nothing is committed and the stats
  * read overflow = 1, bad_buckets = 0xFFFFFFFF. The workspace must be the one
- * given to zero_device_state_init. With a single slot the candidate bf16 values go straight into
- * it and a second kernel restores it from the current master after an overflow;
+ * given to zero_device_state_init. With a single slot the candidate bf16 values
+ * go straight into it and a second kernel restores it from the current master
+ * after an overflow;
  * with a double-buffered slot the candidate goes into slot[1 - cur] and the
  * commit flips it with the state sets, so a step is one kernel. Same arithmetic
  * as zero_adam_step, bit for bit.
@@ -425,8 +429,9 @@ int zero_train_step(const zero_train_args* args, void* stream);
  * and commits, as zero_train_step does; with a single slot the restore kernel
  * follows the last part. p, m, v and the slot come out bit-identical to
  * zero_train_step's; the squared norm is summed in another grouping (equal
- * within rounding). The workspace of zero_workspace_bytes(shard_S) suffices. args must carry no
- * bucket table (ZERO_E_UNSUPPORTED); parts cover padding like a whole-shard step.
+ * within rounding). The workspace of zero_workspace_bytes(shard_S) suffices.
+ * args must carry no bucket table (ZERO_E_UNSUPPORTED); parts cover padding like
+ * a whole-shard step.
  * Errors: as zero_train_step; ZERO_E_INVAL for a NULL part_ends; ZERO_E_RANGE for
  * n_parts outside [1, 4096], part outside [0, n_parts) or a bad boundary.
  */
@@ -479,7 +484,7 @@ int zero_gather_tensors(const void* const* shards, int32_t n_shards, int64_t sha
  * Adam/AdamW on the host, in place on p, m, v over n elements, optionally
  * writing bf16 (nearest even) into slot_bf16. Same operation sequence and fp32
  * scalars as zero_adam_step (step_t >= 1; beta^t as a t-fold product in double).
- * All pointers are host memory, non-overlapping except that nothing aliases.
+ * All pointers are host memory; the arrays must not overlap (not checked).
  * nthreads: worker threads (0: one per CPU in the calling process's affinity mask,
  * at most 256). Synchronous.
  * Errors: ZERO_E_INVAL (NULL pointer with n > 0, a parameter out of domain),
@@ -505,7 +510,8 @@ int zero_host_adam(const zero_host_adam_args* args);
  *  1. on `stream`: fold the replicas into g_dev (fp32 [shard_S], device),
  *     ×1/(N·loss_scale), overflow flag and squared norm into stats_dev
  *     (zero_reduce_shard); copy the 16-byte stats back and wait for them;
- *  2. overflow: nothing is touched, the commit rule skips (state->n_skipped += 1,
+ *  2. overflow: no state or slot buffer is touched, the commit rule skips
+ *     (state->n_skipped += 1,
  *     dynamic loss scale halved), return ZERO_SKIP;
  *  3. clean: g_dev is copied to g_host in chunks of chunk_elems elements, one
  *     event per chunk; as soon as a chunk has landed every host thread updates
