@@ -34,7 +34,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fused shard step: elements/s and achieved HBM GB/s (% of MI355X peak)"
 CPU_SAMPLE_ELEMS = 64 << 20
 KERNEL_SOURCES = [os.path.join(ROOT, "zero_partitioned_optimizer_amd", "csrc", f)
-                  for f in ("step_kernels.hip", "zero_internal.h")]
+                  for f in ("step_kernels.hip", "zero_internal.h")] + [
+                      os.path.join(ROOT, "include", "zero.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -43,9 +44,10 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """sha256[:16] of the step kernel's code: step_kernels.hip and zero_internal.h
-    with comments and whitespace removed, so that a comment edit does not count
-    as a kernel change."""
+    """sha256[:16] of the step kernel's code: step_kernels.hip, zero_internal.h
+    and include/zero.h (whose structs the kernel reads and writes) with comments
+    and whitespace removed, so that a comment edit does not count as a kernel
+    change."""
     import re
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
