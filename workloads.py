@@ -270,12 +270,35 @@ def device_fill_params(buf, w: Workload, covered, rank: int) -> None:
     _zero_outside(buf, covered)
 
 
+_MASKS: dict = {}
+
+
 def _zero_outside(buf, covered) -> None:
+    """Write +0 at every position of ``buf`` outside the ``covered`` runs. Few
+    gaps: one fill per gap. Many gaps (the ragged workload's padding between
+    aligned tensors): one masked fill with a device mask built once per layout,
+    instead of a launch per gap."""
+    import torch
     S = buf.numel()
+    gaps = []
     pos = 0
     for off, ln in sorted((int(o), int(n)) for o, n in covered):
         if off > pos:
-            buf[pos:off].zero_()
+            gaps.append((pos, off))
         pos = max(pos, off + ln)
     if pos < S:
-        buf[pos:S].zero_()
+        gaps.append((pos, S))
+    if len(gaps) <= 64 or S > (1 << 26):
+        for a, b in gaps:
+            buf[a:b].zero_()
+        return
+    key = (S, str(buf.device), tuple(gaps))
+    mask = _MASKS.get(key)
+    if mask is None:
+        host = np.zeros(S, dtype=bool)
+        for a, b in gaps:
+            host[a:b] = True
+        mask = torch.from_numpy(host).to(buf.device)
+        _MASKS.clear()
+        _MASKS[key] = mask
+    buf.masked_fill_(mask, 0)
