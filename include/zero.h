@@ -240,7 +240,8 @@ typedef struct {
     size_t ws_bytes;
     /* optional hipEvent_t handles (NULL: none), created by the caller: the main
        step kernel's launch carries them (hipExtLaunchKernel), so they take that
-       kernel's own start and end time on `stream`, apart from the finalize */
+       kernel's own start and end time on `stream`, apart from the finalize.
+       For eager launches; leave them NULL for a launch under stream capture */
     void* event_begin;
     void* event_end;
 } zero_adam_args;
