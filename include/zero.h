@@ -47,7 +47,7 @@ extern "C" {
 #endif
 
 #define ZERO_ABI_VERSION 1
-#define ZERO_MAX_REPLICAS 256
+#define ZERO_MAX_REPLICAS 1024
 
 typedef enum {
     ZERO_OK = 0,
@@ -184,9 +184,11 @@ typedef struct {
  * Bytes of device workspace a reduce, Adam or train-step call on a shard of
  * shard_S elements needs: 24 bytes of fp64 partials per workgroup, for one
  * workgroup per 1,024 elements plus one per part of a split step (at most
- * 4,096), capped at 4,194,304 workgroups (about 20 MB for a 842M-element shard).
- * The same workspace may be reused by consecutive calls on one stream; calls
- * that run concurrently need their own.
+ * 4,096), capped at 4,194,304 workgroups (about 20 MB for a 842M-element shard),
+ * plus 8 KB + 16 at the end for the device table of replica pointers that a call
+ * with more than 256 replicas uses (the first 256 pointers travel in the kernel
+ * arguments). The same workspace may be reused by consecutive calls on one
+ * stream; calls that run concurrently need their own.
  */
 size_t zero_workspace_bytes(int64_t shard_S);
 
@@ -200,7 +202,11 @@ size_t zero_workspace_bytes(int64_t shard_S);
  *   g   = acc * inv,  inv = fp32(1 / (N * loss_scale)) rounded once from double
  *   stats->overflow = any g non-finite; stats->sumsq = sum (double)g * g
  * replicas: host array of n_replicas device pointers (slot order), each shard_S
- *   elements of grad_dtype. n_replicas in [1, ZERO_MAX_REPLICAS].
+ *   elements of grad_dtype. n_replicas in [1, ZERO_MAX_REPLICAS]. Up to 256
+ *   pointers travel in the kernel arguments; beyond that the call first writes
+ *   all n_replicas pointers into the last 8 * n_replicas (+ up to 16) bytes of
+ *   the workspace with a small kernel on `stream`, and the step reads them
+ *   there (the workspace must then hold that table after its partials).
  * buckets_dev, n_buckets: device bucket table; only elements inside buckets are
  *   read and written (NULL, 0 = the whole shard). Buckets must not overlap;
  *   one that leaves [0, shard_S) is skipped and counted in stats->bad_buckets.

@@ -173,6 +173,57 @@ def test_replica_counts(Z, N):
     single_step_case(Z, 5003, N, "bf16", seed=1000 + N, loss_scale=65536.0, t=3, wd=0.0)
 
 
+@pytest.mark.parametrize("N", [257, 300, 511, 512, 1000, 1024])
+def test_replica_counts_beyond_argument_block(Z, N):
+    """More replicas than the kernel arguments carry: the pointers go through a
+    device table at the end of the workspace, written ahead of the step."""
+    say(f"fused bf16 S=5003 N={N} (pointer table)")
+    single_step_case(Z, 5003, N, "bf16", seed=2000 + N, loss_scale=65536.0, t=2, wd=0.01)
+
+
+@pytest.mark.parametrize("N,dtype,fused,wire", [(300, "f32", True, False), (300, "bf16", True, True),
+                                                (1024, "bf16", False, False),
+                                                (700, "bf16", False, True)])
+def test_pointer_table_other_paths(Z, N, dtype, fused, wire):
+    say(f"{dtype} N={N} fused={fused} wire={wire} (pointer table)")
+    single_step_case(Z, 4101, N, dtype, seed=3000 + N, scale=1e-2, fused=fused, wire=wire, t=3)
+
+
+@pytest.mark.parametrize("double_slot,parts", [(False, None), (True, [1000, 1000, 4096, 9001])])
+def test_device_commit_with_pointer_table(Z, double_slot, parts):
+    """Device-committed steps (one or two slots, whole or split into parts) with
+    N = 300 replicas, an overflow on the second step, against the oracle."""
+    S, N = 9001, 300
+    rng = np.random.default_rng(41)
+    p0 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    hy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    tr = oracle.Trainer(p0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
+                        oracle.f32_to_bf16(p0), loss_scale=256.0, dynamic=True, nthreads=NTHREADS,
+                        wd=0.01, **hy)
+    st = Z.DeviceShardStep(S, N, Z.ZERO_BF16, to_dev(p0), loss_scale=256.0, dynamic=True,
+                           double_slot=double_slot, weight_decay=0.01, **hy)
+    for k in range(3):
+        say(f"device commit N={N} step {k} double_slot={double_slot} parts={parts}")
+        reps = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * 1e-3 * 256.0))
+                for _ in range(N)]
+        if k == 1:
+            reps[N - 1][S // 2] = 0x7F80            # +inf in the last slot
+        flag, sumsq = tr.step(reps)
+        dreps = [to_dev(r) for r in reps]
+        if parts:
+            st.step_parts(dreps, parts)
+        else:
+            st.step(dreps)
+        rec = st.state()
+        assert rec.last_overflow == flag == (1 if k == 1 else 0)
+        assert rec.t == tr.t and rec.loss_scale == tr.loss_scale
+        if not flag:
+            assert sumsq_close(rec.last_sumsq, sumsq), (rec.last_sumsq, sumsq)
+        p, m, v = st.committed()
+        check_state(f"N={N} step {k}", to_host(p), to_host(m), to_host(v),
+                    to_host(st.current_slot()), tr.p, tr.m, tr.v, tr.slot)
+
+
 @pytest.mark.parametrize("N,S", [(1, 999), (2, 2024), (5, 4101)])
 def test_fp32_replicas(Z, N, S):
     say(f"fused f32 S={S} N={N}")
@@ -318,11 +369,14 @@ def test_slot_only_writes_and_guard_bands(Z):
     assert_bitexact("p_in", to_host(P_in.t), p)
 
 
-def test_bucket_table_random(Z):
+@pytest.mark.parametrize("N", [6, 300])
+def test_bucket_table_random(Z, N):
     """Random disjoint buckets at arbitrary (unaligned) offsets: elements inside are
     updated as the oracle says, elements outside keep their sentinel, a bucket
-    that leaves the shard is skipped and counted."""
-    S, N = 20_011, 6
+    that leaves the shard is skipped and counted (N = 300: replica pointers from
+    the workspace table)."""
+    S = 20_011
+    say(f"bucket table N={N}")
     rng = np.random.default_rng(12)
     reps = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * 1e-3)) for _ in range(N)]
     p = (rng.standard_normal(S) * 0.02).astype(np.float32)

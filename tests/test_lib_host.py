@@ -158,7 +158,7 @@ def base_args(Z, **kw):
     (dict(grad_f32=FAKE + 40960, step_t=0), -1),
     (dict(grad_f32=FAKE + 40960, eps=float("nan")), -1),
     (dict(grad_f32=FAKE + 40960, shard_S=-1), -3),
-    (dict(replicas=[FAKE + 45056] * 300), -3),                  # too many replicas
+    (dict(replicas=[FAKE + 45056] * 1025), -3),                 # too many replicas
     (dict(replicas=[FAKE + 45056], loss_scale=0.0), -1),
     (dict(replicas=[FAKE + 45056], p_out=FAKE), -1),            # fused must be out of place
     (dict(grad_f32=FAKE + 40960, p_out=FAKE + 100), -2),        # misaligned output
@@ -181,6 +181,20 @@ def test_adam_step_small_workspace_rejected(Z):
     with pytest.raises(Z.ZeroError) as e:
         Z.zero_adam_step(a, stream=0)
     assert e.value.status == -3
+
+
+def test_workspace_holds_the_pointer_table(Z):
+    # more than 256 replicas: the workspace must also hold their device pointer
+    # table (8 bytes each, at its end); enough room for the partials alone is not
+    S = 64                                 # one workgroup: 24 bytes of partials
+    table = [FAKE + (1 << 20) + 256 * j for j in range(300)]
+    for ws in (24, 24 + 8 * 300):          # partials only; no room for the alignment slack
+        a = base_args(Z, replicas=table, loss_scale=1.0)
+        a.ws_bytes = ws
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_adam_step(a, stream=0)
+        assert e.value.status == -3 and "workspace" in Z.zero_last_error()
+    assert Z.zero_workspace_bytes(S) >= (4096 + 1) * 24 + 8 * 1024 + 16
 
 
 def test_reduce_and_gather_validation(Z):

@@ -23,7 +23,7 @@ ZERO_OK, ZERO_E_INVAL, ZERO_E_ALIGN, ZERO_E_RANGE, ZERO_E_NOMEM, ZERO_E_HIP, ZER
     0, -1, -2, -3, -4, -5, -6
 ZERO_F32, ZERO_BF16, ZERO_BF16_WIRE = 0, 1, 2
 ZERO_COMMIT, ZERO_SKIP = 1, 2
-ZERO_MAX_REPLICAS = 256
+ZERO_MAX_REPLICAS = 1024
 
 _STATUS = {0: "ZERO_OK", -1: "ZERO_E_INVAL", -2: "ZERO_E_ALIGN", -3: "ZERO_E_RANGE",
            -4: "ZERO_E_NOMEM", -5: "ZERO_E_HIP", -6: "ZERO_E_UNSUPPORTED"}

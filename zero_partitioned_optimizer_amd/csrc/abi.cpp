@@ -147,7 +147,8 @@ int check_common(const char* fn, int64_t S, const zero_bucket* buckets, int64_t 
         set_error("%s: stats_dev or workspace_dev is not 16-byte aligned", fn);
         return ZERO_E_ALIGN;
     }
-    const size_t need = (size_t)zk::grid_for(S, n_buckets, n_rep) * zk::kPartialBytes;
+    const size_t need = (size_t)zk::grid_for(S, n_buckets, n_rep) * zk::kPartialBytes +
+                        zk::rep_table_bytes(n_rep);
     if (ws_bytes < need) {
         set_error("%s: workspace of %zu bytes < %zu needed", fn, ws_bytes, need);
         return ZERO_E_RANGE;
@@ -184,7 +185,8 @@ const char* zero_last_error(void) { return zl::g_err.c_str(); }
 const char* zero_version(void) { return "libzero 1.0 (gfx950)"; }
 
 size_t zero_workspace_bytes(int64_t shard_S) {
-    return (size_t)zk::grid_bound(shard_S) * zk::kPartialBytes;
+    return (size_t)zk::grid_bound(shard_S) * zk::kPartialBytes +
+           zk::rep_table_bytes(ZERO_MAX_REPLICAS);
 }
 
 int zero_reduce_shard(const void* const* replicas, int32_t n_replicas, zero_dtype grad_dtype,
@@ -231,6 +233,7 @@ int zero_reduce_shard(const void* const* replicas, int32_t n_replicas, zero_dtyp
     zk::StepDesc d{};
     d.replicas = replicas;
     d.n_rep = n_replicas;
+    d.rep_table = zk::rep_table_at(workspace_dev, ws_bytes, n_replicas);
     d.dtype = grad_dtype;
     d.S = shard_S;
     d.buckets = n_buckets > 0 ? buckets_dev : nullptr;
@@ -336,6 +339,7 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
     zk::StepDesc d{};
     d.replicas = fused ? a.replicas : one_rep;
     d.n_rep = fused ? a.n_replicas : 1;
+    d.rep_table = zk::rep_table_at(a.workspace_dev, a.ws_bytes, d.n_rep);
     d.dtype = fused ? a.grad_dtype : ZERO_F32;
     d.S = S;
     d.buckets = a.n_buckets > 0 ? a.buckets_dev : nullptr;
@@ -519,6 +523,7 @@ static zk::StepDesc train_desc(const zero_train_args& a) {
     zk::StepDesc d{};
     d.replicas = a.replicas;
     d.n_rep = a.n_replicas;
+    d.rep_table = zk::rep_table_at(a.workspace_dev, a.ws_bytes, a.n_replicas);
     d.dtype = a.grad_dtype;
     d.S = a.shard_S;
     d.buckets = a.n_buckets > 0 ? a.buckets_dev : nullptr;
@@ -592,9 +597,10 @@ int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, 
         total += g;
         prev = e;
     }
-    if (total * (int64_t)zk::kPartialBytes > (int64_t)a.ws_bytes || total > INT32_MAX) {
+    const int64_t need = total * (int64_t)zk::kPartialBytes + (int64_t)zk::rep_table_bytes(a.n_replicas);
+    if (need > (int64_t)a.ws_bytes || total > INT32_MAX) {
         set_error("%s: the %d parts need %lld workspace bytes, ws_bytes=%zu", fn, (int)n_parts,
-                  (long long)(total * (int64_t)zk::kPartialBytes), a.ws_bytes);
+                  (long long)need, a.ws_bytes);
         return ZERO_E_RANGE;
     }
     const int64_t lo = part == 0 ? 0 : part_ends[part - 1], hi = part_ends[part];
@@ -636,7 +642,7 @@ int zero_gather_tensors(const void* const* shards, int32_t n_shards, int64_t sha
         set_error("%s: shards, offsets, numels or outs is NULL", fn);
         return ZERO_E_INVAL;
     }
-    if (n_shards < 1 || n_shards > ZERO_MAX_REPLICAS || shard_S < 1 ||
+    if (n_shards < 1 || n_shards > zk::kGatherMaxShards || shard_S < 1 ||
         shard_S > (int64_t(1) << 40)) {
         set_error("%s: n_shards=%d shard_S=%lld out of range", fn, (int)n_shards,
                   (long long)shard_S);

@@ -26,7 +26,7 @@ constexpr int64_t kGatherMaxTasks = int64_t(1) << 20;   // workgroups per gather
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct GatherParams {
-    const void* shard[ZERO_MAX_REPLICAS];
+    const void* shard[kGatherMaxShards];
     int64_t S;
     int32_t n_tensors;
     int32_t reserved;
@@ -94,7 +94,7 @@ hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S,
                          const int64_t* offsets, const int64_t* numels, void* const* outs,
                          int32_t n_tensors, hipStream_t st) {
     GatherParams g{};
-    for (int r = 0; r < ZERO_MAX_REPLICAS; ++r) g.shard[r] = r < n_shards ? shards[r] : nullptr;
+    for (int r = 0; r < kGatherMaxShards; ++r) g.shard[r] = r < n_shards ? shards[r] : nullptr;
     g.S = S;
     for (int32_t base = 0; base < n_tensors; base += kGatherTensors) {
         const int32_t k = n_tensors - base < kGatherTensors ? n_tensors - base : kGatherTensors;

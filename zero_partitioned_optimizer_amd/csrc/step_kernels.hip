@@ -55,7 +55,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct KParams {
-    const void* rep[ZERO_MAX_REPLICAS];
+    const void* rep[kArgReplicas];          // replica pointers, slot order (up to kArgReplicas)
+    const void* const* rep_ext;             // device table of all n_rep pointers (n_rep > kArgReplicas)
     int32_t n_rep;
     int32_t part_base;                      // device commit: partial slot of workgroup 0
     int32_t collect_n;                      // device commit: slots workgroup 0 collects (0: none)
@@ -191,6 +192,25 @@ struct Quad<float> {
     }
 };
 
+// Where a launch finds replica pointer j: in its kernel arguments (up to
+// kArgReplicas replicas), or, for a replica type wrapped in Ext, in a device table
+// (more replicas than the argument block holds). Ext<T> folds exactly as T.
+template <typename T>
+struct Ext {};
+
+template <typename T>
+struct Quad<Ext<T>> : Quad<T> {};
+
+template <typename RT>
+struct Reps {
+    static __device__ __forceinline__ const void* at(const KParams& a, int j) { return a.rep[j]; }
+};
+
+template <typename T>
+struct Reps<Ext<T>> {
+    static __device__ __forceinline__ const void* at(const KParams& a, int j) { return a.rep_ext[j]; }
+};
+
 // ---------------------------------------------------------------------------
 // arithmetic
 // ---------------------------------------------------------------------------
@@ -221,7 +241,7 @@ __device__ __forceinline__ void fold_batch(const KParams& a, int j, int64_t q0, 
     typename Quad<RT>::V buf[K][ROWS];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const void* base = a.rep[j + k];
+        const void* base = Reps<RT>::at(a, j + k);
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) buf[k][r] = Quad<RT>::load(base, q0 + r * qs);
     }
@@ -240,7 +260,7 @@ __device__ __forceinline__ void fold_head(const KParams& a, int64_t q0, int64_t 
     typename Quad<RT>::V buf[K][ROWS];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        const void* base = a.rep[k];
+        const void* base = Reps<RT>::at(a, k);
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) buf[k][r] = Quad<RT>::load(base, q0 + r * qs);
     }
@@ -410,12 +430,12 @@ __device__ __forceinline__ void one_elem(const KParams& a, const Res& rs, int64_
     // repeats the batch's first slot and is dropped): a lane on a bucket edge
     // makes N / 8 memory round trips, not N
     const int n = a.n_rep;
-    float acc = Quad<RT>::one(a.rep[0], e);
+    float acc = Quad<RT>::one(Reps<RT>::at(a, 0), e);
     for (int j = 1; j < n; j += 8) {
         const int cnt = n - j < 8 ? n - j : 8;
         float x[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = Quad<RT>::one(a.rep[k < cnt ? j + k : j], e);
+        for (int k = 0; k < 8; ++k) x[k] = Quad<RT>::one(Reps<RT>::at(a, k < cnt ? j + k : j), e);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float s = Quad<RT>::add1(acc, x[k]);
@@ -797,9 +817,52 @@ static void launch_typed(const StepDesc& d, const KParams& k, int grid, hipStrea
     launch_rows<RT, BUCKETS, 1>(d, k, grid, st);
 }
 
+template <typename RT>
+static void launch_dtype(const StepDesc& d, const KParams& k, int grid, hipStream_t st, bool buckets,
+                         bool ext) {
+    if (ext) {
+        if (buckets) launch_typed<Ext<RT>, true>(d, k, grid, st);
+        else launch_typed<Ext<RT>, false>(d, k, grid, st);
+    } else {
+        if (buckets) launch_typed<RT, true>(d, k, grid, st);
+        else launch_typed<RT, false>(d, k, grid, st);
+    }
+}
+
+// Writes n replica pointers (from the kernel arguments) into a device table.
+struct PtrChunk {
+    const void* p[kArgReplicas];
+};
+
+__global__ void __launch_bounds__(kArgReplicas) k_put_ptrs(const void** dst, const PtrChunk c, int n) {
+    if ((int)threadIdx.x < n) dst[threadIdx.x] = c.p[threadIdx.x];
+}
+
+// More replicas than the kernel arguments hold: their pointers go into the
+// device table d.rep_table first, kArgReplicas per launch, on the same stream.
+static hipError_t put_replica_table(const StepDesc& d, hipStream_t st) {
+    for (int32_t j0 = 0; j0 < d.n_rep; j0 += kArgReplicas) {
+        const int n = d.n_rep - j0 < kArgReplicas ? d.n_rep - j0 : kArgReplicas;
+        PtrChunk c{};
+        for (int i = 0; i < n; ++i) c.p[i] = d.replicas[j0 + i];
+        hipLaunchKernelGGL(k_put_ptrs, dim3(1), dim3(kArgReplicas), 0, st,
+                           const_cast<const void**>(d.rep_table) + j0, c, n);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     KParams k;
-    for (int j = 0; j < ZERO_MAX_REPLICAS; ++j) k.rep[j] = j < d.n_rep ? d.replicas[j] : nullptr;
+    const bool ext = d.n_rep > kArgReplicas;
+    for (int j = 0; j < kArgReplicas; ++j) k.rep[j] = j < d.n_rep ? d.replicas[j] : nullptr;
+    k.rep_ext = ext ? d.rep_table : nullptr;
+    if (ext) {
+        if (!d.rep_table) return hipErrorInvalidValue;
+        const hipError_t e = put_replica_table(d, st);
+        if (e != hipSuccess) return e;
+    }
     k.n_rep = d.n_rep;
     k.reserved = 0;
     k.S = d.S;
@@ -830,14 +893,11 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     k.part_base = d.part_base;
     k.collect_n = d.collect_n == 0 ? grid : (d.collect_n > 0 ? d.collect_n : 0);
     if (d.dtype == ZERO_BF16) {
-        if (buckets) launch_typed<uint16_t, true>(d, k, grid, st);
-        else launch_typed<uint16_t, false>(d, k, grid, st);
+        launch_dtype<uint16_t>(d, k, grid, st, buckets, ext);
     } else if (d.dtype == ZERO_BF16_WIRE) {
-        if (buckets) launch_typed<WireBf16, true>(d, k, grid, st);
-        else launch_typed<WireBf16, false>(d, k, grid, st);
+        launch_dtype<WireBf16>(d, k, grid, st, buckets, ext);
     } else {
-        if (buckets) launch_typed<float, true>(d, k, grid, st);
-        else launch_typed<float, false>(d, k, grid, st);
+        launch_dtype<float>(d, k, grid, st, buckets, ext);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

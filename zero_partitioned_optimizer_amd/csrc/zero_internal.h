@@ -21,6 +21,19 @@ constexpr int kBlock = ZERO_BLOCK;  // threads per workgroup: 4 wave64s
 constexpr int kVec = 4;             // elements per lane per row (one quad)
 constexpr int kGridMax = ZERO_GRID_MAX;  // workgroups of the grid-stride step kernel
 constexpr int kMaxParts = 4096;          // parts of one step split over launches
+constexpr int kArgReplicas = 256;        // replica pointers carried in the kernel arguments
+
+// Bytes at the end of the workspace that a launch with n_rep replicas uses for
+// its device table of replica pointers (only beyond kArgReplicas replicas; 16
+// bytes of slack for alignment), and where that table starts.
+inline size_t rep_table_bytes(int32_t n_rep) {
+    return n_rep > kArgReplicas ? 8 * (size_t)n_rep + 16 : 0;
+}
+inline const void** rep_table_at(void* ws, size_t ws_bytes, int32_t n_rep) {
+    if (n_rep <= kArgReplicas) return nullptr;
+    const uintptr_t end = reinterpret_cast<uintptr_t>(ws) + ws_bytes;
+    return reinterpret_cast<const void**>((end - 8 * (uintptr_t)n_rep) & ~uintptr_t(15));
+}
 
 // Upper bound on the workgroups of any step launch over a shard of S elements
 // (one trip of kBlock * kVec elements each, plus one per part of a split step),
@@ -57,6 +70,7 @@ struct Scalars {
 struct StepDesc {
     const void* const* replicas;    // host array of n_rep device pointers
     int32_t n_rep;
+    const void** rep_table;         // workspace table for n_rep > kArgReplicas, else nullptr
     zero_dtype dtype;
     int64_t S;
     const zero_bucket* buckets;     // device, or nullptr for the whole shard
@@ -93,7 +107,8 @@ int rows_for(int32_t n_rep);
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid = 0);
 hipError_t launch_step(const StepDesc& d, hipStream_t stream);
 hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t stream);
-// Stage-3 fetch (gather_kernels.hip).
+// Stage-3 fetch (gather_kernels.hip), over at most kGatherMaxShards shards.
+constexpr int kGatherMaxShards = 256;
 hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S, int32_t elem_bytes,
                          const int64_t* offsets, const int64_t* numels, void* const* outs,
                          int32_t n_tensors, hipStream_t stream);
