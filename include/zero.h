@@ -73,6 +73,26 @@ typedef enum {
  */
 typedef enum { ZERO_F32 = 0, ZERO_BF16 = 1, ZERO_BF16_WIRE = 2 } zero_dtype;
 
+/*
+ * How the fp32 state of a shard (master p, Adam moments m and v; "ZeRO
+ * Optimizer", "Memory Components") sits in device memory. The pages fix no
+ * layout; the step reads and writes all three together, element by element.
+ *   ZERO_STATE_SPLIT  three arrays p, m, v of shard_S floats each.
+ *   ZERO_STATE_TILED  one buffer per state set of
+ *                     zero_state_set_floats(shard_S, ZERO_STATE_TILED) floats:
+ *                     tiles of ZERO_STATE_TILE elements, tile k holding p, then
+ *                     m, then v of shard elements [k*T, (k+1)*T) (T =
+ *                     ZERO_STATE_TILE), i.e. element e of p, m, v at floats
+ *                     (e / T)*3T + e % T + {0, T, 2T}. Elements of the last tile
+ *                     at or beyond shard_S are never read or written. A step then
+ *                     streams one state buffer in and one out instead of three
+ *                     and three, which HBM serves faster on this GPU.
+ * Entry points taking a state_layout field read m and v from the p buffers
+ * when it is ZERO_STATE_TILED, and then require the m and v pointers to be NULL.
+ */
+#define ZERO_STATE_TILE 8192
+typedef enum { ZERO_STATE_SPLIT = 0, ZERO_STATE_TILED = 1 } zero_state_layout;
+
 /* ------------------------------------------------------------------------ */
 /* Flat layout and shard cut (host only)                                      */
 /* ------------------------------------------------------------------------ */
@@ -250,6 +270,9 @@ typedef struct {
        For eager launches; leave them NULL for a launch under stream capture */
     void* event_begin;
     void* event_end;
+    /* zero_state_layout of p_in/m_in/v_in and p_out/m_out/v_out (0: split). Tiled:
+       p_in and p_out are set buffers, m and v pointers NULL */
+    int32_t state_layout;
 } zero_adam_args;
 
 /*
@@ -286,6 +309,35 @@ int zero_adam_step(const zero_adam_args* args, void* stream);
  */
 int zero_gather_slot(const float* master_dev, int64_t shard_S, uint16_t* slot_bf16_dev,
                      void* stream);
+
+/*
+ * zero_gather_slot with the master read from a tiled state set (the p sections
+ * of set_dev, ZERO_STATE_TILED). Same errors.
+ */
+int zero_gather_slot_tiled(const float* set_dev, int64_t shard_S, uint16_t* slot_bf16_dev,
+                           void* stream);
+
+/*
+ * Floats of one state set for a shard of shard_S elements: 3 * shard_S for
+ * ZERO_STATE_SPLIT (three arrays), 3 * shard_S rounded up to a multiple of
+ * 3 * ZERO_STATE_TILE for ZERO_STATE_TILED (one buffer). -1 for a negative
+ * shard_S or an unknown layout.
+ */
+int64_t zero_state_set_floats(int64_t shard_S, int32_t state_layout);
+
+/*
+ * Conversion between the split arrays p, m, v [shard_S] and one tiled set buffer
+ * (zero_state_set_floats(shard_S, ZERO_STATE_TILED) floats), bit for bit, for
+ * initialising a tiled state and for reading it back (checkpoints, inspection).
+ * Not part of a step. zero_state_unpack skips a NULL destination. The split
+ * arrays must not overlap the set buffer or each other.
+ * Errors: ZERO_E_INVAL (NULL buffers when shard_S > 0, overlap), ZERO_E_ALIGN,
+ * ZERO_E_RANGE (negative shard_S), ZERO_E_HIP.
+ */
+int zero_state_pack(const float* p_dev, const float* m_dev, const float* v_dev, int64_t shard_S,
+                    float* set_dev, void* stream);
+int zero_state_unpack(const float* set_dev, int64_t shard_S, float* p_dev, float* m_dev,
+                      float* v_dev, void* stream);
 
 /*
  * The commit rule of a mixed-precision step, host side. The pages name mixed
@@ -390,6 +442,10 @@ typedef struct {
     size_t ws_bytes;
     void* event_begin;             /* optional hipEvent_t handles: the start and end */
     void* event_end;               /* time of the step kernel itself, as above */
+    /* zero_state_layout of the two sets (0: split). Tiled: p[0], p[1] are the set
+       buffers, m and v NULL; inner part ends of zero_train_step_part must then be
+       multiples of ZERO_STATE_TILE */
+    int32_t state_layout;
 } zero_train_args;
 
 /*

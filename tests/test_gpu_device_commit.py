@@ -30,7 +30,8 @@ def bucket_table(Z, w, rank, bucket_elems):
     return torch.frombuffer(bytearray(bytes(raw)[: 16 * nb]), dtype=torch.uint8).to("cuda"), nb
 
 
-def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None, double_slot=False, wire=False):
+def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None, double_slot=False, wire=False,
+                        tiled=False):
     lay, covered = layout_of(w, rank)
     S = lay.S
     gdt = Z.ZERO_BF16 if w.grad_dtype == "bf16" else Z.ZERO_F32
@@ -41,13 +42,14 @@ def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None, double_slot=Fals
     step = Z.DeviceShardStep(S, w.N, gdt, to_dev(p0), lr=w.lr, beta1=w.beta1, beta2=w.beta2,
                              eps=w.eps, weight_decay=w.wd, loss_scale=w.loss_scale,
                              dynamic=w.dynamic_loss_scale, buckets=bt, n_buckets=nb,
-                             double_slot=double_slot)
+                             double_slot=double_slot,
+                             state_layout=Z.ZERO_STATE_TILED if tiled else Z.ZERO_STATE_SPLIT)
     tr = oracle.Trainer(p0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
                         oracle.f32_to_bf16(p0), loss_scale=w.loss_scale, dynamic=w.dynamic_loss_scale,
                         nthreads=NTHREADS, wire=wire, **w.hyper())
     flags = []
     for s in range(w.steps if steps is None else steps):
-        say(f"device {w.name} rank={rank} step={s} buckets={nb} wire={wire}")
+        say(f"device {w.name} rank={rank} step={s} buckets={nb} wire={wire} tiled={tiled}")
         reps = W.host_replicas(w, S, covered, rank, s)
         step.step([to_dev(r) for r in reps])
         flag, sumsq = tr.step(reps)
@@ -65,27 +67,38 @@ def run_device_protocol(Z, w, rank, bucket_elems=0, steps=None, double_slot=Fals
 
 
 @pytest.mark.parametrize("double_slot", [False, True])
-def test_tiny_every_rank(Z, double_slot):
+@pytest.mark.parametrize("tiled", [False, True])
+def test_tiny_every_rank(Z, double_slot, tiled):
     w = W.get("tiny")
     for rank in range(w.N):
-        assert run_device_protocol(Z, w, rank, double_slot=double_slot) == [0, 0, 0]
+        assert run_device_protocol(Z, w, rank, double_slot=double_slot, tiled=tiled) == [0, 0, 0]
 
 
-@pytest.mark.parametrize("rank,bucket_elems,double_slot", [(0, 0, False), (63, 0, True),
-                                                          (0, 4096, True), (31, 1000, False)])
-def test_ragged_injection(Z, rank, bucket_elems, double_slot):
+@pytest.mark.parametrize("rank,bucket_elems,double_slot,tiled", [
+    (0, 0, False, False), (63, 0, True, False), (0, 4096, True, False), (31, 1000, False, False),
+    (0, 0, False, True), (63, 0, True, True), (0, 4096, True, True), (31, 1000, False, True)])
+def test_ragged_injection(Z, rank, bucket_elems, double_slot, tiled):
     w = W.get("ragged")
     lay, covered = layout_of(w, rank)
     inj = W.injection(w, lay.S, covered, rank)
-    flags = run_device_protocol(Z, w, rank, bucket_elems, double_slot=double_slot)
+    flags = run_device_protocol(Z, w, rank, bucket_elems, double_slot=double_slot, tiled=tiled)
     assert flags == [1 if s == inj[0] else 0 for s in range(w.steps)]
 
 
-@pytest.mark.parametrize("name,rank,double_slot", [("ragged", 63, True), ("gpt2s", 0, False)])
-def test_wire_device_commit(Z, name, rank, double_slot):
+@pytest.mark.parametrize("name,rank,double_slot,tiled", [("ragged", 63, True, False),
+                                                         ("gpt2s", 0, False, False),
+                                                         ("ragged", 0, False, True)])
+def test_wire_device_commit(Z, name, rank, double_slot, tiled):
     w = W.get(name)
     run_device_protocol(Z, w, rank, double_slot=double_slot, wire=True,
-                        steps=None if name == "ragged" else 2)
+                        steps=None if name == "ragged" else 2, tiled=tiled)
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_gpt2_tiled_device_commit(Z, rank):
+    """The benchmark's configuration (GPT-2-small shard, tiled state, two slots)
+    against the oracle for three steps, on the first and last rank."""
+    run_device_protocol(Z, W.get("gpt2s"), rank, double_slot=True, tiled=True, steps=3)
 
 
 def test_gpt2_device_equals_host_commit(Z):

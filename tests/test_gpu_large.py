@@ -1,7 +1,7 @@
 """GPU parity at full shard sizes: the Llama-7B shard (S = 842,301,952, N = 8, loss
 scale 65536) and the Llama-70B shard (S = 2,155,520,256, N = 32, AdamW), in the
 launch configuration bench.py times (device commit, double-buffered slot,
-whole-shard grid).
+whole-shard grid, tiled state), and the Llama-7B shard also with split state.
 
 The oracle cannot run whole shards this size in a test, so it follows the
 trajectory of sampled elements (each element's update depends only on its own
@@ -37,7 +37,7 @@ def gather(t, idx_t):
     return t[idx_t]
 
 
-def run_large(Z, name, steps, n_random, sub_elems):
+def run_large(Z, name, steps, n_random, sub_elems, tiled=True):
     w = W.get(name)
     lay = oracle.Layout(w.numels, N=w.N, A=w.A, B=w.B)
     rank = 0
@@ -47,14 +47,16 @@ def run_large(Z, name, steps, n_random, sub_elems):
     idx = sample_index(S, covered, rng, n_random)
     idx_t = torch.from_numpy(idx).cuda()
     dev = torch.device("cuda")
-    say(f"{name}: S={S} N={w.N}, {idx.size} samples, allocating")
+    say(f"{name}: S={S} N={w.N}, {idx.size} samples, tiled={tiled}, allocating")
     reps = [torch.empty(S, dtype=torch.bfloat16, device=dev) for _ in range(w.N)]
     p0 = torch.empty(S, dtype=torch.float32, device=dev)
     W.device_fill_params(p0, w, covered, rank)
     p0_s = to_host(gather(p0, idx_t))
+    p0_head = p0[:min(S, sub_elems)].clone()
     step = Z.DeviceShardStep(S, w.N, Z.ZERO_BF16, p0, lr=w.lr, beta1=w.beta1, beta2=w.beta2,
                              eps=w.eps, weight_decay=w.wd, loss_scale=w.loss_scale,
-                             dynamic=w.dynamic_loss_scale, double_slot=True)
+                             dynamic=w.dynamic_loss_scale, double_slot=True,
+                             state_layout=Z.ZERO_STATE_TILED if tiled else Z.ZERO_STATE_SPLIT)
     del p0
     torch.cuda.empty_cache()
     tr = oracle.Trainer(p0_s.copy(), np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32),
@@ -68,7 +70,8 @@ def run_large(Z, name, steps, n_random, sub_elems):
         dreps = [r.view(torch.int16) for r in reps]
         if s == 0:
             # whole-shard properties on the first step, before the state moves
-            unfused_properties(Z, w, S, step, dreps, idx, idx_t, sreps, sub_elems)
+            unfused_properties(Z, w, S, p0_head, dreps, idx, idx_t, sreps, sub_elems)
+            del p0_head
         say(f"{name}: step {s}")
         step.step(dreps)
         flag, _ = tr.step(sreps)
@@ -76,15 +79,14 @@ def run_large(Z, name, steps, n_random, sub_elems):
         st = step.last_stats()
         assert flag == 0 and st.overflow == 0 and rec.last_overflow == 0
         assert rec.t == tr.t == s + 1 and np.isfinite(st.sumsq) and st.sumsq > 0
-        P, M, V = step.committed()
-        check_state(f"{name} step {s} (samples)", to_host(gather(P, idx_t)), to_host(gather(M, idx_t)),
-                    to_host(gather(V, idx_t)), to_host(gather(step.current_slot(), idx_t)),
-                    tr.p, tr.m, tr.v, tr.slot)
+        P, M, V = step.committed_at(idx_t)
+        check_state(f"{name} step {s} (samples)", to_host(P), to_host(M), to_host(V),
+                    to_host(gather(step.current_slot(), idx_t)), tr.p, tr.m, tr.v, tr.slot)
     del reps, dreps, step
     torch.cuda.empty_cache()
 
 
-def unfused_properties(Z, w, S, step, dreps, idx, idx_t, sreps, sub_elems):
+def unfused_properties(Z, w, S, p0_head, dreps, idx, idx_t, sreps, sub_elems):
     """On the first step's inputs: reduce_shard's g equals the oracle on the samples;
     its squared norm equals an fp64 sum of g^2; the fused kernel's own norm agrees;
     over the first `sub_elems` elements the unfused update equals the fused one
@@ -108,7 +110,7 @@ def unfused_properties(Z, w, S, step, dreps, idx, idx_t, sreps, sub_elems):
     # unfused update over a sub-range equals the fused kernel on the same sub-range
     n = min(S, sub_elems)
     say(f"{w.name}: fused vs unfused over the first {n} elements")
-    P0 = step.p[0][:n]
+    P0 = p0_head[:n]
     Zr = torch.zeros(n, dtype=torch.float32, device=dev)
     outs_u = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3)]
     slot_u = torch.empty(n, dtype=torch.int16, device=dev)
@@ -132,8 +134,10 @@ def unfused_properties(Z, w, S, step, dreps, idx, idx_t, sreps, sub_elems):
     torch.cuda.empty_cache()
 
 
-def test_llama7b_shard_full_size(Z):
-    run_large(Z, "llama7b", steps=W.get("llama7b").steps, n_random=400_000, sub_elems=1 << 28)
+@pytest.mark.parametrize("tiled", [True, False])
+def test_llama7b_shard_full_size(Z, tiled):
+    run_large(Z, "llama7b", steps=W.get("llama7b").steps, n_random=400_000, sub_elems=1 << 28,
+              tiled=tiled)
 
 
 def test_llama70b_shard_full_size(Z):

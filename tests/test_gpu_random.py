@@ -4,7 +4,8 @@ Each seed draws a replica count (1 to 256), a shard size (1 to 2M elements,
 ragged), the gradient type (bf16, fp32, bf16 wire), the path (host commit,
 device commit with one or two slots, a step split into random parts), Adam
 hyperparameters, a power-of-two loss scale with or without dynamic halving,
-value magnitudes over six decades, and, on about a quarter of the steps, one
+value magnitudes over six decades (seeds 40 and up keep the device paths' state
+in the tiled layout, with tile-aligned parts), and, on about a quarter of the steps, one
 injected +inf, -inf, NaN or 3e38. Every step's overflow flag, t, loss scale and
 squared norm (1e-9 relative) are checked, and the committed p, m, v and slot are
 compared bit for bit with the oracle's. Inputs come from numpy's seeded
@@ -36,9 +37,10 @@ def draw(seed):
     return rng, N, S, kind, path
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_case(Z, seed):
     rng, N, S, kind, path = draw(seed)
+    tiled = seed >= 40 and path != "host"
     steps = int(rng.integers(2, 5))
     ls = float(2.0 ** int(rng.integers(0, 17)))
     dynamic = bool(rng.random() < 0.5)
@@ -57,13 +59,16 @@ def test_random_case(Z, seed):
         st = Z.ShardStep(S, N, gdt, to_dev(p0), loss_scale=ls, dynamic=dynamic, **zhy)
     else:
         st = Z.DeviceShardStep(S, N, gdt, to_dev(p0), loss_scale=ls, dynamic=dynamic,
-                               double_slot=(path != "dev1"), **zhy)
+                               double_slot=(path != "dev1"),
+                               state_layout=Z.ZERO_STATE_TILED if tiled else Z.ZERO_STATE_SPLIT,
+                               **zhy)
     ends = None
     if path == "parts":
         k = int(rng.integers(1, 9))
-        ends = sorted(int(x) // 8 * 8 for x in rng.integers(0, S + 1, size=k - 1)) + [S]
+        g = Z.ZERO_STATE_TILE if tiled else 8
+        ends = sorted(int(x) // g * g for x in rng.integers(0, S + 1, size=k - 1)) + [S]
     desc = (f"seed={seed} N={N} S={S} {kind} {path} steps={steps} loss_scale={ls} "
-            f"dynamic={dynamic} parts={ends}")
+            f"dynamic={dynamic} parts={ends} tiled={tiled}")
     say(desc)
     for s in range(steps):
         sample = [rng.standard_normal(S) * sigma * ls for _ in range(N)]

@@ -396,3 +396,86 @@ def test_offload_step_validation(Z):
     assert status(lr=float("nan")) == -1
     assert status(n_replicas=0) == -3          # from the reduce's own checks
     assert st.t == 0 and st.n_skipped == 0      # nothing was committed
+
+
+def test_state_layout_sizes(Z):
+    T = Z.ZERO_STATE_TILE
+    assert T == 8192
+    for S in (0, 1, 8191, 8192, 8193, 10**9 + 7):
+        assert Z.zero_state_set_floats(S, Z.ZERO_STATE_SPLIT) == 3 * S
+        assert Z.zero_state_set_floats(S, Z.ZERO_STATE_TILED) == 3 * ((S + T - 1) // T) * T
+    assert Z.lib().zero_state_set_floats(-1, Z.ZERO_STATE_TILED) == -1
+    assert Z.lib().zero_state_set_floats(10, 2) == -1
+
+
+def test_state_layout_validation(Z):
+    """Tiled-state arguments are checked on the host before anything is enqueued:
+    the layout value, NULL m and v pointers, and overlaps over the whole set buffer
+    (3 * ZERO_STATE_TILE floats for a 64-element shard, 96 KiB)."""
+    big = 1 << 20                                # beyond one tiled set of S = 64
+    tiled = dict(p_in=FAKE, m_in=0, v_in=0, p_out=FAKE + big, m_out=0, v_out=0,
+                 slot=FAKE + 2 * big, stats=FAKE + 2 * big + 4096, workspace=FAKE + 2 * big + 8192,
+                 state_layout=Z.ZERO_STATE_TILED)
+
+    def adam(**kw):
+        d = dict(tiled)
+        d.update(kw)
+        a = base_args(Z, **d)
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_adam_step(a, stream=0)
+        return e.value.status
+
+    rep = [FAKE + 3 * big]
+    assert adam(replicas=rep, state_layout=2) == -1                 # unknown layout
+    assert adam(replicas=rep, m_in=FAKE + 4 * big) == -1            # m given with a tiled state
+    assert adam(replicas=rep, v_out=FAKE + 4 * big) == -1
+    assert adam(replicas=rep, p_out=FAKE + 4096) == -1              # p_out inside the p_in set
+    assert adam(replicas=rep, slot=FAKE + big + 90000) == -1        # slot inside the p_out set
+    assert adam(replicas=[FAKE + big + 50000 - 50000 % 16]) == -1   # replica inside the p_out set
+    assert adam(grad_f32=FAKE + 3 * big, p_out=FAKE + 64) == -1     # partial in-place overlap
+    assert adam(replicas=rep, p_in=FAKE + 8) == -2
+
+    FAKEREC = FAKE + 5 * big
+    tbase = dict(replicas=[FAKE + 3 * big], grad_dtype=1, p=(FAKE, FAKE + big), m=(0, 0), v=(0, 0),
+                 slot=FAKE + 2 * big, shard_S=64, lr=1e-3, eps=1e-8, weight_decay=0.0,
+                 state=FAKEREC, stats=FAKE + 2 * big + 4096, workspace=FAKE + 2 * big + 8192,
+                 state_layout=Z.ZERO_STATE_TILED)
+
+    def train(**kw):
+        d = dict(tbase)
+        d.update(kw)
+        a = Z.make_train_args(**d)
+        a.ws_bytes = 4096
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_train_step(a, stream=0)
+        return e.value.status
+
+    assert train(p=(FAKE, FAKE + 4096)) == -1                        # the two sets overlap
+    assert train(m=(FAKE + 4 * big, FAKE + 4 * big + 4096)) == -1    # m given with a tiled state
+    assert train(state_layout=-1) == -1
+    assert train(p=(FAKE, 0)) == -1
+    # parts of a tiled step start on tiles
+    a = Z.make_train_args(**dict(tbase, shard_S=20000, stats=FAKE + 2 * big + 65536,
+                                 workspace=FAKE + 2 * big + 131072))
+    a.ws_bytes = 1 << 16
+    tbl, cnt = Z.part_table([8000, 20000])
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_train_step_part(a, tbl, cnt, 0, stream=0)
+    assert e.value.status == -3 and "8192" in Z.zero_last_error()
+
+
+def test_state_convert_validation(Z):
+    L = Z.lib()
+    S = 100
+    SET, P, M, V = FAKE, FAKE + (1 << 20), FAKE + (1 << 20) + 4096, FAKE + (1 << 20) + 8192
+    assert L.zero_state_pack(P, M, V, S, None, None) == -1
+    assert L.zero_state_pack(P, None, V, S, SET, None) == -1          # pack needs all three
+    assert L.zero_state_pack(P, M, V, S, SET + 4, None) == -2
+    assert L.zero_state_pack(P, M, V, -1, SET, None) == -3
+    assert L.zero_state_pack(SET + 4096, M, V, S, SET, None) == -1    # p inside the set
+    assert L.zero_state_pack(P, P + 64, V, S, SET, None) == -1        # p and m overlap
+    assert L.zero_state_unpack(SET, S, P, M, SET + 90000, None) == -1  # v inside the set
+    assert L.zero_state_unpack(SET, S, P + 8, M, V, None) == -2
+    assert L.zero_gather_slot_tiled(SET, S, SET + 90000, None) == -1  # slot inside the set
+    assert L.zero_gather_slot_tiled(SET, -5, P, None) == -3
+    assert L.zero_gather_slot_tiled(SET + 2, S, P, None) == -2

@@ -24,6 +24,8 @@ ZERO_OK, ZERO_E_INVAL, ZERO_E_ALIGN, ZERO_E_RANGE, ZERO_E_NOMEM, ZERO_E_HIP, ZER
 ZERO_F32, ZERO_BF16, ZERO_BF16_WIRE = 0, 1, 2
 ZERO_COMMIT, ZERO_SKIP = 1, 2
 ZERO_MAX_REPLICAS = 1024
+ZERO_STATE_SPLIT, ZERO_STATE_TILED = 0, 1
+ZERO_STATE_TILE = 8192
 
 _STATUS = {0: "ZERO_OK", -1: "ZERO_E_INVAL", -2: "ZERO_E_ALIGN", -3: "ZERO_E_RANGE",
            -4: "ZERO_E_NOMEM", -5: "ZERO_E_HIP", -6: "ZERO_E_UNSUPPORTED"}
@@ -62,7 +64,7 @@ class zero_adam_args(ctypes.Structure):
                 ("n_buckets", i64), ("lr", f64), ("beta1", f64), ("beta2", f64), ("eps", f64),
                 ("weight_decay", f64), ("loss_scale", f64), ("step_t", i64),
                 ("stats_dev", vp), ("workspace_dev", vp), ("ws_bytes", sz),
-                ("event_begin", vp), ("event_end", vp)]
+                ("event_begin", vp), ("event_end", vp), ("state_layout", i32)]
 
 
 class zero_train_state(ctypes.Structure):
@@ -82,7 +84,8 @@ class zero_train_args(ctypes.Structure):
                 ("p", vp * 2), ("m", vp * 2), ("v", vp * 2), ("slot", vp * 2), ("shard_S", i64),
                 ("buckets_dev", vp), ("n_buckets", i64), ("lr", f64), ("eps", f64),
                 ("weight_decay", f64), ("state_dev", vp), ("stats_dev", vp),
-                ("workspace_dev", vp), ("ws_bytes", sz), ("event_begin", vp), ("event_end", vp)]
+                ("workspace_dev", vp), ("ws_bytes", sz), ("event_begin", vp), ("event_end", vp),
+                ("state_layout", i32)]
 
 
 class zero_host_adam_args(ctypes.Structure):
@@ -132,6 +135,11 @@ def lib() -> ctypes.CDLL:
     L.zero_reduce_shard.argtypes = [P(vp), i32, i32, i64, vp, i64, f64, vp, vp, vp, sz, vp]
     L.zero_adam_step.argtypes = [P(zero_adam_args), vp]
     L.zero_gather_slot.argtypes = [vp, i64, vp, vp]
+    L.zero_gather_slot_tiled.argtypes = [vp, i64, vp, vp]
+    L.zero_state_set_floats.argtypes = [i64, i32]
+    L.zero_state_set_floats.restype = i64
+    L.zero_state_pack.argtypes = [vp, vp, vp, i64, vp, vp]
+    L.zero_state_unpack.argtypes = [vp, i64, vp, vp, vp, vp]
     L.zero_commit_rule.argtypes = [P(zero_train_state), P(zero_stats)]
     L.zero_device_state_init.argtypes = [vp, vp, sz, f64, f64, f64, f64, i32, vp]
     L.zero_device_state_load.argtypes = [vp, vp, sz, P(zero_device_state), vp]
@@ -147,7 +155,8 @@ def lib() -> ctypes.CDLL:
     for name in ("zero_layout_build", "zero_layout_info_get", "zero_layout_offsets",
                  "zero_layout_segments", "zero_layout_buckets", "zero_layout_mem_values",
                  "zero_layout_mem_bytes", "zero_reduce_shard", "zero_adam_step",
-                 "zero_gather_slot", "zero_commit_rule", "zero_device_state_init",
+                 "zero_gather_slot", "zero_gather_slot_tiled", "zero_state_pack",
+                 "zero_state_unpack", "zero_commit_rule", "zero_device_state_init",
                  "zero_device_state_load", "zero_train_step", "zero_train_step_part",
                  "zero_host_adam", "zero_offload_step", "zero_gather_tensors"):
         getattr(L, name).restype = ctypes.c_int
@@ -272,7 +281,7 @@ def make_adam_args(*, replicas=None, grad_dtype: int = ZERO_BF16, grad_f32=None,
                    p_out, m_out, v_out, slot=None, shard_S: int, buckets=None, n_buckets: int = 0,
                    lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
                    loss_scale: float = 1.0, step_t: int, stats, workspace, event_begin=None,
-                   event_end=None):
+                   event_end=None, state_layout: int = 0):
     a = zero_adam_args()
     keep = []
     if replicas is not None:
@@ -295,6 +304,7 @@ def make_adam_args(*, replicas=None, grad_dtype: int = ZERO_BF16, grad_f32=None,
     a.ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
     a.event_begin = _event(event_begin)
     a.event_end = _event(event_end)
+    a.state_layout = int(state_layout)
     a._keep = keep
     return a
 
@@ -320,6 +330,28 @@ def zero_gather_slot(master, shard_S: int, slot, stream=None) -> None:
     _check(lib().zero_gather_slot(_addr(master), int(shard_S), _addr(slot), _stream(stream)))
 
 
+def zero_gather_slot_tiled(set_buf, shard_S: int, slot, stream=None) -> None:
+    _check(lib().zero_gather_slot_tiled(_addr(set_buf), int(shard_S), _addr(slot), _stream(stream)))
+
+
+def zero_state_set_floats(shard_S: int, state_layout: int) -> int:
+    n = lib().zero_state_set_floats(int(shard_S), int(state_layout))
+    if n < 0:
+        raise ZeroError(ZERO_E_INVAL, f"zero_state_set_floats: shard_S={shard_S}, "
+                                      f"state_layout={state_layout}")
+    return n
+
+
+def zero_state_pack(p, m, v, shard_S: int, set_buf, stream=None) -> None:
+    _check(lib().zero_state_pack(_addr(p), _addr(m), _addr(v), int(shard_S), _addr(set_buf),
+                                 _stream(stream)))
+
+
+def zero_state_unpack(set_buf, shard_S: int, p=None, m=None, v=None, stream=None) -> None:
+    _check(lib().zero_state_unpack(_addr(set_buf), int(shard_S), _addr(p), _addr(m), _addr(v),
+                                   _stream(stream)))
+
+
 def zero_commit_rule(state: zero_train_state, stats_host: zero_stats) -> int:
     return _check(lib().zero_commit_rule(ctypes.byref(state), ctypes.byref(stats_host)))
 
@@ -340,7 +372,8 @@ def zero_device_state_load(state, workspace, saved: zero_device_state, stream=No
 
 def make_train_args(*, replicas, grad_dtype: int, p, m, v, slot=None, shard_S: int, buckets=None,
                     n_buckets: int = 0, lr: float, eps: float, weight_decay: float, state, stats,
-                    workspace, event_begin=None, event_end=None) -> zero_train_args:
+                    workspace, event_begin=None, event_end=None,
+                    state_layout: int = 0) -> zero_train_args:
     a = zero_train_args()
     table = _replica_table(replicas)
     a.replicas = ctypes.cast(table, ctypes.POINTER(vp))
@@ -362,6 +395,7 @@ def make_train_args(*, replicas, grad_dtype: int, p, m, v, slot=None, shard_S: i
     a.ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
     a.event_begin = _event(event_begin)
     a.event_end = _event(event_end)
+    a.state_layout = int(state_layout)
     a._keep = [table]
     return a
 

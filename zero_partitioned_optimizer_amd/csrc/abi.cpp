@@ -94,6 +94,28 @@ zk::Scalars adam_scalars(const zero_adam_args& a, int32_t n, double loss_scale) 
 
 int64_t elem_bytes(zero_dtype dt) { return dt == ZERO_F32 ? 4 : 2; }
 
+// Floats of one tiled state set (three sections per tile of ZERO_STATE_TILE).
+int64_t tiled_floats(int64_t S) {
+    return 3 * ((S + ZERO_STATE_TILE - 1) / ZERO_STATE_TILE) * ZERO_STATE_TILE;
+}
+
+// state_layout must be split or tiled; a tiled state takes m and v from the p
+// buffers, so their pointers must be NULL.
+int check_layout(const char* fn, int32_t layout, const void* const* mv, int n_mv) {
+    if (layout != ZERO_STATE_SPLIT && layout != ZERO_STATE_TILED) {
+        set_error("%s: unknown state_layout %d", fn, (int)layout);
+        return ZERO_E_INVAL;
+    }
+    if (layout == ZERO_STATE_TILED)
+        for (int i = 0; i < n_mv; ++i)
+            if (mv[i]) {
+                set_error("%s: a tiled state keeps m and v in the p buffers; the m and v pointers "
+                          "must be NULL", fn);
+                return ZERO_E_INVAL;
+            }
+    return ZERO_OK;
+}
+
 int check_replicas(const char* fn, const void* const* replicas, int32_t n, zero_dtype dt,
                    int64_t S) {
     if (!replicas) {
@@ -267,8 +289,13 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
         rc = check_replicas(fn, a.replicas, a.n_replicas, a.grad_dtype, S);
         if (rc) return rc;
     }
-    const void* need[] = {fused ? (const void*)a.replicas : (const void*)a.grad_f32, a.p_in, a.m_in,
-                          a.v_in, a.p_out, a.m_out, a.v_out};
+    const void* mv[] = {a.m_in, a.v_in, a.m_out, a.v_out};
+    rc = check_layout(fn, a.state_layout, mv, 4);
+    if (rc) return rc;
+    const bool tiled = a.state_layout == ZERO_STATE_TILED;
+    const void* need[] = {fused ? (const void*)a.replicas : (const void*)a.grad_f32, a.p_in,
+                          tiled ? a.p_in : a.m_in, tiled ? a.p_in : a.v_in, a.p_out,
+                          tiled ? a.p_out : a.m_out, tiled ? a.p_out : a.v_out};
     for (const void* p : need) {
         if (!p && (S > 0 || p == (const void*)a.replicas)) {
             set_error("%s: a state or gradient buffer (p/m/v in/out, grad_f32) is NULL", fn);
@@ -294,8 +321,10 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
     // Aliasing: outputs must be pairwise disjoint and disjoint from every input,
     // except that the unfused path may update p, m, v exactly in place.
     const int64_t b4 = 4 * S;
-    const Span outs[] = {span("p_out", a.p_out, b4), span("m_out", a.m_out, b4),
-                         span("v_out", a.v_out, b4),
+    const int64_t bp = tiled ? 4 * tiled_floats(S) : b4;   // p buffer: the whole set when tiled
+    const int64_t bmv = tiled ? 0 : b4;
+    const Span outs[] = {span("p_out", a.p_out, bp), span("m_out", a.m_out, bmv),
+                         span("v_out", a.v_out, bmv),
                          span("slot", a.slot_bf16, a.slot_bf16 ? 2 * S : 0),
                          span("stats", a.stats_dev, 16),
                          span("workspace", a.workspace_dev, (int64_t)a.ws_bytes)};
@@ -306,8 +335,8 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
                 set_error("%s: outputs %s and %s overlap", fn, outs[i].name, outs[k].name);
                 return ZERO_E_INVAL;
             }
-    const Span ins_state[] = {span("p_in", a.p_in, b4), span("m_in", a.m_in, b4),
-                              span("v_in", a.v_in, b4)};
+    const Span ins_state[] = {span("p_in", a.p_in, bp), span("m_in", a.m_in, bmv),
+                              span("v_in", a.v_in, bmv)};
     for (int i = 0; i < n_outs; ++i) {
         for (int k = 0; k < 3; ++k) {
             if (!overlap(outs[i], ins_state[k])) continue;
@@ -353,6 +382,7 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
     d.v_out = a.v_out;
     d.slot = a.slot_bf16;
     d.g_out = nullptr;
+    d.tiled = tiled;
     // the unfused source is already averaged and unscaled: inv = 1 (x * 1 == x)
     d.sc = adam_scalars(a, fused ? a.n_replicas : 1, fused ? a.loss_scale : 1.0);
     d.stats = a.stats_dev;
@@ -464,7 +494,12 @@ static int check_train_args(const char* fn, const zero_train_args* args) {
         set_error("%s: state_dev is not 16-byte aligned", fn);
         return ZERO_E_ALIGN;
     }
-    const float* sets[6] = {a.p[0], a.p[1], a.m[0], a.m[1], a.v[0], a.v[1]};
+    const void* mv[] = {a.m[0], a.m[1], a.v[0], a.v[1]};
+    rc = check_layout(fn, a.state_layout, mv, 4);
+    if (rc) return rc;
+    const bool tiled = a.state_layout == ZERO_STATE_TILED;
+    const float* sets[6] = {a.p[0], a.p[1], tiled ? a.p[0] : a.m[0], tiled ? a.p[1] : a.m[1],
+                            tiled ? a.p[0] : a.v[0], tiled ? a.p[1] : a.v[1]};
     for (const float* p : sets) {
         if (!p && S > 0) {
             set_error("%s: a state buffer is NULL", fn);
@@ -489,9 +524,11 @@ static int check_train_args(const char* fn, const zero_train_args* args) {
         return ZERO_E_INVAL;
     }
     const int64_t b4 = 4 * S;
-    const Span bufs[] = {span("p[0]", a.p[0], b4), span("p[1]", a.p[1], b4),
-                         span("m[0]", a.m[0], b4), span("m[1]", a.m[1], b4),
-                         span("v[0]", a.v[0], b4), span("v[1]", a.v[1], b4),
+    const int64_t bp = tiled ? 4 * tiled_floats(S) : b4;   // p buffer: the whole set when tiled
+    const int64_t bmv = tiled ? 0 : b4;
+    const Span bufs[] = {span("p[0]", a.p[0], bp), span("p[1]", a.p[1], bp),
+                         span("m[0]", a.m[0], bmv), span("m[1]", a.m[1], bmv),
+                         span("v[0]", a.v[0], bmv), span("v[1]", a.v[1], bmv),
                          span("slot[0]", a.slot[0], a.slot[0] ? 2 * S : 0),
                          span("slot[1]", a.slot[1], a.slot[1] ? 2 * S : 0),
                          span("stats", a.stats_dev, 16),
@@ -535,6 +572,7 @@ static zk::StepDesc train_desc(const zero_train_args& a) {
         d.set_v[i] = a.v[i];
     }
     d.ctrl = a.state_dev;
+    d.tiled = a.state_layout == ZERO_STATE_TILED;
     d.slot = a.slot[0];
     if (a.slot[1]) {
         d.set_slot[0] = a.slot[0];
@@ -578,18 +616,21 @@ int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, 
         set_error("%s: part %d of n_parts=%d out of range", fn, (int)part, (int)n_parts);
         return ZERO_E_RANGE;
     }
-    // boundaries: non-decreasing, multiples of 8 elements (16 bytes), the last one S;
+    // boundaries: non-decreasing, multiples of 8 elements (16 bytes; of ZERO_STATE_TILE
+    // with a tiled state, so that a part starts on a tile), the last one S;
     // every part gets at most kGridMax / n_parts workgroups, so the partial slots
     // of all parts fit the workspace of a whole-shard step
     const int part_cap = zk::kGridMax / n_parts;
+    const bool tiled = a.state_layout == ZERO_STATE_TILED;
+    const int64_t gran = tiled ? ZERO_STATE_TILE : 8;
     int64_t prev = 0, total = 0, base = 0;
     for (int32_t k = 0; k < n_parts; ++k) {
         const int64_t e = part_ends[k];
         const bool last = k == n_parts - 1;
-        if (e < prev || e > S || (last ? e != S : (e % 8) != 0)) {
+        if (e < prev || e > S || (last ? e != S : (e % gran) != 0)) {
             set_error("%s: part_ends[%d]=%lld invalid (previous %lld, shard_S %lld; inner ends "
-                      "must be multiples of 8, the last must equal shard_S)",
-                      fn, (int)k, (long long)e, (long long)prev, (long long)S);
+                      "must be multiples of %lld, the last must equal shard_S)",
+                      fn, (int)k, (long long)e, (long long)prev, (long long)S, (long long)gran);
             return ZERO_E_RANGE;
         }
         const int64_t g = zk::grid_for(e - prev, 0, a.n_replicas, part_cap);
@@ -613,9 +654,13 @@ int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, 
     d.replicas = shifted;
     d.S = hi - lo;
     for (int i = 0; i < 2; ++i) {
-        d.set_p[i] = a.p[i] + lo;
-        d.set_m[i] = a.m[i] + lo;
-        d.set_v[i] = a.v[i] + lo;
+        if (tiled) {
+            d.set_p[i] = a.p[i] + lo / ZERO_STATE_TILE * 3 * ZERO_STATE_TILE;   // lo starts a tile
+        } else {
+            d.set_p[i] = a.p[i] + lo;
+            d.set_m[i] = a.m[i] + lo;
+            d.set_v[i] = a.v[i] + lo;
+        }
         if (d.set_slot[i]) d.set_slot[i] = d.set_slot[i] + lo;
     }
     if (d.slot) d.slot = d.slot + lo;
@@ -625,7 +670,7 @@ int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, 
     d.no_restore = true;
     rc = hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
     if (rc || !last || !a.slot[0] || a.slot[1]) return rc;
-    return hip_status(zk::launch_restore(a.state_dev, a.p[0], a.p[1], a.slot[0], S,
+    return hip_status(zk::launch_restore(a.state_dev, a.p[0], a.p[1], a.slot[0], S, tiled,
                                          static_cast<hipStream_t>(stream)),
                       fn);
 }
@@ -692,9 +737,8 @@ int zero_gather_tensors(const void* const* shards, int32_t n_shards, int64_t sha
                       fn);
 }
 
-int zero_gather_slot(const float* master_dev, int64_t shard_S, uint16_t* slot_bf16_dev,
-                     void* stream) {
-    static const char* fn = "zero_gather_slot";
+static int gather_slot(const char* fn, const float* master_dev, int64_t shard_S, bool tiled,
+                       uint16_t* slot_bf16_dev, void* stream) {
     if (shard_S < 0) {
         set_error("%s: shard_S=%lld is negative", fn, (long long)shard_S);
         return ZERO_E_RANGE;
@@ -707,13 +751,70 @@ int zero_gather_slot(const float* master_dev, int64_t shard_S, uint16_t* slot_bf
         set_error("%s: buffers must be 16-byte aligned", fn);
         return ZERO_E_ALIGN;
     }
-    if (overlap(span("master", master_dev, 4 * shard_S), span("slot", slot_bf16_dev, 2 * shard_S))) {
+    const int64_t mb = 4 * (tiled ? tiled_floats(shard_S) : shard_S);
+    if (overlap(span("master", master_dev, mb), span("slot", slot_bf16_dev, 2 * shard_S))) {
         set_error("%s: master and slot overlap", fn);
         return ZERO_E_INVAL;
     }
     if (shard_S == 0) return ZERO_OK;
-    return hip_status(zk::launch_cast_slot(master_dev, shard_S, slot_bf16_dev,
+    return hip_status(zk::launch_cast_slot(master_dev, shard_S, tiled, slot_bf16_dev,
                                            static_cast<hipStream_t>(stream)), fn);
+}
+
+int zero_gather_slot(const float* master_dev, int64_t shard_S, uint16_t* slot_bf16_dev,
+                     void* stream) {
+    return gather_slot("zero_gather_slot", master_dev, shard_S, false, slot_bf16_dev, stream);
+}
+
+int zero_gather_slot_tiled(const float* set_dev, int64_t shard_S, uint16_t* slot_bf16_dev,
+                           void* stream) {
+    return gather_slot("zero_gather_slot_tiled", set_dev, shard_S, true, slot_bf16_dev, stream);
+}
+
+int64_t zero_state_set_floats(int64_t shard_S, int32_t state_layout) {
+    if (shard_S < 0) return -1;
+    if (state_layout == ZERO_STATE_SPLIT) return 3 * shard_S;
+    if (state_layout == ZERO_STATE_TILED) return tiled_floats(shard_S);
+    return -1;
+}
+
+static int state_convert(const char* fn, bool unpack, float* set_dev, int64_t S, float* p, float* m,
+                         float* v, void* stream) {
+    if (S < 0) {
+        set_error("%s: shard_S=%lld is negative", fn, (long long)S);
+        return ZERO_E_RANGE;
+    }
+    if (S > 0 && (!set_dev || (!unpack && (!p || !m || !v)))) {
+        set_error("%s: NULL buffer", fn);
+        return ZERO_E_INVAL;
+    }
+    if (!aligned16(set_dev) || !aligned16(p) || !aligned16(m) || !aligned16(v)) {
+        set_error("%s: buffers must be 16-byte aligned", fn);
+        return ZERO_E_ALIGN;
+    }
+    const Span b[] = {span("set", set_dev, 4 * tiled_floats(S)), span("p", p, p ? 4 * S : 0),
+                      span("m", m, m ? 4 * S : 0), span("v", v, v ? 4 * S : 0)};
+    for (int i = 0; i < 4; ++i)
+        for (int k = i + 1; k < 4; ++k)
+            if (overlap(b[i], b[k])) {
+                set_error("%s: buffers %s and %s overlap", fn, b[i].name, b[k].name);
+                return ZERO_E_INVAL;
+            }
+    if (S == 0) return ZERO_OK;
+    return hip_status(zk::launch_state_convert(unpack, set_dev, p, m, v, S,
+                                               static_cast<hipStream_t>(stream)), fn);
+}
+
+int zero_state_pack(const float* p_dev, const float* m_dev, const float* v_dev, int64_t shard_S,
+                    float* set_dev, void* stream) {
+    return state_convert("zero_state_pack", false, set_dev, shard_S, const_cast<float*>(p_dev),
+                         const_cast<float*>(m_dev), const_cast<float*>(v_dev), stream);
+}
+
+int zero_state_unpack(const float* set_dev, int64_t shard_S, float* p_dev, float* m_dev,
+                      float* v_dev, void* stream) {
+    return state_convert("zero_state_unpack", true, const_cast<float*>(set_dev), shard_S, p_dev, m_dev,
+                         v_dev, stream);
 }
 
 int zero_commit_rule(zero_train_state* state, const zero_stats* stats_host) {

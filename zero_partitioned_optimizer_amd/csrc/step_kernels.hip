@@ -100,6 +100,26 @@ struct Res {
 // memory access
 // ---------------------------------------------------------------------------
 
+// Where quad q / element e of the fp32 state lives in a set's buffer. Split
+// layout: p, m and v are three arrays indexed by element. Tiled layout: one
+// array of tiles of kStateTile elements, each holding that range of p, then of
+// m, then of v; the m and v bases are the p base plus one and two sections, so
+// the same index serves all three.
+template <bool TILED>
+__device__ __forceinline__ int64_t state_q(int64_t q) {
+    if constexpr (TILED)
+        return (q >> kStateTileQuadsLog2) * (3 * kStateTileQuads) + (q & (kStateTileQuads - 1));
+    else
+        return q;
+}
+template <bool TILED>
+__device__ __forceinline__ int64_t state_e(int64_t e) {
+    if constexpr (TILED)
+        return (e >> kStateTileLog2) * (3 * kStateTile) + (e & (kStateTile - 1));
+    else
+        return e;
+}
+
 template <typename T>
 __device__ __forceinline__ T ld(const T* p) {
 #if ZERO_NT
@@ -307,7 +327,7 @@ __device__ __forceinline__ void fold(const KParams& a, int64_t q0, int64_t qs, f
 // launches read the committed state's record: which state set is current, the
 // loss scale and beta^t; each workgroup derives the update's scalars from it
 // with the same double operations, rounded once to fp32, that the host uses.
-template <bool CTRL>
+template <bool CTRL, bool TILED>
 __device__ __forceinline__ Res resolve(const KParams& a) {
     Res r;
     r.sc = a.sc;
@@ -343,6 +363,13 @@ __device__ __forceinline__ Res resolve(const KParams& a) {
         r.slot = a.set_slot[1] ? a.set_slot[nxt] : a.slot;
         r.tag = c->seq + 1u;
     }
+    if constexpr (TILED) {
+        // one buffer per set: m and v sit one and two sections after p in each tile
+        r.m_in = r.p_in + kStateTile;
+        r.v_in = r.p_in + 2 * kStateTile;
+        r.m_out = r.p_out + kStateTile;
+        r.v_out = r.p_out + 2 * kStateTile;
+    }
     return r;
 }
 
@@ -355,7 +382,7 @@ struct Outs {
 // ROWS quads at q0, q0 + qs, ...: fold, average, flag, g^2 and (with ADAM) the
 // update of 4*ROWS elements of this lane. Reduce-only launches store g here;
 // the update is returned in `o` for quads_store.
-template <typename RT, bool ADAM, bool WRITE_G, int ROWS>
+template <typename RT, bool ADAM, bool WRITE_G, bool TILED, int ROWS>
 __device__ __forceinline__ void quads_compute(const KParams& a, const Res& rs, int64_t q0,
                                               int64_t qs, double& sq, uint32_t& bad,
                                               Outs<ROWS>& o) {
@@ -363,7 +390,7 @@ __device__ __forceinline__ void quads_compute(const KParams& a, const Res& rs, i
     if constexpr (ADAM) {
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-            const int64_t q = q0 + r * qs;
+            const int64_t q = state_q<TILED>(q0 + r * qs);
             p[r] = ld(reinterpret_cast<const f32x4*>(rs.p_in) + q);
             m[r] = ld(reinterpret_cast<const f32x4*>(rs.m_in) + q);
             v[r] = ld(reinterpret_cast<const f32x4*>(rs.v_in) + q);
@@ -395,15 +422,16 @@ __device__ __forceinline__ void quads_compute(const KParams& a, const Res& rs, i
     }
 }
 
-template <int ROWS>
+template <bool TILED, int ROWS>
 __device__ __forceinline__ void quads_store(const Res& rs, int64_t q0, int64_t qs,
                                             const Outs<ROWS>& o) {
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
         const int64_t q = q0 + r * qs;
-        st(reinterpret_cast<f32x4*>(rs.p_out) + q, o.pn[r]);
-        st(reinterpret_cast<f32x4*>(rs.m_out) + q, o.m1[r]);
-        st(reinterpret_cast<f32x4*>(rs.v_out) + q, o.v1[r]);
+        const int64_t qt = state_q<TILED>(q);
+        st(reinterpret_cast<f32x4*>(rs.p_out) + qt, o.pn[r]);
+        st(reinterpret_cast<f32x4*>(rs.m_out) + qt, o.m1[r]);
+        st(reinterpret_cast<f32x4*>(rs.v_out) + qt, o.v1[r]);
         if (rs.slot) {
             u32x2 w;
             w.x = f2bf(o.pn[r].x) | (f2bf(o.pn[r].y) << 16);
@@ -414,16 +442,16 @@ __device__ __forceinline__ void quads_store(const Res& rs, int64_t q0, int64_t q
 }
 
 // The whole step for ROWS quads of this lane.
-template <typename RT, bool ADAM, bool WRITE_G, int ROWS>
+template <typename RT, bool ADAM, bool WRITE_G, bool TILED, int ROWS>
 __device__ __forceinline__ void quads(const KParams& a, const Res& rs, int64_t q0, int64_t qs,
                                       double& sq, uint32_t& bad) {
     Outs<ROWS> o;
-    quads_compute<RT, ADAM, WRITE_G, ROWS>(a, rs, q0, qs, sq, bad, o);
-    if constexpr (ADAM) quads_store<ROWS>(rs, q0, qs, o);
+    quads_compute<RT, ADAM, WRITE_G, TILED, ROWS>(a, rs, q0, qs, sq, bad, o);
+    if constexpr (ADAM) quads_store<TILED, ROWS>(rs, q0, qs, o);
 }
 
 // One element, for bucket edges and the shard tail.
-template <typename RT, bool ADAM, bool WRITE_G>
+template <typename RT, bool ADAM, bool WRITE_G, bool TILED>
 __device__ __forceinline__ void one_elem(const KParams& a, const Res& rs, int64_t e, double& sq,
                                          uint32_t& bad) {
     // replica loads in batches of 8, all in flight before their adds (a spare load
@@ -449,31 +477,32 @@ __device__ __forceinline__ void one_elem(const KParams& a, const Res& rs, int64_
     if constexpr (WRITE_G) a.g_out[e] = g;
     if constexpr (ADAM) {
         float pn, m1, v1;
-        adam1(g, rs.p_in[e], rs.m_in[e], rs.v_in[e], rs.sc, pn, m1, v1);
-        rs.p_out[e] = pn;
-        rs.m_out[e] = m1;
-        rs.v_out[e] = v1;
+        const int64_t es = state_e<TILED>(e);
+        adam1(g, rs.p_in[es], rs.m_in[es], rs.v_in[es], rs.sc, pn, m1, v1);
+        rs.p_out[es] = pn;
+        rs.m_out[es] = m1;
+        rs.v_out[es] = v1;
         if (rs.slot) rs.slot[e] = (uint16_t)f2bf(pn);
     }
 }
 
 // All elements of [lo, hi) by the threads of one workgroup.
-template <typename RT, bool ADAM, bool WRITE_G, int ROWS>
+template <typename RT, bool ADAM, bool WRITE_G, bool TILED, int ROWS>
 __device__ __forceinline__ void range(const KParams& a, const Res& rs, int64_t lo, int64_t hi,
                                       double& sq, uint32_t& bad) {
     const int tid = threadIdx.x;
     const int64_t qa = (lo + 3) >> 2;       // first whole quad
     const int64_t qb = hi >> 2;             // one past the last whole quad
     if (qa >= qb) {
-        for (int64_t e = lo + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
+        for (int64_t e = lo + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
         return;
     }
-    for (int64_t e = lo + tid; e < qa * 4; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
+    for (int64_t e = lo + tid; e < qa * 4; e += kBlock) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
     int64_t q = qa + tid;
     for (; q + (ROWS - 1) * kBlock < qb; q += ROWS * kBlock)
-        quads<RT, ADAM, WRITE_G, ROWS>(a, rs, q, kBlock, sq, bad);
-    for (; q < qb; q += kBlock) quads<RT, ADAM, WRITE_G, 1>(a, rs, q, 0, sq, bad);
-    for (int64_t e = qb * 4 + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
+        quads<RT, ADAM, WRITE_G, TILED, ROWS>(a, rs, q, kBlock, sq, bad);
+    for (; q < qb; q += kBlock) quads<RT, ADAM, WRITE_G, TILED, 1>(a, rs, q, 0, sq, bad);
+    for (int64_t e = qb * 4 + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
 }
 
 // Wave64 shuffles, then LDS across the workgroup's waves, in a fixed order.
@@ -617,9 +646,9 @@ __device__ __forceinline__ void collect_and_commit(const uint64_t* base, int n, 
     }
 }
 
-template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL, int ROWS>
+template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL, bool TILED, int ROWS>
 __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
-    const Res rs = resolve<CTRL>(a);
+    const Res rs = resolve<CTRL, TILED>(a);
     double sq = 0.0;
     uint32_t bad = 0u, badb = 0u;
     if constexpr (!BUCKETS) {
@@ -627,13 +656,13 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
         const int64_t per_trip = (int64_t)ROWS * kBlock;
         const int64_t ntrips = nq / per_trip;
         for (int64_t trip = blockIdx.x; trip < ntrips; trip += gridDim.x)
-            quads<RT, ADAM, WRITE_G, ROWS>(a, rs, trip * per_trip + threadIdx.x, kBlock, sq, bad);
+            quads<RT, ADAM, WRITE_G, TILED, ROWS>(a, rs, trip * per_trip + threadIdx.x, kBlock, sq, bad);
         // whole quads after the last full trip, and the last S % 4 elements
         if ((int64_t)blockIdx.x == ntrips % gridDim.x) {
             for (int64_t q = ntrips * per_trip + threadIdx.x; q < nq; q += kBlock)
-                quads<RT, ADAM, WRITE_G, 1>(a, rs, q, 0, sq, bad);
+                quads<RT, ADAM, WRITE_G, TILED, 1>(a, rs, q, 0, sq, bad);
             const int64_t e = nq * 4 + threadIdx.x;
-            if (e < a.S) one_elem<RT, ADAM, WRITE_G>(a, rs, e, sq, bad);
+            if (e < a.S) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
         }
     } else {
         for (int64_t b = blockIdx.x; b < a.n_buckets; b += gridDim.x) {
@@ -643,7 +672,7 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
                 if (threadIdx.x == 0) badb += 1u;
                 continue;
             }
-            range<RT, ADAM, WRITE_G, ROWS>(a, rs, lo, lo + len, sq, bad);
+            range<RT, ADAM, WRITE_G, TILED, ROWS>(a, rs, lo, lo + len, sq, bad);
         }
     }
     block_reduce(sq, bad, badb);
@@ -700,12 +729,14 @@ __global__ void __launch_bounds__(kFinalizeBlock) k_finalize(const Partial* part
     }
 }
 
-// slot[i] = bf16(master[i]) over quads [0, S/4) by the whole grid, tail by workgroup 0.
+// slot[i] = bf16(master[i]) over quads [0, S/4) by the whole grid, tail by workgroup
+// 0; master is a p array (split) or a set buffer (tiled).
+template <bool TILED>
 __device__ __forceinline__ void cast_range(const float* master, int64_t S, uint16_t* slot) {
     const int64_t nq = S >> 2;
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x; q < nq; q += stride) {
-        const f32x4 x = ld(reinterpret_cast<const f32x4*>(master) + q);
+        const f32x4 x = ld(reinterpret_cast<const f32x4*>(master) + state_q<TILED>(q));
         u32x2 w;
         w.x = f2bf(x.x) | (f2bf(x.y) << 16);
         w.y = f2bf(x.z) | (f2bf(x.w) << 16);
@@ -713,24 +744,64 @@ __device__ __forceinline__ void cast_range(const float* master, int64_t S, uint1
     }
     if (blockIdx.x == 0) {
         const int64_t e = nq * 4 + threadIdx.x;
-        if (e < S) slot[e] = (uint16_t)f2bf(master[e]);
+        if (e < S) slot[e] = (uint16_t)f2bf(master[state_e<TILED>(e)]);
     }
 }
 
+template <bool TILED>
 __global__ void __launch_bounds__(kBlock) k_cast_slot(const float* master, int64_t S,
                                                      uint16_t* slot) {
-    cast_range(master, S, slot);
+    cast_range<TILED>(master, S, slot);
 }
 
 // After a device-resident step: if it overflowed, restore the slot from the
 // committed master (the current set, which a skipped step leaves current).
 // Every workgroup reads the verdict the step's commit wrote into the record and,
 // on a clean step, exits at once.
+template <bool TILED>
 __global__ void __launch_bounds__(kBlock) k_restore(const zero_device_state* ctrl,
                                                    const float* set_p0, const float* set_p1,
                                                    uint16_t* slot, int64_t S) {
     if (ctrl->last_overflow == 0u) return;
-    cast_range((ctrl->cur & 1u) ? set_p1 : set_p0, S, slot);
+    cast_range<TILED>((ctrl->cur & 1u) ? set_p1 : set_p0, S, slot);
+}
+
+// Conversion between three split arrays p, m, v [S] and one tiled set buffer;
+// UNPACK copies tiled -> split (a NULL destination is skipped), else split -> tiled.
+// Elements of the last tile at or beyond S are not touched.
+template <bool UNPACK>
+__global__ void __launch_bounds__(kBlock) k_state_convert(float* tiled, float* p, float* m, float* v,
+                                                         int64_t S) {
+    const int64_t nq = S >> 2;
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    float* const sec[3] = {p, m, v};
+    for (int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x; q < nq; q += stride) {
+        const int64_t t = state_q<true>(q);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            f32x4* tq = reinterpret_cast<f32x4*>(tiled) + t + k * kStateTileQuads;
+            f32x4* sq = reinterpret_cast<f32x4*>(sec[k]) + q;
+            if constexpr (UNPACK) {
+                if (sec[k]) st(sq, ld(tq));
+            } else {
+                st(tq, ld(sq));
+            }
+        }
+    }
+    if (blockIdx.x == 0) {
+        const int64_t e = nq * 4 + threadIdx.x;
+        if (e < S) {
+            const int64_t t = state_e<true>(e);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                if constexpr (UNPACK) {
+                    if (sec[k]) sec[k][e] = tiled[t + k * kStateTile];
+                } else {
+                    tiled[t + k * kStateTile] = sec[k][e];
+                }
+            }
+        }
+    }
 }
 
 // Writing a whole record (initial or restored), and clearing the workspace its
@@ -787,26 +858,29 @@ static int grid_stream(int64_t S) {
 // One launch of the step kernel. With timing events the launch carries them
 // (hipExtLaunchKernelGGL), so they take the kernel's own start and end and their
 // interval is the kernel alone, not the stream's gaps around it.
-template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL, int ROWS>
+template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL, bool TILED, int ROWS>
 static void launch_one(const StepDesc& d, const KParams& k, int grid, hipStream_t st) {
     if (d.ev_begin || d.ev_end)
-        hipExtLaunchKernelGGL((k_step<RT, BUCKETS, ADAM, WRITE_G, CTRL, ROWS>), dim3(grid),
+        hipExtLaunchKernelGGL((k_step<RT, BUCKETS, ADAM, WRITE_G, CTRL, TILED, ROWS>), dim3(grid),
                               dim3(kBlock), 0, st, d.ev_begin, d.ev_end, 0, k);
     else
-        hipLaunchKernelGGL((k_step<RT, BUCKETS, ADAM, WRITE_G, CTRL, ROWS>), dim3(grid), dim3(kBlock),
-                           0, st, k);
+        hipLaunchKernelGGL((k_step<RT, BUCKETS, ADAM, WRITE_G, CTRL, TILED, ROWS>), dim3(grid),
+                           dim3(kBlock), 0, st, k);
 }
 
 template <typename RT, bool BUCKETS, int ROWS>
 static void launch_rows(const StepDesc& d, const KParams& k, int grid, hipStream_t st) {
-    if (d.ctrl)
-        launch_one<RT, BUCKETS, true, false, true, ROWS>(d, k, grid, st);
-    else if (d.adam)
-        launch_one<RT, BUCKETS, true, false, false, ROWS>(d, k, grid, st);
-    else if (d.g_out)
-        launch_one<RT, BUCKETS, false, true, false, ROWS>(d, k, grid, st);
-    else
-        launch_one<RT, BUCKETS, false, false, false, ROWS>(d, k, grid, st);
+    if (d.ctrl) {
+        if (d.tiled) launch_one<RT, BUCKETS, true, false, true, true, ROWS>(d, k, grid, st);
+        else launch_one<RT, BUCKETS, true, false, true, false, ROWS>(d, k, grid, st);
+    } else if (d.adam) {
+        if (d.tiled) launch_one<RT, BUCKETS, true, false, false, true, ROWS>(d, k, grid, st);
+        else launch_one<RT, BUCKETS, true, false, false, false, ROWS>(d, k, grid, st);
+    } else if (d.g_out) {
+        launch_one<RT, BUCKETS, false, true, false, false, ROWS>(d, k, grid, st);
+    } else {
+        launch_one<RT, BUCKETS, false, false, false, false, ROWS>(d, k, grid, st);
+    }
 }
 
 template <typename RT, bool BUCKETS>
@@ -903,7 +977,7 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     if (e != hipSuccess) return e;
     if (d.ctrl) {
         if (d.slot && !d.set_slot[1] && !d.no_restore)
-            return launch_restore(d.ctrl, d.set_p[0], d.set_p[1], d.slot, d.S, st);
+            return launch_restore(d.ctrl, d.set_p[0], d.set_p[1], d.slot, d.S, d.tiled, st);
     } else {
         hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kFinalizeBlock), 0, st,
                            (const Partial*)d.partials, grid, d.stats);
@@ -912,14 +986,35 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
 }
 
 hipError_t launch_restore(const zero_device_state* ctrl, const float* set_p0, const float* set_p1,
-                          uint16_t* slot, int64_t S, hipStream_t st) {
-    hipLaunchKernelGGL(k_restore, dim3(grid_stream(S)), dim3(kBlock), 0, st, ctrl, set_p0, set_p1,
-                       slot, S);
+                          uint16_t* slot, int64_t S, bool tiled, hipStream_t st) {
+    if (tiled)
+        hipLaunchKernelGGL(k_restore<true>, dim3(grid_stream(S)), dim3(kBlock), 0, st, ctrl, set_p0,
+                           set_p1, slot, S);
+    else
+        hipLaunchKernelGGL(k_restore<false>, dim3(grid_stream(S)), dim3(kBlock), 0, st, ctrl, set_p0,
+                           set_p1, slot, S);
     return hipGetLastError();
 }
 
-hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t st) {
-    hipLaunchKernelGGL(k_cast_slot, dim3(grid_stream(S)), dim3(kBlock), 0, st, master, S, slot);
+hipError_t launch_cast_slot(const float* master, int64_t S, bool tiled, uint16_t* slot,
+                            hipStream_t st) {
+    if (tiled)
+        hipLaunchKernelGGL(k_cast_slot<true>, dim3(grid_stream(S)), dim3(kBlock), 0, st, master, S,
+                           slot);
+    else
+        hipLaunchKernelGGL(k_cast_slot<false>, dim3(grid_stream(S)), dim3(kBlock), 0, st, master, S,
+                           slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_convert(bool unpack, float* tiled, float* p, float* m, float* v, int64_t S,
+                                hipStream_t st) {
+    if (unpack)
+        hipLaunchKernelGGL(k_state_convert<true>, dim3(grid_stream(S)), dim3(kBlock), 0, st, tiled, p,
+                           m, v, S);
+    else
+        hipLaunchKernelGGL(k_state_convert<false>, dim3(grid_stream(S)), dim3(kBlock), 0, st, tiled,
+                           p, m, v, S);
     return hipGetLastError();
 }
 

@@ -43,6 +43,12 @@ inline int64_t grid_bound(int64_t S) {
     const int64_t g = trips + kMaxParts;
     return g < kGridMax ? g : kGridMax;
 }
+// Tiled state layout: tiles of kStateTile elements, each [p | m | v].
+constexpr int kStateTileLog2 = 13;
+constexpr int64_t kStateTile = int64_t(1) << kStateTileLog2;
+constexpr int kStateTileQuadsLog2 = kStateTileLog2 - 2;
+constexpr int64_t kStateTileQuads = int64_t(1) << kStateTileQuadsLog2;
+static_assert(kStateTile == ZERO_STATE_TILE, "the tile of the ABI");
 constexpr int kCommitGrid = 512;    // workgroups of the commit / cast kernels
 constexpr int kFinalizeBlock = 256;
 
@@ -100,13 +106,19 @@ struct StepDesc {
                                     // whole step); > 0: collect slots [0, n) and commit;
                                     // < 0: publish only (a part before the last)
     bool no_restore;                // single slot: leave the restore kernel to the caller
+    bool tiled;                     // state sets in the tiled layout (m, v pointers unused)
     int max_grid;                   // cap on the workgroups (0: kGridMax)
 };
 
 int rows_for(int32_t n_rep);
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid = 0);
 hipError_t launch_step(const StepDesc& d, hipStream_t stream);
-hipError_t launch_cast_slot(const float* master, int64_t S, uint16_t* slot, hipStream_t stream);
+hipError_t launch_cast_slot(const float* master, int64_t S, bool tiled, uint16_t* slot,
+                            hipStream_t stream);
+// Split p, m, v [S] <-> one tiled set buffer (unpack: tiled -> split; NULL
+// destinations skipped).
+hipError_t launch_state_convert(bool unpack, float* tiled, float* p, float* m, float* v, int64_t S,
+                                hipStream_t stream);
 // Stage-3 fetch (gather_kernels.hip), over at most kGatherMaxShards shards.
 constexpr int kGatherMaxShards = 256;
 hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S, int32_t elem_bytes,
@@ -115,7 +127,7 @@ hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S,
 // After a device-committed step with a single slot: recast the slot from the
 // current master if the step was skipped (no-op kernel otherwise).
 hipError_t launch_restore(const zero_device_state* ctrl, const float* set_p0, const float* set_p1,
-                          uint16_t* slot, int64_t S, hipStream_t stream);
+                          uint16_t* slot, int64_t S, bool tiled, hipStream_t stream);
 // Write rec to *s and clear the workspace (ws_bytes / 8 words), on st.
 hipError_t launch_state_write(zero_device_state* s, const zero_device_state& rec, void* ws,
                               size_t ws_bytes, hipStream_t st);

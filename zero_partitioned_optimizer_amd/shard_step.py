@@ -157,20 +157,35 @@ class DeviceShardStep:
                  lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
                  loss_scale: float = 1.0, dynamic: bool = False, min_loss_scale: float = 1.0,
                  slot: Optional[torch.Tensor] = None, buckets: Optional[torch.Tensor] = None,
-                 n_buckets: int = 0, double_slot: bool = False):
+                 n_buckets: int = 0, double_slot: bool = False,
+                 state_layout: int = B.ZERO_STATE_SPLIT):
         """double_slot: keep a second slot buffer so that the candidate bf16 values
         land in the non-current one and a skipped step needs no restore kernel;
         ``slot`` is then the pair's first buffer and ``current_slot()`` the
-        committed one."""
+        committed one. state_layout: ZERO_STATE_SPLIT keeps p, m, v of each set in
+        three arrays (``self.p[k]``, ``self.m[k]``, ``self.v[k]``);
+        ZERO_STATE_TILED keeps each set in one tiled buffer (``self.sets[k]``)."""
         dev = p0.device
         S = int(shard_S)
         assert p0.dtype == torch.float32 and p0.numel() == S and p0.is_contiguous()
         self.S, self.N, self.grad_dtype = S, int(n_replicas), int(grad_dtype)
         self.lr, self.eps, self.weight_decay = float(lr), float(eps), float(weight_decay)
         self.double_slot = bool(double_slot)
-        self.p = [p0.clone(), torch.zeros_like(p0)]
-        self.m = [torch.zeros_like(p0), torch.zeros_like(p0)]
-        self.v = [torch.zeros_like(p0), torch.zeros_like(p0)]
+        self.tiled = int(state_layout) == B.ZERO_STATE_TILED
+        assert int(state_layout) in (B.ZERO_STATE_SPLIT, B.ZERO_STATE_TILED)
+        if self.tiled:
+            n = B.zero_state_set_floats(S, B.ZERO_STATE_TILED)
+            self.sets = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(2)]
+            zm, zv = torch.zeros_like(p0), torch.zeros_like(p0)
+            B.zero_state_pack(p0, zm, zv, S, self.sets[0])
+            torch.cuda.current_stream(dev).synchronize()
+            del zm, zv
+            self.p = self.m = self.v = None
+        else:
+            self.sets = None
+            self.p = [p0.clone(), torch.zeros_like(p0)]
+            self.m = [torch.zeros_like(p0), torch.zeros_like(p0)]
+            self.v = [torch.zeros_like(p0), torch.zeros_like(p0)]
         self.slot = slot if slot is not None else torch.empty(S, dtype=torch.int16, device=dev)
         assert self.slot.numel() == S and self.slot.element_size() == 2
         self.slot_alt = torch.zeros(S, dtype=torch.int16, device=dev) if self.double_slot else None
@@ -180,7 +195,7 @@ class DeviceShardStep:
         self.ws = torch.empty(B.zero_workspace_bytes(S), dtype=torch.uint8, device=dev)
         B.zero_device_state_init(self.record, self.ws, beta1, beta2, loss_scale, min_loss_scale,
                                  dynamic)
-        B.zero_gather_slot(self.p[0], S, self.slot)
+        self._cast_slot(0, self.slot)
         self._args = None
         self._args_key = None
 
@@ -188,12 +203,18 @@ class DeviceShardStep:
         key = tuple(r.data_ptr() for r in replicas)
         if self._args_key != key:
             slot = (self.slot, self.slot_alt) if self.double_slot else self.slot
+            if self.tiled:
+                p, m, v = self.sets, (None, None), (None, None)
+            else:
+                p, m, v = self.p, self.m, self.v
             self._args = B.make_train_args(replicas=list(replicas), grad_dtype=self.grad_dtype,
-                                           p=self.p, m=self.m, v=self.v, slot=slot,
+                                           p=p, m=m, v=v, slot=slot,
                                            shard_S=self.S, buckets=self.buckets,
                                            n_buckets=self.n_buckets, lr=self.lr, eps=self.eps,
                                            weight_decay=self.weight_decay, state=self.record,
-                                           stats=self.stats, workspace=self.ws)
+                                           stats=self.stats, workspace=self.ws,
+                                           state_layout=B.ZERO_STATE_TILED if self.tiled
+                                           else B.ZERO_STATE_SPLIT)
             self._args_key = key
         a = self._args
         a.lr, a.eps, a.weight_decay = self.lr, self.eps, self.weight_decay
@@ -237,18 +258,49 @@ class DeviceShardStep:
     def last_stats(self) -> B.zero_stats:
         return B.stats_from_tensor(self.stats)
 
+    def _cast_slot(self, k: int, slot: torch.Tensor) -> None:
+        """Cast set k's master into ``slot`` (bf16)."""
+        if self.tiled:
+            B.zero_gather_slot_tiled(self.sets[k], self.S, slot)
+        else:
+            B.zero_gather_slot(self.p[k], self.S, slot)
+
+    def set_state(self, k: int):
+        """(master, m, v) of state set k as flat fp32 tensors: views of the split
+        arrays, or copies unpacked from the tiled buffer (on the current stream)."""
+        if not self.tiled:
+            return self.p[k], self.m[k], self.v[k]
+        out = [torch.empty(self.S, dtype=torch.float32, device=self.sets[k].device)
+               for _ in range(3)]
+        B.zero_state_unpack(self.sets[k], self.S, *out)
+        return tuple(out)
+
+    def set_state_at(self, k: int, idx: torch.Tensor):
+        """(master, m, v) of state set k at the element indices ``idx`` (an int64
+        device tensor), without unpacking the whole set."""
+        if not self.tiled:
+            return self.p[k][idx], self.m[k][idx], self.v[k][idx]
+        T = B.ZERO_STATE_TILE
+        base = (idx // T) * (3 * T) + idx % T
+        s = self.sets[k]
+        return s[base], s[base + T], s[base + 2 * T]
+
     def committed(self):
         """(master, m, v) of the committed state (synchronizes)."""
-        c = self.state().cur & 1
-        return self.p[c], self.m[c], self.v[c]
+        return self.set_state(self.state().cur & 1)
+
+    def committed_at(self, idx: torch.Tensor):
+        """(master, m, v) of the committed state at element indices ``idx``
+        (synchronizes)."""
+        return self.set_state_at(self.state().cur & 1, idx)
 
     def state_dict(self) -> dict:
         """The committed state on the host (synchronizes): the record's bytes and
-        the master copy and moments of its current set."""
+        the master copy and moments of its current set, as flat fp32 arrays in
+        either layout."""
         rec = self.state()
-        c = rec.cur & 1
-        return {"record": bytes(rec), "p": self.p[c].cpu(), "m": self.m[c].cpu(),
-                "v": self.v[c].cpu()}
+        p, m, v = self.set_state(rec.cur & 1)
+        return {"record": bytes(rec), "p": p.cpu(), "m": m.cpu(), "v": v.cpu()}
 
     def load_state_dict(self, sd: dict) -> None:
         """Resume from ``state_dict()``: the saved set goes back into the set the
@@ -256,12 +308,19 @@ class DeviceShardStep:
         the slot is cast again from the master copy."""
         rec = B.zero_device_state.from_buffer_copy(sd["record"])
         c = rec.cur & 1
-        for dst, key in ((self.p[c], "p"), (self.m[c], "m"), (self.v[c], "v")):
+        for key in ("p", "m", "v"):
             assert sd[key].numel() == self.S and sd[key].dtype == torch.float32
-            dst.copy_(sd[key])
+        if self.tiled:
+            dev = self.sets[c].device
+            p, m, v = (sd[key].to(dev).contiguous() for key in ("p", "m", "v"))
+            B.zero_state_pack(p, m, v, self.S, self.sets[c])
+            torch.cuda.current_stream(dev).synchronize()
+        else:
+            for dst, key in ((self.p[c], "p"), (self.m[c], "m"), (self.v[c], "v")):
+                dst.copy_(sd[key])
         B.zero_device_state_load(self.record, self.ws, rec)
         slot = self.slot_alt if (self.double_slot and c) else self.slot
-        B.zero_gather_slot(self.p[c], self.S, slot)
+        self._cast_slot(c, slot)
 
     def current_slot(self) -> torch.Tensor:
         """The slot buffer holding the committed bf16 parameters (synchronizes)."""
