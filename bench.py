@@ -19,6 +19,7 @@ step by default (timed launches cost the stream a few microseconds each).
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -59,15 +60,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, state: str):
     """HBM bytes per launch of the step kernel from the committed rocprofv3 counter
-    runs, or None if there are none for this workload or the kernel changed since."""
+    runs, or None if there are none for this workload and state layout or the
+    kernel changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
     if not rec or rec.get("kernel_sha") != kernel_source_hash():
+        return None
+    if rec.get("state", "split") != state:
         return None
     return rec.get("bytes_per_launch")
 
@@ -480,6 +484,10 @@ def main() -> int:
     ap.add_argument("--commit", default="device", choices=["device", "host"],
                     help="device: commit kernel, no host round trip per step; host: read the "
                          "stats back and apply the commit rule on the host every step")
+    ap.add_argument("--state", default="tiled", choices=["tiled", "split"],
+                    help="fp32 state layout of the device-commit step: one tiled buffer per "
+                         "state set (p, m, v in tiles of 8192 elements) or three arrays "
+                         "(the host commit always uses three arrays)")
     ap.add_argument("--single-slot", action="store_true",
                     help="device commit with one slot buffer (restore kernel after an overflow) "
                          "instead of a double-buffered slot")
@@ -583,11 +591,20 @@ def main() -> int:
     kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.wd,
               loss_scale=w.loss_scale, dynamic=w.dynamic_loss_scale, buckets=buckets_t,
               n_buckets=nb)
+    state = args.state if args.commit == "device" else "split"
     if args.commit == "device":
-        step = Z.DeviceShardStep(S, w.N, gdt, p0, double_slot=not args.single_slot, **kw)
+        step = Z.DeviceShardStep(S, w.N, gdt, p0, double_slot=not args.single_slot,
+                                 state_layout=Z.ZERO_STATE_TILED if state == "tiled"
+                                 else Z.ZERO_STATE_SPLIT, **kw)
     else:
         step = Z.ShardStep(S, w.N, gdt, p0, **kw)
     torch.cuda.synchronize()
+    # Python's generation-2 garbage collection walks every object torch and numpy
+    # created (tens of milliseconds) and fires after a count of allocations, so
+    # sooner or later inside the step loop; collect once now and move what exists
+    # out of its reach
+    gc.collect()
+    gc.freeze()
     if args.overlap:
         return overlap_bench(args, Z, w, S, reps, p0, kw, gdt)
     if args.offload:
@@ -644,7 +661,7 @@ def main() -> int:
     # the committed counter runs cover the default launch of each workload: device
     # commit, whole shard, fp32 fold; other launches report no traffic
     default_launch = not wire and args.commit == "device" and not args.bucket_elems
-    traffic = measured_traffic(w.name) if default_launch else None
+    traffic = measured_traffic(w.name, state) if default_launch else None
     out = {
         "metric": METRIC,
         "value": S * K / elapsed,
@@ -661,7 +678,8 @@ def main() -> int:
         "config": {"workload": f"{w.name} shard, rank {args.rank} of N={w.N}", "shard_elems": S,
                    "n_replicas": w.N, "grad_dtype": w.grad_dtype, "state_dtype": "f32",
                    "bytes_per_elem": bpe, "bucket_elems": args.bucket_elems,
-                   "commit": args.commit, "fold": args.fold, "mall_flushed": bool(args.flush_mall),
+                   "commit": args.commit, "state": state, "fold": args.fold,
+                   "mall_flushed": bool(args.flush_mall),
                    "slot": "single" if (args.single_slot or args.commit == "host") else "double",
                    "seed": w.seed},
         "step_gbps": S * bpe / (elapsed / K) / 1e9,
