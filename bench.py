@@ -709,8 +709,10 @@ def main() -> int:
         hp = json.loads(res.stdout.strip().splitlines()[-1])
         mix = "mix_2to1" if bpe - 26 <= 2 * 14 else "mix_5to1"
         hp["step_kernel_vs_" + mix] = achieved / hp[mix]
-        if "step_shape" in hp:
-            hp["step_kernel_vs_step_shape"] = achieved / hp["step_shape"]["gbps"]
+        key = "step_shape_tiled" if state == "tiled" else "step_shape"
+        if key in hp:
+            hp["step_kernel_vs_step_shape"] = achieved / hp[key]["gbps"]
+            hp["step_shape_layout"] = state
         out["hbm_probe"] = hp
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)

@@ -9,7 +9,9 @@
 // Given a shard size S and a replica count N as well, it also times a stream of
 // the fused step's own shape at that size: N bf16 replica reads (dwordx2), three
 // fp32 reads and three fp32 writes (dwordx4) and one bf16 write (dwordx2) per
-// quad, one quad per lane and one trip per workgroup, with trivial arithmetic.
+// quad, one quad per lane and one trip per workgroup, with trivial arithmetic;
+// once with p, m, v as three arrays per state set and once with each set one
+// buffer of 8192-element tiles [p | m | v] (the step's two state layouts).
 //
 // All buffers hold pseudo-random small normal values, not zeros: streams of
 // zeros run measurably faster on this part, and the step's data is not zero.
@@ -78,7 +80,10 @@ __global__ void __launch_bounds__(kB) k_write(f4* __restrict__ dst, int64_t n4) 
     }
 }
 
-// The step's shape: quad q of this lane, one trip per workgroup.
+// The step's shape: quad q of this lane, one trip per workgroup. TILED: p, m, v
+// point at one set buffer (m, v one and two 2048-quad sections after p) and the
+// quad's state index is (q / 2048) * 6144 + q % 2048.
+template <bool TILED>
 __global__ void __launch_bounds__(kB) k_step_shape(const u2* const* __restrict__ rep, int n_rep,
                                                  const f4* __restrict__ p, const f4* __restrict__ m,
                                                  const f4* __restrict__ v, f4* __restrict__ po,
@@ -86,9 +91,10 @@ __global__ void __launch_bounds__(kB) k_step_shape(const u2* const* __restrict__
                                                  u2* __restrict__ slot, int64_t nq) {
     const int64_t q = (int64_t)blockIdx.x * kB + threadIdx.x;
     if (q >= nq) return;
-    const f4 a = __builtin_nontemporal_load(p + q);
-    const f4 b = __builtin_nontemporal_load(m + q);
-    const f4 c = __builtin_nontemporal_load(v + q);
+    const int64_t s = TILED ? (q >> 11) * 6144 + (q & 2047) : q;
+    const f4 a = __builtin_nontemporal_load(p + s);
+    const f4 b = __builtin_nontemporal_load(m + s);
+    const f4 c = __builtin_nontemporal_load(v + s);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < n_rep; j += 8) {
         u2 r[8];
@@ -104,9 +110,9 @@ __global__ void __launch_bounds__(kB) k_step_shape(const u2* const* __restrict__
             }
         }
     }
-    __builtin_nontemporal_store(a + acc, po + q);
-    __builtin_nontemporal_store(b * acc, mo + q);
-    __builtin_nontemporal_store(c - acc, vo + q);
+    __builtin_nontemporal_store(a + acc, po + s);
+    __builtin_nontemporal_store(b * acc, mo + s);
+    __builtin_nontemporal_store(c - acc, vo + s);
     const f4 n = a - acc;
     u2 w;
     w.x = (__float_as_uint(n.x) >> 16) | (__float_as_uint(n.y) & 0xffff0000u);
@@ -204,10 +210,22 @@ int main(int argc, char** argv) {
         CK(hipMalloc(&rtab, sizeof(u2*) * shape_N));
         CK(hipMemcpy(rtab, reps.data(), sizeof(u2*) * shape_N, hipMemcpyHostToDevice));
         CK(hipGetLastError());
+        // tiled state sets: 3 * S rounded up to whole 8192-element tiles, in floats
+        const int64_t tiled_floats = 3 * ((shape_S + 8191) / 8192) * 8192;
+        f4* ts[2];
+        for (auto& x : ts) {
+            CK(hipMalloc(&x, tiled_floats * 4));
+            hipLaunchKernelGGL(k_fill, 4096, kB, 0, 0, reinterpret_cast<uint32_t*>(x), tiled_floats, seed++);
+        }
+        CK(hipGetLastError());
         const int64_t sgrid = (nq + kB - 1) / kB;
         const double t_shape = time_it([&] {
-            hipLaunchKernelGGL(k_step_shape, dim3((unsigned)sgrid), kB, 0, 0, rtab, shape_N, st[0], st[1],
-                               st[2], st[3], st[4], st[5], slot, nq);
+            hipLaunchKernelGGL(k_step_shape<false>, dim3((unsigned)sgrid), kB, 0, 0, rtab, shape_N, st[0],
+                               st[1], st[2], st[3], st[4], st[5], slot, nq);
+        });
+        const double t_tiled = time_it([&] {
+            hipLaunchKernelGGL(k_step_shape<true>, dim3((unsigned)sgrid), kB, 0, 0, rtab, shape_N, ts[0],
+                               ts[0] + 2048, ts[0] + 4096, ts[1], ts[1] + 2048, ts[1] + 4096, slot, nq);
         });
         CK(hipGetLastError());
         CK(hipDeviceSynchronize());
@@ -215,8 +233,11 @@ int main(int argc, char** argv) {
         printf(", \"step_shape\": {\"shard_elems\": %lld, \"n_replicas\": %d, \"bytes\": %.0f, "
                "\"us\": %.2f, \"gbps\": %.1f}",
                (long long)shape_S, shape_N, sb, t_shape * 1e6, sb / t_shape / 1e9);
+        printf(", \"step_shape_tiled\": {\"us\": %.2f, \"gbps\": %.1f}", t_tiled * 1e6,
+               sb / t_tiled / 1e9);
         for (auto& r : reps) CK(hipFree(r));
         for (auto& x : st) CK(hipFree(x));
+        for (auto& x : ts) CK(hipFree(x));
         CK(hipFree(slot));
         CK(hipFree(rtab));
     }
