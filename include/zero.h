@@ -202,13 +202,15 @@ typedef struct {
 
 /*
  * Bytes of device workspace a reduce, Adam or train-step call on a shard of
- * shard_S elements needs: 24 bytes of fp64 partials per workgroup, for one
- * workgroup per 1,024 elements plus one per part of a split step (at most
- * 4,096), capped at 4,194,304 workgroups (about 20 MB for a 842M-element shard),
- * plus 8 KB + 16 at the end for the device table of replica pointers that a call
- * with more than 256 replicas uses (the first 256 pointers travel in the kernel
- * arguments). The same workspace may be reused by consecutive calls on one
- * stream; calls that run concurrently need their own.
+ * shard_S elements needs. Per workgroup slot (one workgroup per 1,024 elements
+ * plus one per part of a split step, at most 4,096, capped at 4,194,304 slots):
+ * 24 bytes of fp64 partials for a host-commit call; for a device-committed
+ * record 56 bytes (the partials of two consecutive steps and a start mark, about
+ * 46 MB for a 842M-element shard) and 64 bytes of flag words. At the end, 8 KB +
+ * 16 for the device table of replica pointers that a call with more than 256
+ * replicas uses (the first 256 pointers travel in the kernel arguments). The
+ * same workspace may be reused by consecutive calls on one stream; calls that
+ * run concurrently need their own.
  */
 size_t zero_workspace_bytes(int64_t shard_S);
 
@@ -367,12 +369,17 @@ int zero_commit_rule(zero_train_state* state, const zero_stats* stats_host);
 /* ------------------------------------------------------------------------ */
 
 /*
- * The committed-state record of one rank's shard, in device memory (88 bytes,
- * 16-byte aligned, caller-owned). zero_train_step reads it to pick the current
- * state set, t, the loss scale and beta^t, and the step's own commit (workgroup
- * 0 of the step kernel, after every partial is in) updates it, so consecutive
- * steps need no host synchronization (and can be graph-captured).
- * The host may copy it back at any time after synchronizing the stream.
+ * The committed-state record of one rank's shard, in device memory (96 bytes,
+ * 16-byte aligned, caller-owned). It holds the state after its `seq` finalized
+ * steps. The step that a zero_train_step runs is not folded into the record by
+ * its own launch but by the next one (or by zero_device_state_flush): until then
+ * it is pending (pending_n > 0), its overflow flag and partial sums in the
+ * workspace. Every launch derives the committed state from the record and the
+ * pending step's flag with the skip rule of zero_commit_rule, so consecutive
+ * steps need no host synchronization and no launch waits for its own last
+ * workgroup (and steps can be graph-captured). To read the record on the host,
+ * enqueue zero_device_state_flush, synchronize, then copy it: the flushed record
+ * describes every step enqueued before the flush, and so do the stats.
  */
 typedef struct {
     double beta1, beta2;           /* fixed for the life of the record */
@@ -385,7 +392,10 @@ typedef struct {
     uint32_t cur;                  /* 0/1: which state set holds the committed state */
     uint32_t dynamic;              /* nonzero: halve the loss scale on overflow */
     uint32_t last_overflow;
-    uint32_t seq;                  /* steps run on this record (committed or skipped) */
+    uint32_t seq;                  /* steps folded into this record (committed or skipped) */
+    uint32_t pending_n;            /* > 0: one more step has run and awaits folding in (its
+                                      partial count); 0 after init, load and flush */
+    uint32_t reserved;
 } zero_device_state;
 
 /*
@@ -422,6 +432,18 @@ int zero_device_state_init(zero_device_state* state_dev, void* workspace_dev, si
 int zero_device_state_load(zero_device_state* state_dev, void* workspace_dev, size_t ws_bytes,
                            const zero_device_state* saved, void* stream);
 
+/*
+ * Fold the pending step of a device-committed record into it (one small kernel
+ * on `stream`): t, the loss scale, beta^t, the current set, n_skipped,
+ * last_overflow and last_sumsq then describe every step enqueued before the
+ * flush, and *stats_dev holds that last step's overflow flag, bucket count and
+ * squared norm. No-op if nothing is pending. The workspace must be the record's.
+ * Errors: ZERO_E_INVAL (NULL, overlapping buffers), ZERO_E_ALIGN, ZERO_E_RANGE
+ * (workspace too small for any step), ZERO_E_HIP.
+ */
+int zero_device_state_flush(zero_device_state* state_dev, zero_stats* stats_dev, void* workspace_dev,
+                            size_t ws_bytes, void* stream);
+
 typedef struct {
     const void* const* replicas;   /* host array of n_replicas device pointers, slot order */
     int32_t n_replicas;
@@ -451,17 +473,21 @@ typedef struct {
 /*
  * One whole step of this rank's shard with the commit on the device: the fused
  * pass of zero_adam_step (fold in slot order, average and unscale, overflow flag
- * and squared norm, Adam/AdamW, bf16 slot), reading set state->cur and writing
- * the other set; every workgroup leaves a partial tagged with the step's number
- * in the workspace, and workgroup 0 waits for all of them, folds them in
- * workgroup order and applies the skip rule of zero_commit_rule to *state_dev
- * (clean: t += 1 and the written set becomes current; overflow: nothing
- * committed, dynamic loss scale halved). The wait is bounded (2 s); should it run
- * out, which a correct launch never does, nothing is committed and the stats
- * read overflow = 1, bad_buckets = 0xFFFFFFFF. The workspace must be the one
- * given to zero_device_state_init. With a single slot the candidate bf16 values
- * go straight into it and a second kernel restores it from the current master
- * after an overflow;
+ * and squared norm, Adam/AdamW, bf16 slot), reading the committed set and writing
+ * the other set. Every workgroup first derives the committed state from the
+ * record and the previous step's overflow flag (the skip rule of
+ * zero_commit_rule: clean -> t += 1 and the written set became current;
+ * overflow -> nothing committed, dynamic loss scale halved), leaves a start mark,
+ * and at its end a partial tagged with the step's number (and the step's flag
+ * word if it saw a non-finite gradient). Workgroup 0 sums the previous step's
+ * partials in workgroup order and, once every workgroup of the launch has left
+ * its start mark, folds that step into *state_dev; this step stays pending until
+ * the next step or zero_device_state_flush. The waits are bounded (2 s); should
+ * one run out, which a correct launch never does, the stats read overflow = 1,
+ * bad_buckets = 0xFFFFFFFF. The workspace must be the one given to
+ * zero_device_state_init, of at least zero_workspace_bytes(shard_S) bytes. With
+ * a single slot the candidate bf16 values go straight into it and a second kernel
+ * restores it from the committed master after an overflow;
  * with a double-buffered slot the candidate goes into slot[1 - cur] and the
  * commit flips it with the state sets, so a step is one kernel. Same arithmetic
  * as zero_adam_step, bit for bit.

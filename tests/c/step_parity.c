@@ -131,6 +131,7 @@ int main(void) {
         a.workspace_dev = ws_d;
         a.ws_bytes = ws;
         ZCK(zero_train_step(&a, NULL));
+        ZCK(zero_device_state_flush(rec_d, stats_d, ws_d, ws, NULL));
 
         const void* hr[N];
         for (int j = 0; j < N; ++j) hr[j] = reps_h[s][j];

@@ -76,7 +76,7 @@ class zero_device_state(ctypes.Structure):
     _fields_ = [("beta1", f64), ("beta2", f64), ("beta1_pow", f64), ("beta2_pow", f64),
                 ("loss_scale", f64), ("min_loss_scale", f64), ("last_sumsq", f64),
                 ("t", i64), ("n_skipped", i64), ("cur", u32), ("dynamic", u32),
-                ("last_overflow", u32), ("seq", u32)]
+                ("last_overflow", u32), ("seq", u32), ("pending_n", u32), ("reserved", u32)]
 
 
 class zero_train_args(ctypes.Structure):
@@ -104,7 +104,7 @@ class zero_offload_args(ctypes.Structure):
                 ("reserved", i32), ("stream_h2d", vp)]
 
 
-assert ctypes.sizeof(zero_device_state) == 88
+assert ctypes.sizeof(zero_device_state) == 96
 assert ctypes.sizeof(zero_bucket) == 16 and ctypes.sizeof(zero_stats) == 16
 assert ctypes.sizeof(zero_segment) == 32
 
@@ -143,6 +143,7 @@ def lib() -> ctypes.CDLL:
     L.zero_commit_rule.argtypes = [P(zero_train_state), P(zero_stats)]
     L.zero_device_state_init.argtypes = [vp, vp, sz, f64, f64, f64, f64, i32, vp]
     L.zero_device_state_load.argtypes = [vp, vp, sz, P(zero_device_state), vp]
+    L.zero_device_state_flush.argtypes = [vp, vp, vp, sz, vp]
     L.zero_train_step.argtypes = [P(zero_train_args), vp]
     L.zero_train_step_part.argtypes = [P(zero_train_args), vp, i32, i32, vp]
     L.zero_gather_tensors.argtypes = [P(vp), i32, i64, i32, P(i64), P(i64), P(vp), i32, vp]
@@ -157,7 +158,7 @@ def lib() -> ctypes.CDLL:
                  "zero_layout_mem_bytes", "zero_reduce_shard", "zero_adam_step",
                  "zero_gather_slot", "zero_gather_slot_tiled", "zero_state_pack",
                  "zero_state_unpack", "zero_commit_rule", "zero_device_state_init",
-                 "zero_device_state_load", "zero_train_step", "zero_train_step_part",
+                 "zero_device_state_load", "zero_device_state_flush", "zero_train_step", "zero_train_step_part",
                  "zero_host_adam", "zero_offload_step", "zero_gather_tensors"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -370,6 +371,12 @@ def zero_device_state_load(state, workspace, saved: zero_device_state, stream=No
                                         _stream(stream)))
 
 
+def zero_device_state_flush(state, stats, workspace, stream=None) -> None:
+    ws = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    _check(lib().zero_device_state_flush(_addr(state), _addr(stats), _addr(workspace), ws,
+                                         _stream(stream)))
+
+
 def make_train_args(*, replicas, grad_dtype: int, p, m, v, slot=None, shard_S: int, buckets=None,
                     n_buckets: int = 0, lr: float, eps: float, weight_decay: float, state, stats,
                     workspace, event_begin=None, event_end=None,
@@ -474,7 +481,7 @@ def zero_train_step_part(args: zero_train_args, table, n_parts: int, part: int, 
 
 
 def device_state_from_tensor(t) -> zero_device_state:
-    """Read a device zero_device_state (uint8 tensor of 88+ bytes) to the host (synchronizes)."""
+    """Read a device zero_device_state (uint8 tensor of 96+ bytes) to the host (synchronizes)."""
     raw = bytes(t.detach().to("cpu").numpy().tobytes())[: ctypes.sizeof(zero_device_state)]
     return zero_device_state.from_buffer_copy(raw)
 

@@ -207,8 +207,10 @@ const char* zero_last_error(void) { return zl::g_err.c_str(); }
 const char* zero_version(void) { return "libzero 1.0 (gfx950)"; }
 
 size_t zero_workspace_bytes(int64_t shard_S) {
-    return (size_t)zk::grid_bound(shard_S) * zk::kPartialBytes +
-           zk::rep_table_bytes(ZERO_MAX_REPLICAS);
+    // the device-commit layout (CommitWs) is the larger one; a host-commit call
+    // uses its first grid * kPartialBytes bytes and the pointer table at the end
+    return (size_t)zk::grid_bound(shard_S) * zk::kCommitSlotBytes + zk::kFlagBytes +
+           zk::kRepTableMax;
 }
 
 int zero_reduce_shard(const void* const* replicas, int32_t n_replicas, zero_dtype grad_dtype,
@@ -465,11 +467,48 @@ int zero_device_state_load(zero_device_state* state_dev, void* workspace_dev, si
                   r.beta2_pow);
         return ZERO_E_INVAL;
     }
+    if (r.pending_n != 0u) {
+        set_error("%s: the saved record has a pending step (pending_n=%u): flush before saving", fn,
+                  r.pending_n);
+        return ZERO_E_INVAL;
+    }
     zero_device_state rec = r;
     rec.dynamic = r.dynamic ? 1u : 0u;
     rec.seq = 0u;                    // the cleared workspace holds no tag of an earlier step
+    rec.reserved = 0u;
     return hip_status(zk::launch_state_write(state_dev, rec, workspace_dev, ws_bytes,
                                              static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+int zero_device_state_flush(zero_device_state* state_dev, zero_stats* stats_dev, void* workspace_dev,
+                            size_t ws_bytes, void* stream) {
+    static const char* fn = "zero_device_state_flush";
+    int rc = check_record_buffers(fn, state_dev, workspace_dev, ws_bytes);
+    if (rc) return rc;
+    if (!stats_dev) {
+        set_error("%s: stats_dev is NULL", fn);
+        return ZERO_E_INVAL;
+    }
+    if (!aligned16(stats_dev)) {
+        set_error("%s: stats_dev is not 16-byte aligned", fn);
+        return ZERO_E_ALIGN;
+    }
+    const zk::CommitWs cw = zk::commit_ws(workspace_dev, ws_bytes);
+    if (cw.cap < 1) {
+        set_error("%s: ws_bytes=%zu is smaller than any step's workspace", fn, ws_bytes);
+        return ZERO_E_RANGE;
+    }
+    const Span b[] = {span("state", state_dev, (int64_t)sizeof(zero_device_state)),
+                      span("stats", stats_dev, 16),
+                      span("workspace", workspace_dev, (int64_t)ws_bytes)};
+    for (int i = 0; i < 3; ++i)
+        for (int k = i + 1; k < 3; ++k)
+            if (overlap(b[i], b[k])) {
+                set_error("%s: %s and %s overlap", fn, b[i].name, b[k].name);
+                return ZERO_E_INVAL;
+            }
+    return hip_status(zk::launch_flush(state_dev, stats_dev, cw, static_cast<hipStream_t>(stream)),
                       fn);
 }
 
@@ -584,6 +623,11 @@ static zk::StepDesc train_desc(const zero_train_args& a) {
     d.sc.decay = (float)(1.0 - a.lr * a.weight_decay);
     d.stats = a.stats_dev;
     d.partials = static_cast<zk::Partial*>(a.workspace_dev);
+    const zk::CommitWs cw = zk::commit_ws(a.workspace_dev, a.ws_bytes);
+    d.ws_half[0] = cw.half[0];
+    d.ws_half[1] = cw.half[1];
+    d.ws_started = cw.started;
+    d.ws_flags = cw.flags;
     d.ev_begin = static_cast<hipEvent_t>(a.event_begin);
     d.ev_end = static_cast<hipEvent_t>(a.event_end);
     return d;
@@ -593,6 +637,14 @@ int zero_train_step(const zero_train_args* args, void* stream) {
     static const char* fn = "zero_train_step";
     const int rc = check_train_args(fn, args);
     if (rc) return rc;
+    const zero_train_args& a = *args;
+    const int64_t cap = zk::commit_ws(a.workspace_dev, a.ws_bytes).cap;
+    const int grid = zk::grid_for(a.shard_S, a.n_buckets, a.n_replicas);
+    if (cap < grid) {
+        set_error("%s: ws_bytes=%zu holds %lld workgroup slots of a device-committed step, %d "
+                  "needed (zero_workspace_bytes)", fn, a.ws_bytes, (long long)cap, grid);
+        return ZERO_E_RANGE;
+    }
     const zk::StepDesc d = train_desc(*args);
     return hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
 }
@@ -638,10 +690,10 @@ int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, 
         total += g;
         prev = e;
     }
-    const int64_t need = total * (int64_t)zk::kPartialBytes + (int64_t)zk::rep_table_bytes(a.n_replicas);
-    if (need > (int64_t)a.ws_bytes || total > INT32_MAX) {
-        set_error("%s: the %d parts need %lld workspace bytes, ws_bytes=%zu", fn, (int)n_parts,
-                  (long long)need, a.ws_bytes);
+    const int64_t cap = zk::commit_ws(a.workspace_dev, a.ws_bytes).cap;
+    if (total > cap || total > INT32_MAX) {
+        set_error("%s: the %d parts need %lld workgroup slots, ws_bytes=%zu holds %lld", fn,
+                  (int)n_parts, (long long)total, a.ws_bytes, (long long)cap);
         return ZERO_E_RANGE;
     }
     const int64_t lo = part == 0 ? 0 : part_ends[part - 1], hi = part_ends[part];
@@ -670,7 +722,8 @@ int zero_train_step_part(const zero_train_args* args, const int64_t* part_ends, 
     d.no_restore = true;
     rc = hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
     if (rc || !last || !a.slot[0] || a.slot[1]) return rc;
-    return hip_status(zk::launch_restore(a.state_dev, a.p[0], a.p[1], a.slot[0], S, tiled,
+    return hip_status(zk::launch_restore(a.state_dev, zk::commit_ws(a.workspace_dev, a.ws_bytes).flags,
+                                         a.p[0], a.p[1], a.slot[0], S, tiled,
                                          static_cast<hipStream_t>(stream)),
                       fn);
 }

@@ -80,6 +80,9 @@ struct KParams {
     uint16_t* slot;
     float* g_out;
     Partial* partials;
+    uint64_t* ws_half[2];                   // device commit: tagged partials, by step number parity
+    uint64_t* ws_started;                   // device commit: start marks, one per workgroup slot
+    uint64_t* ws_flags;                     // device commit: overflow flag words, by step number parity
     Scalars sc;
 };
 
@@ -93,7 +96,9 @@ struct Res {
     float* m_out;
     float* v_out;
     uint16_t* slot;                         // where the bf16 result goes, or nullptr
-    uint32_t tag;                           // device-commit: number of this step (record seq + 1)
+    uint32_t tag;                           // device-commit: number of this step
+    uint64_t mark;                          // device-commit: start mark (tag, and a checksum of the
+                                            // record words read, so it waits for all of them)
 };
 
 // ---------------------------------------------------------------------------
@@ -327,6 +332,90 @@ __device__ __forceinline__ void fold(const KParams& a, int64_t q0, int64_t qs, f
 // launches read the committed state's record: which state set is current, the
 // loss scale and beta^t; each workgroup derives the update's scalars from it
 // with the same double operations, rounded once to fp32, that the host uses.
+// Relaxed agent-scope loads: coherent across XCDs, for words that other
+// workgroups of the same launch write (partials, start marks).
+__device__ __forceinline__ uint32_t rd32(const uint32_t* p) {
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t rd64(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double rdf64(const double* p) {
+    return __longlong_as_double((long long)rd64(reinterpret_cast<const uint64_t*>(p)));
+}
+__device__ __forceinline__ uint32_t fold32(uint64_t x) { return (uint32_t)x ^ (uint32_t)(x >> 32); }
+// The record's words are the same in every lane: keep them in scalar registers.
+__device__ __forceinline__ uint32_t uni32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint64_t uni64(uint64_t x) {
+    return ((uint64_t)uni32((uint32_t)(x >> 32)) << 32) | uni32((uint32_t)x);
+}
+
+// The committed state as a launch sees it: the record (state after its `seq`
+// finalized steps) with the pending step -- the one that ran after them, if
+// pending_n > 0 -- folded in by the skip rule: a clean pending step advances the
+// current set and beta^t, an overflowed one halves a dynamic loss scale. Every
+// workgroup derives it from the same words, so all agree; workgroup 0 writes it
+// back into the record later in the launch.
+struct RecView {
+    uint32_t seq, pend, cur, dynamic;
+    uint64_t flag;                          // flag word of the pending step's parity
+    double b1, b2, pow1, pow2, ls, min_ls;  // pow: beta^t of the committed t
+    uint32_t sum;                           // checksum of every word read
+};
+
+// The record and the flag words are read with plain loads: what earlier
+// launches wrote is visible at a launch's start (caches are written back and
+// invalidated between launches), and within a launch workgroup 0 rewrites the
+// record only after every workgroup has posted its start mark, whose value
+// depends on every word read here, so no workgroup can see the new record.
+__device__ __forceinline__ RecView read_record(const zero_device_state* c, const uint64_t* flags) {
+    RecView v;
+    v.seq = uni32(c->seq);
+    v.pend = uni32(c->pending_n);
+    v.cur = uni32(c->cur);
+    v.dynamic = uni32(c->dynamic);
+    const uint64_t b1 = uni64((uint64_t)__double_as_longlong(c->beta1));
+    const uint64_t b2 = uni64((uint64_t)__double_as_longlong(c->beta2));
+    const uint64_t p1 = uni64((uint64_t)__double_as_longlong(c->beta1_pow));
+    const uint64_t p2 = uni64((uint64_t)__double_as_longlong(c->beta2_pow));
+    const uint64_t ls = uni64((uint64_t)__double_as_longlong(c->loss_scale));
+    const uint64_t ml = uni64((uint64_t)__double_as_longlong(c->min_loss_scale));
+    // both flag words, so that neither load waits for seq
+    const uint64_t f0 = uni64(flags[0]), f1 = uni64(flags[1]);
+    v.flag = ((v.seq + 1u) & 1u) ? f1 : f0;
+    v.b1 = __longlong_as_double((long long)b1);
+    v.b2 = __longlong_as_double((long long)b2);
+    v.pow1 = __longlong_as_double((long long)p1);
+    v.pow2 = __longlong_as_double((long long)p2);
+    v.ls = __longlong_as_double((long long)ls);
+    v.min_ls = __longlong_as_double((long long)ml);
+    v.sum = v.seq ^ v.pend ^ v.cur ^ v.dynamic ^ fold32(b1) ^ fold32(b2) ^ fold32(p1) ^ fold32(p2) ^
+            fold32(ls) ^ fold32(ml) ^ fold32(v.flag);
+    v.cur &= 1u;
+    return v;
+}
+
+// Did the pending step overflow? Its workgroups that saw a non-finite gradient
+// stored its number into the flag word of its parity; an older number there is
+// a step two or more back.
+__device__ __forceinline__ bool pending_overflow(const RecView& v) {
+    return v.flag == (uint64_t)(v.seq + 1u);
+}
+
+// The skip rule applied to the pending step (the same operations as the
+// zero_commit_rule of the host).
+__device__ __forceinline__ void apply_pending(RecView& v) {
+    if (!v.pend) return;
+    if (!pending_overflow(v)) {
+        v.cur ^= 1u;
+        v.pow1 = v.pow1 * v.b1;
+        v.pow2 = v.pow2 * v.b2;
+    } else if (v.dynamic) {
+        const double half = v.ls / 2.0;
+        v.ls = half > v.min_ls ? half : v.min_ls;
+    }
+}
+
 template <bool CTRL, bool TILED>
 __device__ __forceinline__ Res resolve(const KParams& a) {
     Res r;
@@ -340,13 +429,18 @@ __device__ __forceinline__ Res resolve(const KParams& a) {
         r.v_out = a.v_out;
         r.slot = a.slot;
         r.tag = 0u;
+        r.mark = 0u;
     } else {
-        const zero_device_state* c = a.ctrl;
-        const uint32_t cur = c->cur & 1u, nxt = cur ^ 1u;
-        const double b1 = c->beta1, b2 = c->beta2;
-        const double pow1 = c->beta1_pow * b1;      // beta^(t+1), one more factor of the product
-        const double pow2 = c->beta2_pow * b2;
-        r.sc.inv = (float)(1.0 / ((double)a.n_rep * c->loss_scale));
+        RecView v = read_record(a.ctrl, a.ws_flags);
+        const uint32_t tag = v.seq + (v.pend ? 2u : 1u);
+        r.tag = tag;
+        r.mark = ((uint64_t)tag << 32) | v.sum;
+        apply_pending(v);
+        const uint32_t cur = v.cur, nxt = cur ^ 1u;
+        const double b1 = v.b1, b2 = v.b2;
+        const double pow1 = v.pow1 * b1;            // beta^(t+1), one more factor of the product
+        const double pow2 = v.pow2 * b2;
+        r.sc.inv = (float)(1.0 / ((double)a.n_rep * v.ls));
         r.sc.b1 = (float)b1;
         r.sc.b2 = (float)b2;
         r.sc.omb1 = (float)(1.0 - b1);
@@ -361,7 +455,6 @@ __device__ __forceinline__ Res resolve(const KParams& a) {
         r.v_out = a.set_v[nxt];
         // a double-buffered slot takes the candidate in the out buffer, like the state
         r.slot = a.set_slot[1] ? a.set_slot[nxt] : a.slot;
-        r.tag = c->seq + 1u;
     }
     if constexpr (TILED) {
         // one buffer per set: m and v sit one and two sections after p in each tile
@@ -543,51 +636,45 @@ __device__ __forceinline__ void block_reduce(double& sq, uint32_t& bad, uint32_t
 // kernels
 // ---------------------------------------------------------------------------
 
-// The commit of a device-resident step (thread 0 of workgroup 0, after it has
-// collected every partial):
-//   clean:    t += 1, beta^t *= beta, the written state set becomes current;
-//   overflow: skipped += 1, a dynamic loss scale halves (not below its floor).
-__device__ __forceinline__ void commit_record(zero_device_state* c, zero_stats* stats, double sq,
-                                              uint32_t bad, uint32_t badb) {
-    const bool overflow = bad != 0u;
-    stats->overflow = overflow ? 1u : 0u;
-    stats->bad_buckets = badb;
-    stats->sumsq = sq;
-    c->last_overflow = overflow ? 1u : 0u;
-    c->last_sumsq = sq;
-    if (!overflow) {
-        c->t = c->t + 1;
-        c->beta1_pow = c->beta1_pow * c->beta1;
-        c->beta2_pow = c->beta2_pow * c->beta2;
-        c->cur = (c->cur & 1u) ^ 1u;
-    } else {
-        c->n_skipped = c->n_skipped + 1;
-        if (c->dynamic) {
-            const double half = c->loss_scale / 2.0;
-            c->loss_scale = half > c->min_loss_scale ? half : c->min_loss_scale;
-        }
-    }
-}
-
-// Workgroup 0 of a device-commit launch: wait for the n tagged partials (this
-// launch's, or those of every part of a step split over several launches on one
-// stream), fold them in slot order (thread t takes partials t, t + 256, ...,
-// then the fixed tree of block_reduce) and commit. The wait is bounded by
-// kCollectTimeout ticks of the 100 MHz real-time counter; if it runs out (which a
-// correct launch never does) nothing is committed and the stats carry the marker
+// Device commit. A launch does not commit its own step: every workgroup leaves
+// its partial (three 64-bit words tagged with the step's number) in the
+// workspace half of that number's parity, and one that finds a non-finite
+// gradient stores the number into the flag word of that parity. The next launch
+// on the record -- or zero_device_state_flush -- folds the step in: its
+// workgroups all derive the committed state from the record and the flag word
+// (apply_pending), and its workgroup 0 sums the pending step's partials (long
+// complete) and rewrites the record once every workgroup of its own launch has
+// read it, which each signals with a start mark. Nobody waits for the last
+// workgroup to finish, and nothing runs after it.
+//
+// Waits are bounded by kCollectTimeout ticks of the 100 MHz real-time counter;
+// if one runs out (which a correct launch never does) the stats carry the marker
 // bad_buckets = 0xFFFFFFFF.
 constexpr uint64_t kCollectTimeout = 200000000ull;   // 2 s
 
-__device__ __forceinline__ void collect_and_commit(const uint64_t* base, int n, zero_stats* stats,
-                                                  zero_device_state* c, uint32_t tag) {
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    bool timed_out = false;
-    double sq = 0.0;
-    uint32_t bad = 0u, badb = 0u;
-    // thread t takes partials t, t + kBlock, t + 2 kBlock, ... in that order, kBatch
-    // at a time: their loads are all in flight before the tags are checked
+// OR of a per-thread flag over the workgroup, in every thread.
+__device__ __forceinline__ uint32_t block_or(uint32_t x) {
+    __shared__ uint32_t s_or[kBlock / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x |= __shfl_xor(x, off, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s_or[threadIdx.x >> 6] = x;
+    __syncthreads();
+    uint32_t r = 0u;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) r |= s_or[w];
+    return r;
+}
+
+// Sum n partials tagged `tag` at `base` in slot order (thread t takes partials t,
+// t + kBlock, ..., kBatch at a time with their loads all in flight; then the
+// fixed tree of block_reduce, which leaves the totals in thread 0). Partials are
+// polled until they carry the tag.
+__device__ __forceinline__ void collect(const uint64_t* base, int n, uint32_t tag, uint64_t t0,
+                                       double& sq, uint32_t& bad, uint32_t& badb, uint32_t& tmo) {
     constexpr int kBatch = 4;
-    for (int b = threadIdx.x; b < n; b += kBatch * kBlock) {
+    bool timed_out = false;
+    for (int b = threadIdx.x; b < n && !timed_out; b += kBatch * kBlock) {
         uint64_t w[kBatch][3];
         uint32_t want = 0u, have = 0u;
 #pragma unroll
@@ -598,9 +685,9 @@ __device__ __forceinline__ void collect_and_commit(const uint64_t* base, int n, 
             for (int k = 0; k < kBatch; ++k) {
                 if (!((want & ~have) >> k & 1u)) continue;
                 const uint64_t* q = base + 3 * (int64_t)(b + k * kBlock);
-                w[k][0] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                w[k][1] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                w[k][2] = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                w[k][0] = rd64(q);
+                w[k][1] = rd64(q + 1);
+                w[k][2] = rd64(q + 2);
             }
 #pragma unroll
             for (int k = 0; k < kBatch; ++k)
@@ -624,31 +711,100 @@ __device__ __forceinline__ void collect_and_commit(const uint64_t* base, int n, 
             badb += (uint32_t)(w[k][2] & 0xffffffffull) >> 1;
         }
     }
-    uint32_t tmo = timed_out ? 1u : 0u;
+    if (timed_out) tmo = 1u;
     block_reduce(sq, bad, badb);
-    // every thread's time-out flag reaches thread 0 through the same tree
-    __shared__ uint32_t s_tmo[kBlock / 64];
+}
+
+// Wait until the n start marks at `marks` carry `tag`: every workgroup of this
+// launch has read the record. Thread t checks marks t, t + kBlock, ..., kBatch at
+// a time with their loads all in flight, re-polling the ones not yet in.
+__device__ __forceinline__ void wait_marks(const uint64_t* marks, int n, uint32_t tag, uint64_t t0,
+                                          uint32_t& tmo) {
+    constexpr int kBatch = 4;
+    for (int b = threadIdx.x; b < n; b += kBatch * kBlock) {
+        uint32_t want = 0u, have = 0u;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) tmo |= __shfl_xor(tmo, off, 64);
-    if ((threadIdx.x & 63) == 0) s_tmo[threadIdx.x >> 6] = tmo;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 0; w < kBlock / 64; ++w) tmo |= s_tmo[w];
+        for (int k = 0; k < kBatch; ++k)
+            if (b + k * kBlock < n) want |= 1u << k;
+        for (;;) {
+            uint64_t w[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                w[k] = ((want & ~have) >> k & 1u) ? rd64(marks + b + k * kBlock) : 0ull;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                if ((uint32_t)(w[k] >> 32) == tag) have |= (want >> k & 1u) << k;
+            if (have == want) break;
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kCollectTimeout) {
+                tmo = 1u;
+                return;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+    }
+}
+
+// Thread 0: fold the pending step into the record (with the squared norm and
+// bucket count summed from its partials) and write its stats; the step that
+// just ran (new_pending partials; 0 for a flush) becomes the pending one.
+__device__ __forceinline__ void fold_pending(zero_device_state* c, zero_stats* stats,
+                                             const uint64_t* flags, double sq, uint32_t badb,
+                                             bool tmo, uint32_t new_pending) {
+    RecView v = read_record(c, flags);
+    if (v.pend) {
+        const bool overflow = pending_overflow(v);
         if (tmo) {
             stats->overflow = 1u;
             stats->bad_buckets = 0xffffffffu;
             stats->sumsq = __longlong_as_double(0x7ff8000000000000ll);
-            c->last_overflow = 1u;
         } else {
-            commit_record(c, stats, sq, bad, badb);
+            stats->overflow = overflow ? 1u : 0u;
+            stats->bad_buckets = badb;
+            stats->sumsq = sq;
         }
-        c->seq = tag;
+        c->last_overflow = overflow ? 1u : 0u;
+        c->last_sumsq = sq;
+        if (!overflow) c->t = c->t + 1;
+        else c->n_skipped = c->n_skipped + 1;
+        apply_pending(v);
+        c->cur = v.cur;
+        c->beta1_pow = v.pow1;
+        c->beta2_pow = v.pow2;
+        c->loss_scale = v.ls;
+        c->seq = v.seq + 1u;
+    } else if (tmo) {
+        stats->overflow = 1u;
+        stats->bad_buckets = 0xffffffffu;
+        stats->sumsq = __longlong_as_double(0x7ff8000000000000ll);
     }
+    c->pending_n = new_pending;
+}
+
+// Workgroup 0 of the launch that ends a step (all its threads): fold the pending
+// step into the record once every workgroup of this launch has read it.
+__device__ __forceinline__ void finalize_launch(const KParams& a, uint32_t tag) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    const zero_device_state* c = a.ctrl;
+    const uint32_t seq = rd32(&c->seq), pend = rd32(&c->pending_n);
+    double sq = 0.0;
+    uint32_t bad = 0u, badb = 0u, tmo = 0u;
+    if (pend) collect(a.ws_half[(seq + 1u) & 1u], (int)pend, seq + 1u, t0, sq, bad, badb, tmo);
+    wait_marks(a.ws_started + a.part_base, (int)gridDim.x, tag, t0, tmo);
+    tmo = block_or(tmo);
+    if (threadIdx.x == 0) fold_pending(a.ctrl_rw, a.stats, a.ws_flags, sq, badb, tmo != 0u,
+                                       (uint32_t)a.collect_n);
 }
 
 template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL, bool TILED, int ROWS>
 __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
     const Res rs = resolve<CTRL, TILED>(a);
+    if constexpr (CTRL) {
+        // this workgroup has read the record (the mark's value depends on every
+        // word it read); workgroup 0 may rewrite it once all marks are in
+        if (threadIdx.x == 0)
+            __hip_atomic_store(a.ws_started + ((int64_t)a.part_base + blockIdx.x), rs.mark,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     double sq = 0.0;
     uint32_t bad = 0u, badb = 0u;
     if constexpr (!BUCKETS) {
@@ -687,26 +843,24 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
     } else {
         // Each workgroup publishes its partial as three 64-bit agent-scope atomic
         // stores (written through to the coherence point all XCDs share), each
-        // word tagged with this step's number, and leaves at once: no wait, no
-        // counter. Workgroup 0 -- dispatched first, so never starved of a CU --
-        // then polls the partials in workgroup order until every word carries the
-        // tag, sums them in that fixed order and commits the record. A word with
-        // an older tag is a partial not yet arrived; 64-bit aligned stores and
-        // loads are single-copy atomic, so no word is ever seen half written.
+        // word tagged with this step's number, in the workspace half of the
+        // number's parity, sets the step's flag word if it saw a non-finite
+        // gradient, and leaves at once. 64-bit aligned stores and loads are
+        // single-copy atomic, so no word is ever seen half written.
         if (threadIdx.x == 0) {
             const uint64_t tag = (uint64_t)rs.tag << 32;
             const uint64_t sqb = (uint64_t)__double_as_longlong(sq);
-            uint64_t* w = reinterpret_cast<uint64_t*>(a.partials) +
-                          3 * ((int64_t)a.part_base + blockIdx.x);
+            uint64_t* w = a.ws_half[rs.tag & 1u] + 3 * ((int64_t)a.part_base + blockIdx.x);
             __hip_atomic_store(w + 0, tag | (sqb >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(w + 1, tag | (sqb & 0xffffffffull), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(w + 2, tag | (uint64_t)((bad ? 1u : 0u) | (badb << 1)), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
+            if (bad)
+                __hip_atomic_store(a.ws_flags + (rs.tag & 1u), (uint64_t)rs.tag, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (blockIdx.x == 0 && a.collect_n > 0)
-            collect_and_commit(reinterpret_cast<const uint64_t*>(a.partials), a.collect_n, a.stats,
-                               a.ctrl_rw, rs.tag);
+        if (blockIdx.x == 0 && a.collect_n > 0) finalize_launch(a, rs.tag);
     }
 }
 
@@ -760,10 +914,29 @@ __global__ void __launch_bounds__(kBlock) k_cast_slot(const float* master, int64
 // on a clean step, exits at once.
 template <bool TILED>
 __global__ void __launch_bounds__(kBlock) k_restore(const zero_device_state* ctrl,
-                                                   const float* set_p0, const float* set_p1,
-                                                   uint16_t* slot, int64_t S) {
-    if (ctrl->last_overflow == 0u) return;
+                                                   const uint64_t* flags, const float* set_p0,
+                                                   const float* set_p1, uint16_t* slot, int64_t S) {
+    // the step just run is pending in the record (or folded in by a flush)
+    const uint32_t seq = ctrl->seq, pend = ctrl->pending_n;
+    const bool overflow = pend ? flags[(seq + 1u) & 1u] == (uint64_t)(seq + 1u)
+                               : ctrl->last_overflow != 0u;
+    if (!overflow) return;
+    // a skipped step leaves the current set of the record current
     cast_range<TILED>((ctrl->cur & 1u) ? set_p1 : set_p0, S, slot);
+}
+
+// zero_device_state_flush: one workgroup folds the pending step into the record.
+__global__ void __launch_bounds__(kBlock) k_flush(zero_device_state* c, zero_stats* stats,
+                                                 const uint64_t* half0, const uint64_t* half1,
+                                                 const uint64_t* flags) {
+    const uint32_t seq = rd32(&c->seq), pend = rd32(&c->pending_n);
+    if (!pend) return;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    double sq = 0.0;
+    uint32_t bad = 0u, badb = 0u, tmo = 0u;
+    collect(((seq + 1u) & 1u) ? half1 : half0, (int)pend, seq + 1u, t0, sq, bad, badb, tmo);
+    tmo = block_or(tmo);
+    if (threadIdx.x == 0) fold_pending(c, stats, flags, sq, badb, tmo != 0u, 0u);
 }
 
 // Conversion between three split arrays p, m, v [S] and one tiled set buffer;
@@ -961,6 +1134,9 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     k.set_slot[1] = d.set_slot[1];
     k.g_out = d.g_out;
     k.partials = d.partials;
+    for (int i = 0; i < 2; ++i) k.ws_half[i] = d.ws_half[i];
+    k.ws_started = d.ws_started;
+    k.ws_flags = d.ws_flags;
     k.sc = d.sc;
     const bool buckets = d.n_buckets > 0;
     const int grid = grid_for(d.S, d.n_buckets, d.n_rep, d.max_grid);
@@ -977,7 +1153,7 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     if (e != hipSuccess) return e;
     if (d.ctrl) {
         if (d.slot && !d.set_slot[1] && !d.no_restore)
-            return launch_restore(d.ctrl, d.set_p[0], d.set_p[1], d.slot, d.S, d.tiled, st);
+            return launch_restore(d.ctrl, d.ws_flags, d.set_p[0], d.set_p[1], d.slot, d.S, d.tiled, st);
     } else {
         hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kFinalizeBlock), 0, st,
                            (const Partial*)d.partials, grid, d.stats);
@@ -985,14 +1161,21 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_restore(const zero_device_state* ctrl, const float* set_p0, const float* set_p1,
-                          uint16_t* slot, int64_t S, bool tiled, hipStream_t st) {
+hipError_t launch_restore(const zero_device_state* ctrl, const uint64_t* flags, const float* set_p0,
+                          const float* set_p1, uint16_t* slot, int64_t S, bool tiled, hipStream_t st) {
     if (tiled)
-        hipLaunchKernelGGL(k_restore<true>, dim3(grid_stream(S)), dim3(kBlock), 0, st, ctrl, set_p0,
-                           set_p1, slot, S);
+        hipLaunchKernelGGL(k_restore<true>, dim3(grid_stream(S)), dim3(kBlock), 0, st, ctrl, flags,
+                           set_p0, set_p1, slot, S);
     else
-        hipLaunchKernelGGL(k_restore<false>, dim3(grid_stream(S)), dim3(kBlock), 0, st, ctrl, set_p0,
-                           set_p1, slot, S);
+        hipLaunchKernelGGL(k_restore<false>, dim3(grid_stream(S)), dim3(kBlock), 0, st, ctrl, flags,
+                           set_p0, set_p1, slot, S);
+    return hipGetLastError();
+}
+
+hipError_t launch_flush(zero_device_state* ctrl, zero_stats* stats, const CommitWs& w,
+                        hipStream_t st) {
+    hipLaunchKernelGGL(k_flush, dim3(1), dim3(kBlock), 0, st, ctrl, stats, w.half[0], w.half[1],
+                       w.flags);
     return hipGetLastError();
 }
 

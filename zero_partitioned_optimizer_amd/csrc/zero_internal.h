@@ -52,6 +52,35 @@ static_assert(kStateTile == ZERO_STATE_TILE, "the tile of the ABI");
 constexpr int kCommitGrid = 512;    // workgroups of the commit / cast kernels
 constexpr int kFinalizeBlock = 256;
 
+// Workspace of a device-committed record: two halves of tagged partials (three
+// 64-bit words per workgroup slot; steps with odd and even numbers alternate, so
+// a launch can fold the previous step's partials while writing its own), one
+// start mark per workgroup slot, the two overflow flag words (by step number
+// parity, padded to 64 bytes), and the replica pointer table reserved at the end.
+// Slots = cap, derived from the workspace size alone, so every launch on a
+// record sees the same layout.
+constexpr size_t kRepTableMax = 8 * (size_t)ZERO_MAX_REPLICAS + 16;
+constexpr size_t kCommitSlotBytes = 2 * 24 + 8;
+constexpr size_t kFlagBytes = 64;
+struct CommitWs {
+    uint64_t* half[2];
+    uint64_t* started;
+    uint64_t* flags;
+    int64_t cap;                    // workgroup slots
+};
+inline CommitWs commit_ws(void* ws, size_t ws_bytes) {
+    CommitWs w{};
+    if (!ws || ws_bytes < kRepTableMax + kFlagBytes) return w;
+    const int64_t cap = (int64_t)((ws_bytes - kRepTableMax - kFlagBytes) / kCommitSlotBytes);
+    uint64_t* b = static_cast<uint64_t*>(ws);
+    w.half[0] = b;
+    w.half[1] = b + 3 * cap;
+    w.started = b + 6 * cap;
+    w.flags = b + 7 * cap;
+    w.cap = cap;
+    return w;
+}
+
 // Per-workgroup partial result of the overflow flag and the squared norm.
 struct Partial {
     double sumsq;
@@ -107,6 +136,9 @@ struct StepDesc {
                                     // < 0: publish only (a part before the last)
     bool no_restore;                // single slot: leave the restore kernel to the caller
     bool tiled;                     // state sets in the tiled layout (m, v pointers unused)
+    uint64_t* ws_half[2];           // device-commit path: the workspace regions of CommitWs
+    uint64_t* ws_started;
+    uint64_t* ws_flags;
     int max_grid;                   // cap on the workgroups (0: kGridMax)
 };
 
@@ -126,8 +158,12 @@ hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S,
                          int32_t n_tensors, hipStream_t stream);
 // After a device-committed step with a single slot: recast the slot from the
 // current master if the step was skipped (no-op kernel otherwise).
-hipError_t launch_restore(const zero_device_state* ctrl, const float* set_p0, const float* set_p1,
-                          uint16_t* slot, int64_t S, bool tiled, hipStream_t stream);
+hipError_t launch_restore(const zero_device_state* ctrl, const uint64_t* flags, const float* set_p0,
+                          const float* set_p1, uint16_t* slot, int64_t S, bool tiled,
+                          hipStream_t stream);
+// Fold the pending step of a device-committed record into it (one workgroup).
+hipError_t launch_flush(zero_device_state* ctrl, zero_stats* stats, const CommitWs& w,
+                        hipStream_t stream);
 // Write rec to *s and clear the workspace (ws_bytes / 8 words), on st.
 hipError_t launch_state_write(zero_device_state* s, const zero_device_state& rec, void* ws,
                               size_t ws_bytes, hipStream_t st);

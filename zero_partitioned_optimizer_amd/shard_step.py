@@ -147,11 +147,12 @@ class ShardStep:
 
 
 class DeviceShardStep:
-    """The same step with the commit on the device (``zero_train_step``): the fused
-    kernel reads the committed-state record, and its workgroup 0 folds every
-    workgroup's partial and applies the skip rule to the record, so steps queue
-    back to back with no host synchronization. The host reads the record (t, loss
-    scale, current set) only when it wants to."""
+    """The same step with the commit on the device (``zero_train_step``): each
+    launch derives the committed state from the record and the previous step's
+    overflow flag, and its workgroup 0 folds the previous step into the record,
+    so steps queue back to back with no host synchronization. The host reads the
+    record (t, loss scale, current set) only when it wants to, after a flush
+    (``state()``, ``last_stats()`` and the methods built on them do that)."""
 
     def __init__(self, shard_S: int, n_replicas: int, grad_dtype: int, p0: torch.Tensor, *,
                  lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
@@ -251,11 +252,18 @@ class DeviceShardStep:
             B.zero_train_step_part(a, self._parts, self._parts_n, k, st)
         a.event_begin = a.event_end = None
 
+    def flush(self, stream=None) -> None:
+        """Enqueue the folding of the last step into the record and the stats."""
+        B.zero_device_state_flush(self.record, self.stats, self.ws, stream)
+
     def state(self) -> B.zero_device_state:
-        """Copy the committed-state record back (synchronizes)."""
+        """Flush, then copy the committed-state record back (synchronizes)."""
+        self.flush()
         return B.device_state_from_tensor(self.record)
 
     def last_stats(self) -> B.zero_stats:
+        """Flush, then copy the last step's stats back (synchronizes)."""
+        self.flush()
         return B.stats_from_tensor(self.stats)
 
     def _cast_slot(self, k: int, slot: torch.Tensor) -> None:
