@@ -514,8 +514,10 @@ int zero_train_step(const zero_train_args* args, void* stream);
  * of 8 elements and part_ends[n_parts - 1] == shard_S (empty parts are allowed).
  * Call part = 0, 1, ..., n_parts - 1 in that order on ONE stream: every part reads
  * the same committed record and leaves tagged partials, and the last part's
- * workgroup 0 collects the partials of all parts (in part, then workgroup order)
- * and commits, as zero_train_step does; with a single slot the restore kernel
+ * workgroup 0 folds the previous step into the record once the last part's
+ * workgroups have read it, as zero_train_step does; the step whose parts these
+ * are then stays pending (its partials, in part then workgroup order, are summed
+ * by the next step or flush); with a single slot the restore kernel
  * follows the last part. p, m, v and the slot come out bit-identical to
  * zero_train_step's; the squared norm is summed in another grouping (equal
  * within rounding). The workspace of zero_workspace_bytes(shard_S) suffices.

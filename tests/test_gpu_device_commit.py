@@ -200,3 +200,42 @@ def test_stale_workspace_from_an_earlier_record(Z):
         check_state(f"record {run}", to_host(P), to_host(M), to_host(V), to_host(step.current_slot()),
                     tr.p, tr.m, tr.v, tr.slot)
         assert step.state().seq == 2
+
+
+@pytest.mark.parametrize("double_slot", [False, True])
+def test_deferred_commit_overflow_on_last_step(Z, double_slot):
+    """A step is folded into the record by the next launch or by a flush. Queue
+    five steps with no host read in between, the last one carrying a +inf: the
+    flush folds that skipped step in (t stays 4, the loss scale halves, the slot
+    holds the committed master), and a second flush changes nothing."""
+    S, N, K = 50_001, 3, 5
+    rng = np.random.default_rng(21)
+    hy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    p0 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    sets = []
+    for k in range(K):
+        reps = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * 1e-3 * 64.0)) for _ in range(N)]
+        if k == K - 1:
+            reps[1][S // 2] = W._bf16_bits_from_f32(np.array([np.inf]))[0]
+        sets.append(reps)
+    step = Z.DeviceShardStep(S, N, Z.ZERO_BF16, to_dev(p0), weight_decay=0.0, loss_scale=64.0,
+                             dynamic=True, double_slot=double_slot, **hy)
+    for reps in sets:
+        step.step([to_dev(r) for r in reps])
+    torch.cuda.synchronize()
+    raw = Z.device_state_from_tensor(step.record)
+    assert raw.pending_n > 0 and raw.seq == K - 1      # the last step is still pending
+    tr = oracle.Trainer(p0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
+                        oracle.f32_to_bf16(p0), loss_scale=64.0, dynamic=True, wd=0.0,
+                        nthreads=NTHREADS, **hy)
+    flags = [tr.step(reps)[0] for reps in sets]
+    assert flags == [0, 0, 0, 0, 1]
+    rec = step.state()
+    assert (rec.seq, rec.pending_n, rec.t, rec.n_skipped, rec.last_overflow) == (K, 0, 4, 1, 1)
+    assert rec.loss_scale == tr.loss_scale == 32.0
+    assert step.last_stats().overflow == 1
+    P, M, V = step.committed()
+    check_state("deferred overflow", to_host(P), to_host(M), to_host(V),
+                to_host(step.current_slot()), tr.p, tr.m, tr.v, tr.slot)
+    again = step.state()
+    assert bytes(again) == bytes(rec)

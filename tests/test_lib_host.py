@@ -301,6 +301,31 @@ def test_device_state_load_validation(Z):
     assert status(beta2_pow=1.5) == -1
     assert status(beta1_pow=float("nan")) == -1
     assert status(t=0) == -1                           # beta^0 must be 1
+    assert status(pending_n=3) == -1                   # saved without a flush
+
+
+def test_device_state_flush_validation(Z):
+    """zero_device_state_flush checks its buffers on the host before enqueuing."""
+    L = Z.lib()
+    REC, STATS, WS = FAKE + 65536, FAKE + 69632, FAKE + (1 << 20)
+    wsb = Z.zero_workspace_bytes(64)
+    assert L.zero_device_state_flush(None, STATS, WS, wsb, None) == -1
+    assert L.zero_device_state_flush(REC, None, WS, wsb, None) == -1
+    assert L.zero_device_state_flush(REC, STATS, None, wsb, None) == -1
+    assert L.zero_device_state_flush(REC + 8, STATS, WS, wsb, None) == -2
+    assert L.zero_device_state_flush(REC, STATS + 4, WS, wsb, None) == -2
+    assert L.zero_device_state_flush(REC, STATS, WS, 4096, None) == -3      # too small for any step
+    assert L.zero_device_state_flush(REC, REC + 16, WS, wsb, None) == -1    # stats inside the record
+    assert L.zero_device_state_flush(REC, WS + 64, WS, wsb, None) == -1     # stats inside the workspace
+
+
+def test_workspace_layout_sizes(Z):
+    """A device-committed record's workspace holds, per workgroup slot, the partials
+    of two consecutive steps (2 x 24 bytes) and a start mark (8 bytes), then 64
+    bytes of flag words and the replica pointer table."""
+    for S in (1, 1024, 15_554_976, 842_301_952):
+        slots = min((S + 1023) // 1024 + 4096, 4_194_304)
+        assert Z.zero_workspace_bytes(S) == slots * 56 + 64 + 8 * 1024 + 16
 
 
 def test_train_step_part_validation(Z):
