@@ -60,7 +60,7 @@ struct KParams {
     int32_t n_rep;
     int32_t part_base;                      // device commit: partial slot of workgroup 0
     int32_t collect_n;                      // device commit: slots workgroup 0 collects (0: none)
-    int32_t reserved;
+    int32_t even_quads;                     // > 0: whole-shard launch split evenly, quads per workgroup
     int64_t S;
     const zero_bucket* buckets;
     int64_t n_buckets;
@@ -808,17 +808,30 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
     double sq = 0.0;
     uint32_t bad = 0u, badb = 0u;
     if constexpr (!BUCKETS) {
-        const int64_t nq = a.S >> 2;
-        const int64_t per_trip = (int64_t)ROWS * kBlock;
-        const int64_t ntrips = nq / per_trip;
-        for (int64_t trip = blockIdx.x; trip < ntrips; trip += gridDim.x)
-            quads<RT, ADAM, WRITE_G, TILED, ROWS>(a, rs, trip * per_trip + threadIdx.x, kBlock, sq, bad);
-        // whole quads after the last full trip, and the last S % 4 elements
-        if ((int64_t)blockIdx.x == ntrips % gridDim.x) {
-            for (int64_t q = ntrips * per_trip + threadIdx.x; q < nq; q += kBlock)
+        if (a.even_quads > 0) {
+            // quads [b*c, (b+1)*c) of the shard, and the last S % 4 elements with the
+            // last workgroup
+            const int64_t nq = a.S >> 2, c = a.even_quads, b = blockIdx.x;
+            const int64_t qhi = (b + 1) * c < nq ? (b + 1) * c : nq;
+            for (int64_t q = b * c + threadIdx.x; q < qhi; q += kBlock)
                 quads<RT, ADAM, WRITE_G, TILED, 1>(a, rs, q, 0, sq, bad);
-            const int64_t e = nq * 4 + threadIdx.x;
-            if (e < a.S) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
+            if (b == (int64_t)gridDim.x - 1) {
+                const int64_t e = nq * 4 + threadIdx.x;
+                if (e < a.S) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
+            }
+        } else {
+            const int64_t nq = a.S >> 2;
+            const int64_t per_trip = (int64_t)ROWS * kBlock;
+            const int64_t ntrips = nq / per_trip;
+            for (int64_t trip = blockIdx.x; trip < ntrips; trip += gridDim.x)
+                quads<RT, ADAM, WRITE_G, TILED, ROWS>(a, rs, trip * per_trip + threadIdx.x, kBlock, sq, bad);
+            // whole quads after the last full trip, and the last S % 4 elements
+            if ((int64_t)blockIdx.x == ntrips % gridDim.x) {
+                for (int64_t q = ntrips * per_trip + threadIdx.x; q < nq; q += kBlock)
+                    quads<RT, ADAM, WRITE_G, TILED, 1>(a, rs, q, 0, sq, bad);
+                const int64_t e = nq * 4 + threadIdx.x;
+                if (e < a.S) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
+            }
         }
     } else {
         for (int64_t b = blockIdx.x; b < a.n_buckets; b += gridDim.x) {
@@ -1005,7 +1018,27 @@ int rows_for(int32_t n_rep) { return n_rep <= 16 ? ZERO_ROWS_FEW : 1; }
 // one trip each up to about 134M elements), at most kGridMax / 2 with two rows
 // per lane and kGridMax with one, and balanced so that every workgroup makes
 // the same number of full trips (no ragged last round).
+// A whole-shard launch of kEvenMin .. kEvenMax - 1 trips (one trip per workgroup
+// covers a workgroup's worth of quads) rounds its grid up to a multiple of
+// kEvenUnit workgroups and gives each an equal quad-aligned range: with few
+// workgroups per compute unit, one more on some units than on others sets the
+// launch's length. Returns the quads per workgroup, or 0 for the usual grid.
+constexpr int64_t kEvenUnit = 256, kEvenMin = 256, kEvenMax = 2048;
+int64_t even_quads_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid) {
+    if (max_grid <= 0 || max_grid > kGridMax) max_grid = kGridMax;
+    if (n_buckets > 0 || rows_for(n_rep) != 1) return 0;
+    const int64_t trips = S / ((int64_t)kBlock * kVec);
+    const int64_t grid = (trips + kEvenUnit - 1) / kEvenUnit * kEvenUnit;
+    if (trips < kEvenMin || trips >= kEvenMax || grid > max_grid) return 0;
+    const int64_t nq = S >> 2;
+    return (nq + grid - 1) / grid;
+}
+
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid) {
+    if (even_quads_for(S, n_buckets, n_rep, max_grid) > 0) {
+        const int64_t trips = S / ((int64_t)kBlock * kVec);
+        return (int)((trips + kEvenUnit - 1) / kEvenUnit * kEvenUnit);
+    }
     if (max_grid <= 0 || max_grid > kGridMax) max_grid = kGridMax;
     if (n_buckets > 0) {
         // bucket launches stride over the table; at most grid_bound(S) workgroups
@@ -1111,7 +1144,7 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     k.n_rep = d.n_rep;
-    k.reserved = 0;
+    k.even_quads = 0;
     k.S = d.S;
     k.buckets = d.buckets;
     k.n_buckets = d.n_buckets;
@@ -1140,6 +1173,7 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     k.sc = d.sc;
     const bool buckets = d.n_buckets > 0;
     const int grid = grid_for(d.S, d.n_buckets, d.n_rep, d.max_grid);
+    k.even_quads = (int32_t)even_quads_for(d.S, d.n_buckets, d.n_rep, d.max_grid);
     k.part_base = d.part_base;
     k.collect_n = d.collect_n == 0 ? grid : (d.collect_n > 0 ? d.collect_n : 0);
     if (d.dtype == ZERO_BF16) {

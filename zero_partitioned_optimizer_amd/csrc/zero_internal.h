@@ -144,6 +144,7 @@ struct StepDesc {
 
 int rows_for(int32_t n_rep);
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid = 0);
+int64_t even_quads_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid = 0);
 hipError_t launch_step(const StepDesc& d, hipStream_t stream);
 hipError_t launch_cast_slot(const float* master, int64_t S, bool tiled, uint16_t* slot,
                             hipStream_t stream);
