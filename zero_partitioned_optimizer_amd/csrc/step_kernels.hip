@@ -60,7 +60,8 @@ struct KParams {
     int32_t n_rep;
     int32_t part_base;                      // device commit: partial slot of workgroup 0
     int32_t collect_n;                      // device commit: slots workgroup 0 collects (0: none)
-    int32_t even_quads;                     // > 0: whole-shard launch split evenly, quads per workgroup
+    int32_t even_blocks;                    // > 0: whole-shard launch split evenly over this many
+                                            // blocks of kEvenBlockQuads quads
     int64_t S;
     const zero_bucket* buckets;
     int64_t n_buckets;
@@ -808,12 +809,14 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
     double sq = 0.0;
     uint32_t bad = 0u, badb = 0u;
     if constexpr (!BUCKETS) {
-        if (a.even_quads > 0) {
-            // quads [b*c, (b+1)*c) of the shard, and the last S % 4 elements with the
-            // last workgroup
-            const int64_t nq = a.S >> 2, c = a.even_quads, b = blockIdx.x;
-            const int64_t qhi = (b + 1) * c < nq ? (b + 1) * c : nq;
-            for (int64_t q = b * c + threadIdx.x; q < qhi; q += kBlock)
+        if (a.even_blocks > 0) {
+            // blocks [b*NB/G, (b+1)*NB/G) of the shard's quads, and the last S % 4
+            // elements with the last workgroup
+            const int64_t nq = a.S >> 2, nb = a.even_blocks, g = gridDim.x, b = blockIdx.x;
+            const int64_t qlo = (b * nb / g) * kEvenBlockQuads;
+            int64_t qhi = ((b + 1) * nb / g) * kEvenBlockQuads;
+            if (qhi > nq) qhi = nq;
+            for (int64_t q = qlo + threadIdx.x; q < qhi; q += kBlock)
                 quads<RT, ADAM, WRITE_G, TILED, 1>(a, rs, q, 0, sq, bad);
             if (b == (int64_t)gridDim.x - 1) {
                 const int64_t e = nq * 4 + threadIdx.x;
@@ -1020,22 +1023,25 @@ int rows_for(int32_t n_rep) { return n_rep <= 16 ? ZERO_ROWS_FEW : 1; }
 // the same number of full trips (no ragged last round).
 // A whole-shard launch of kEvenMin .. kEvenMax - 1 trips (one trip per workgroup
 // covers a workgroup's worth of quads) rounds its grid up to a multiple of
-// kEvenUnit workgroups and gives each an equal quad-aligned range: with few
+// kEvenUnit workgroups and splits the shard evenly over them: with few
 // workgroups per compute unit, one more on some units than on others sets the
-// launch's length. Returns the quads per workgroup, or 0 for the usual grid.
+// launch's length. The split is in blocks of kEvenBlockQuads quads (128 bytes of
+// a bf16 replica, 256 of fp32 state), so no cache line is fetched by two
+// workgroups; workgroup b takes blocks [b*NB/G, (b+1)*NB/G). Returns NB, the
+// number of blocks, or 0 for the usual grid.
 constexpr int64_t kEvenUnit = 256, kEvenMin = 256, kEvenMax = 2048;
-int64_t even_quads_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid) {
+int64_t even_blocks_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid) {
     if (max_grid <= 0 || max_grid > kGridMax) max_grid = kGridMax;
     if (n_buckets > 0 || rows_for(n_rep) != 1) return 0;
     const int64_t trips = S / ((int64_t)kBlock * kVec);
     const int64_t grid = (trips + kEvenUnit - 1) / kEvenUnit * kEvenUnit;
     if (trips < kEvenMin || trips >= kEvenMax || grid > max_grid) return 0;
     const int64_t nq = S >> 2;
-    return (nq + grid - 1) / grid;
+    return (nq + kEvenBlockQuads - 1) / kEvenBlockQuads;
 }
 
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid) {
-    if (even_quads_for(S, n_buckets, n_rep, max_grid) > 0) {
+    if (even_blocks_for(S, n_buckets, n_rep, max_grid) > 0) {
         const int64_t trips = S / ((int64_t)kBlock * kVec);
         return (int)((trips + kEvenUnit - 1) / kEvenUnit * kEvenUnit);
     }
@@ -1144,7 +1150,7 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     k.n_rep = d.n_rep;
-    k.even_quads = 0;
+    k.even_blocks = 0;
     k.S = d.S;
     k.buckets = d.buckets;
     k.n_buckets = d.n_buckets;
@@ -1173,7 +1179,7 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     k.sc = d.sc;
     const bool buckets = d.n_buckets > 0;
     const int grid = grid_for(d.S, d.n_buckets, d.n_rep, d.max_grid);
-    k.even_quads = (int32_t)even_quads_for(d.S, d.n_buckets, d.n_rep, d.max_grid);
+    k.even_blocks = (int32_t)even_blocks_for(d.S, d.n_buckets, d.n_rep, d.max_grid);
     k.part_base = d.part_base;
     k.collect_n = d.collect_n == 0 ? grid : (d.collect_n > 0 ? d.collect_n : 0);
     if (d.dtype == ZERO_BF16) {
