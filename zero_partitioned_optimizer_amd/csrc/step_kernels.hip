@@ -22,12 +22,14 @@
 //  - one short workgroup per 1,024 elements (one quad per lane, one trip),
 //    far more workgroups than are resident, so faster CUs take more of them
 //    and the tail is one short workgroup; beyond kGridMax workgroups the grid
-//    strides over the shard with the same number of trips per workgroup;
+//    strides over the shard with the same number of trips per workgroup; small
+//    shards are instead split evenly over a multiple of 256 workgroups;
+//  - fp32 state as three arrays or in tiles of p | m | v (state_q, state_e);
 //  - the flag and the fp64 squared norm are reduced with wave shuffles, then
 //    LDS, then one partial per workgroup, summed in workgroup order (by a
 //    one-workgroup finalize kernel, or, with the device commit, by workgroup 0
-//    of the same launch), so the norm is bit-reproducible; there are no float
-//    atomics and no memsets;
+//    of the next launch on the record), so the norm is bit-reproducible; there
+//    are no float atomics and no memsets;
 //  - loads of data read once use the nontemporal hint, and so do the stores.
 // Arithmetic is one IEEE fp32 operation per source operation, built with
 // -ffp-contract=off; division and sqrt are the correctly rounded forms.
@@ -59,7 +61,9 @@ struct KParams {
     const void* const* rep_ext;             // device table of all n_rep pointers (n_rep > kArgReplicas)
     int32_t n_rep;
     int32_t part_base;                      // device commit: partial slot of workgroup 0
-    int32_t collect_n;                      // device commit: slots workgroup 0 collects (0: none)
+    int32_t collect_n;                      // device commit: > 0: workgroup 0 folds the pending step
+                                            // in, and this step (collect_n partials) becomes
+                                            // pending; 0: a part before the last
     int32_t even_blocks;                    // > 0: whole-shard launch split evenly over this many
                                             // blocks of kEvenBlockQuads quads
     int64_t S;

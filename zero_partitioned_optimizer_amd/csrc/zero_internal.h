@@ -132,9 +132,11 @@ struct StepDesc {
     hipEvent_t ev_end;
     // device commit split over several launches (parts of one step):
     int32_t part_base;              // partial slot of this launch's workgroup 0
-    int32_t collect_n;              // 0: collect this launch's own partials and commit (a
-                                    // whole step); > 0: collect slots [0, n) and commit;
-                                    // < 0: publish only (a part before the last)
+    int32_t collect_n;              // 0: a whole step (its own grid of partials); > 0: the last
+                                    // part of a split step, n partials over all parts; either
+                                    // way workgroup 0 folds the pending step into the record and
+                                    // this step becomes pending; < 0: a part before the last
+                                    // (publish only)
     bool no_restore;                // single slot: leave the restore kernel to the caller
     bool tiled;                     // state sets in the tiled layout (m, v pointers unused)
     uint64_t* ws_half[2];           // device-commit path: the workspace regions of CommitWs
