@@ -1,5 +1,6 @@
 """GPU parity at full shard sizes: the Llama-7B shard (S = 842,301,952, N = 8, loss
-scale 65536) and the Llama-70B shard (S = 2,155,520,256, N = 32, AdamW), in the
+scale 65536; also every element of it, test_llama7b_shard_every_element) and the
+Llama-70B shard (S = 2,155,520,256, N = 32, AdamW), in the
 launch configuration bench.py times (device commit, double-buffered slot,
 whole-shard grid, tiled state), and the Llama-7B shard also with split state.
 
@@ -18,7 +19,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import NTHREADS, check_state, say, sumsq_close, to_host
+from gpu_util import NTHREADS, assert_bitexact, check_state, say, sumsq_close, to_host
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -146,3 +147,61 @@ def test_llama70b_shard_full_size(Z):
     if free < need:
         pytest.skip(f"needs ~215 GiB of free device memory, {free / 2**30:.0f} GiB free")
     run_large(Z, "llama70b", steps=W.get("llama70b").steps, n_random=300_000, sub_elems=1 << 27)
+
+
+def test_llama7b_shard_every_element(Z):
+    """Every element of the Llama-7B shard through all its steps, in the bench's
+    launch configuration (device commit, double-buffered slot, tiled state): after
+    each step the committed p, m, v and slot come back in chunks of 2^27 elements
+    and the oracle steps the same chunk of its own state with the same replica
+    values; every element must agree bit for bit, and the squared norm within
+    1e-9 relative (it is summed in another grouping)."""
+    w = W.get("llama7b")
+    lay = oracle.Layout(w.numels, N=w.N, A=w.A, B=w.B)
+    rank = 0
+    S = lay.S
+    covered = [(int(s[2]), int(s[3])) for s in lay.segments(rank)]
+    dev = torch.device("cuda")
+    say(f"llama7b every element: S={S} N={w.N}, allocating")
+    reps = [torch.empty(S, dtype=torch.bfloat16, device=dev) for _ in range(w.N)]
+    p0 = torch.empty(S, dtype=torch.float32, device=dev)
+    W.device_fill_params(p0, w, covered, rank)
+    p = to_host(p0)
+    m = np.zeros(S, np.float32)
+    v = np.zeros(S, np.float32)
+    slot = oracle.f32_to_bf16(p)
+    step = Z.DeviceShardStep(S, w.N, Z.ZERO_BF16, p0, lr=w.lr, beta1=w.beta1, beta2=w.beta2,
+                             eps=w.eps, weight_decay=w.wd, loss_scale=w.loss_scale,
+                             dynamic=w.dynamic_loss_scale, double_slot=True,
+                             state_layout=Z.ZERO_STATE_TILED)
+    del p0
+    torch.cuda.empty_cache()
+    C = 1 << 27
+    for s in range(w.steps):
+        for j, r in enumerate(reps):
+            W.device_fill_replica(r, w, covered, rank, s, j)
+        dreps = [r.view(torch.int16) for r in reps]
+        say(f"llama7b every element: step {s}")
+        step.step(dreps)
+        P, M, V = step.committed()
+        cur_slot = step.current_slot()
+        total = 0.0
+        for c0 in range(0, S, C):
+            c1 = min(S, c0 + C)
+            hreps = [to_host(r[c0:c1]) for r in dreps]
+            flag, sq = oracle.step(hreps, p[c0:c1], m[c0:c1], v[c0:c1], slot[c0:c1],
+                                   loss_scale=w.loss_scale, t=s + 1, nthreads=NTHREADS,
+                                   **w.hyper())
+            assert flag == 0
+            total += sq
+            # bit equality (which implies the 1e-6 / 1-ulp bar) over the chunk
+            for name, g, want in (("p", P, p), ("m", M, m), ("v", V, v), ("slot", cur_slot, slot)):
+                assert_bitexact(f"llama7b step {s} {name} [{c0}, {c1})", to_host(g[c0:c1]),
+                                want[c0:c1])
+        rec = step.state()
+        assert rec.t == s + 1 and rec.last_overflow == 0
+        assert sumsq_close(step.last_stats().sumsq, total, 1e-9), (step.last_stats().sumsq, total)
+        del P, M, V, hreps
+        torch.cuda.empty_cache()
+    del reps, dreps, step
+    torch.cuda.empty_cache()
