@@ -65,3 +65,53 @@ def test_captured_step_replays_like_eager(Z, double_slot):
             assert torch.equal(a, b)
         assert torch.equal(sg.current_slot(), se.current_slot())
     assert sg.state().t == K - 1 and sg.state().loss_scale == 128.0
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_graph_of_two_steps_replayed_back_to_back(Z, tiled):
+    """A graph of two steps replayed three times with no host read in between:
+    each launch folds the previous step into the record on the device, a replay's
+    first launch folding in the previous replay's last step. Both steps of the
+    second replay see an injected +inf. After one flush the record, the committed
+    state and the slot equal six eager steps with the same inputs."""
+    S, N = 300_007, 4
+    rng = np.random.default_rng(41)
+    reps_h = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * 1e-3 * 64.0))
+              for _ in range(N)]
+    p0 = to_dev((rng.standard_normal(S) * 0.02).astype(np.float32))
+    hy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, loss_scale=64.0,
+              dynamic=True, state_layout=Z.ZERO_STATE_TILED if tiled else Z.ZERO_STATE_SPLIT)
+    reps_g = [to_dev(r) for r in reps_h]
+    reps_e = [to_dev(r) for r in reps_h]
+    sg = Z.DeviceShardStep(S, N, Z.ZERO_BF16, p0, **hy)
+    se = Z.DeviceShardStep(S, N, Z.ZERO_BF16, p0, **hy)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        sg._args_for(reps_g)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            sg.step(reps_g)
+            sg.step(reps_g)
+    torch.cuda.synchronize()
+    bad = int(reps_h[1][5].view(np.int16))
+    for r in range(3):
+        say(f"two-step graph replay {r} (tiled={tiled})")
+        if r == 1:
+            reps_g[1][5] = 0x7F80
+            reps_e[1][5] = 0x7F80
+        graph.replay()
+        se.step(reps_e)
+        se.step(reps_e)
+        if r == 1:
+            reps_g[1][5] = bad
+            reps_e[1][5] = bad
+    torch.cuda.synchronize()
+    rg, re = sg.state(), se.state()
+    assert (rg.t, rg.n_skipped, rg.seq, rg.loss_scale) == (re.t, re.n_skipped, re.seq, re.loss_scale)
+    assert (rg.t, rg.n_skipped, rg.seq, rg.loss_scale) == (4, 2, 6, 16.0)
+    for a, b in zip(sg.committed(), se.committed()):
+        assert torch.equal(a, b)
+    assert torch.equal(sg.current_slot(), se.current_slot())
