@@ -76,7 +76,8 @@ def test_tiny_every_rank(Z, double_slot, tiled):
 
 @pytest.mark.parametrize("rank,bucket_elems,double_slot,tiled", [
     (0, 0, False, False), (63, 0, True, False), (0, 4096, True, False), (31, 1000, False, False),
-    (0, 0, False, True), (63, 0, True, True), (0, 4096, True, True), (31, 1000, False, True)])
+    (0, 0, False, True), (63, 0, True, True), (0, 4096, True, True), (31, 1000, False, True),
+    (5, 65536, False, True), (40, 1 << 20, True, False)])
 def test_ragged_injection(Z, rank, bucket_elems, double_slot, tiled):
     w = W.get("ragged")
     lay, covered = layout_of(w, rank)

@@ -91,7 +91,8 @@ def test_gpt2_small_shard(Z, rank):
     run_protocol(Z, w, rank, steps=3 if rank == 0 else 1)
 
 
-@pytest.mark.parametrize("rank,bucket_elems", [(0, 0), (0, 4096), (63, 0), (63, 1000), (31, 2048)])
+@pytest.mark.parametrize("rank,bucket_elems", [(0, 0), (0, 4096), (63, 0), (63, 1000), (31, 2048),
+                                               (17, 65536)])
 def test_ragged_inf_injection_and_dynamic_scale(Z, rank, bucket_elems):
     w = W.get("ragged")
     lay, covered = layout_of(w, rank)
@@ -369,24 +370,25 @@ def test_slot_only_writes_and_guard_bands(Z):
     assert_bitexact("p_in", to_host(P_in.t), p)
 
 
-@pytest.mark.parametrize("N", [6, 300])
-def test_bucket_table_random(Z, N):
+@pytest.mark.parametrize("N,S,n_cuts", [(6, 20_011, 400), (300, 20_011, 400), (6, 300_007, 40),
+                                         (65, 300_007, 40), (8, 300_007, 1)])
+def test_bucket_table_random(Z, N, S, n_cuts):
     """Random disjoint buckets at arbitrary (unaligned) offsets: elements inside are
     updated as the oracle says, elements outside keep their sentinel, a bucket
     that leaves the shard is skipped and counted (N = 300: replica pointers from
-    the workspace table)."""
-    S = 20_011
-    say(f"bucket table N={N}")
+    the workspace table). S = 300,007 with few cuts: a short table of long
+    buckets, cut into chunks spread over the grid."""
+    say(f"bucket table N={N} S={S} cuts={n_cuts}")
     rng = np.random.default_rng(12)
     reps = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * 1e-3)) for _ in range(N)]
     p = (rng.standard_normal(S) * 0.02).astype(np.float32)
     m = (rng.standard_normal(S) * 1e-4).astype(np.float32)
     v = ((rng.standard_normal(S) * 1e-4) ** 2).astype(np.float32)
-    cuts = np.sort(rng.choice(np.arange(1, S), size=400, replace=False))
+    cuts = np.sort(rng.choice(np.arange(1, S), size=n_cuts, replace=False))
     edges = np.concatenate([[0], cuts, [S]])
     table = []
     for a0, b0 in zip(edges[:-1], edges[1:]):
-        if rng.random() < 0.6 and b0 > a0:
+        if (rng.random() < 0.6 or n_cuts < 2) and b0 > a0:
             table.append((int(a0), int(b0 - a0), 0))
     inside = np.zeros(S, bool)
     for o, ln, _ in table:

@@ -64,8 +64,9 @@ struct KParams {
     int32_t collect_n;                      // device commit: > 0: workgroup 0 folds the pending step
                                             // in, and this step (collect_n partials) becomes
                                             // pending; 0: a part before the last
-    int32_t even_blocks;                    // > 0: whole-shard launch split evenly over this many
-                                            // blocks of kEvenBlockQuads quads
+    int32_t even_blocks;                    // whole shard: > 0: split evenly over this many
+                                            // blocks of kEvenBlockQuads quads; bucket table:
+                                            // > 0: buckets cut into chunks of kChunk elements
     int64_t S;
     const zero_bucket* buckets;
     int64_t n_buckets;
@@ -840,6 +841,69 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
                 if (e < a.S) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
             }
         }
+    } else if (a.even_blocks > 0) {
+        // A short table of long buckets: every bucket is cut into chunks of kChunk
+        // elements (boundaries on 64-element lines) and the chunks are dealt over
+        // the grid. Each workgroup reads the table and prefix-sums the chunk counts
+        // in LDS: first[b] is bucket b's first chunk, first[n] the total.
+        __shared__ int64_t first[kChunkTableMax + 1];
+        __shared__ int64_t wave_sum[kBlock / 64];
+        const int64_t nbk = a.n_buckets;
+        const int64_t per = (nbk + kBlock - 1) / kBlock;
+        const int64_t b0 = threadIdx.x * per;
+        int64_t mine = 0;
+        for (int64_t i = 0; i < per; ++i) {
+            const int64_t b = b0 + i;
+            if (b >= nbk) break;
+            const zero_bucket bk = a.buckets[b];
+            const int64_t lo = bk.shard_off, len = bk.len;
+            int64_t c = 0;
+            if (lo < 0 || len < 0 || lo > a.S || len > a.S - lo) {
+                if (blockIdx.x == 0) badb += 1u;     // counted once, by workgroup 0
+            } else {
+                c = (len + kChunk - 1) / kChunk;
+            }
+            first[b] = c;
+            mine += c;
+        }
+        const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        int64_t incl = mine;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int64_t y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        if (lane == 63) wave_sum[wv] = incl;
+        __syncthreads();
+        int64_t run = incl - mine;
+        for (int w = 0; w < wv; ++w) run += wave_sum[w];
+        if (threadIdx.x == kBlock - 1) first[nbk] = run + mine;
+        for (int64_t i = 0; i < per; ++i) {
+            const int64_t b = b0 + i;
+            if (b >= nbk) break;
+            const int64_t c = first[b];
+            first[b] = run;
+            run += c;
+        }
+        __syncthreads();
+        const int64_t total = first[nbk];
+        for (int64_t j = blockIdx.x; j < total; j += gridDim.x) {
+            // the bucket holding chunk j: first[lb] <= j < first[lb + 1]
+            int64_t lb = 0, ub = nbk;
+            while (ub - lb > 1) {
+                const int64_t mid = (lb + ub) >> 1;
+                if (first[mid] <= j) lb = mid;
+                else ub = mid;
+            }
+            const zero_bucket bk = a.buckets[lb];
+            const int64_t blo = bk.shard_off, bhi = blo + bk.len;
+            const int64_t k = j - first[lb], last = first[lb + 1] - first[lb] - 1;
+            int64_t lo = k == 0 ? blo : ((blo + k * kChunk) & ~int64_t(63));
+            int64_t hi = k == last ? bhi : ((blo + (k + 1) * kChunk) & ~int64_t(63));
+            if (lo < blo) lo = blo;
+            if (hi < blo) hi = blo;
+            range<RT, ADAM, WRITE_G, TILED, ROWS>(a, rs, lo, hi, sq, bad);
+        }
     } else {
         for (int64_t b = blockIdx.x; b < a.n_buckets; b += gridDim.x) {
             const zero_bucket bk = a.buckets[b];
@@ -1044,12 +1108,22 @@ int64_t even_blocks_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_gri
     return (nq + kEvenBlockQuads - 1) / kEvenBlockQuads;
 }
 
+bool bucket_chunks(int64_t S, int64_t n_buckets) {
+    return n_buckets > 0 && n_buckets <= kChunkTableMax && n_buckets * 2 * kChunk <= S;
+}
+
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid) {
     if (even_blocks_for(S, n_buckets, n_rep, max_grid) > 0) {
         const int64_t trips = S / ((int64_t)kBlock * kVec);
         return (int)((trips + kEvenUnit - 1) / kEvenUnit * kEvenUnit);
     }
     if (max_grid <= 0 || max_grid > kGridMax) max_grid = kGridMax;
+    if (bucket_chunks(S, n_buckets)) {
+        // enough workgroups for one chunk each when the buckets are disjoint
+        const int64_t g = (S + kChunk - 1) / kChunk + n_buckets;
+        const int64_t cap = grid_bound(S) < max_grid ? grid_bound(S) : max_grid;
+        return (int)(g < cap ? g : cap);
+    }
     if (n_buckets > 0) {
         // bucket launches stride over the table; at most grid_bound(S) workgroups
         int64_t g = n_buckets < max_grid ? n_buckets : max_grid;
@@ -1183,7 +1257,8 @@ hipError_t launch_step(const StepDesc& d, hipStream_t st) {
     k.sc = d.sc;
     const bool buckets = d.n_buckets > 0;
     const int grid = grid_for(d.S, d.n_buckets, d.n_rep, d.max_grid);
-    k.even_blocks = (int32_t)even_blocks_for(d.S, d.n_buckets, d.n_rep, d.max_grid);
+    k.even_blocks = buckets ? (bucket_chunks(d.S, d.n_buckets) ? 1 : 0)
+                            : (int32_t)even_blocks_for(d.S, d.n_buckets, d.n_rep, d.max_grid);
     k.part_base = d.part_base;
     k.collect_n = d.collect_n == 0 ? grid : (d.collect_n > 0 ? d.collect_n : 0);
     if (d.dtype == ZERO_BF16) {

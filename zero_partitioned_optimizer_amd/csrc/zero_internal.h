@@ -23,6 +23,10 @@ constexpr int kGridMax = ZERO_GRID_MAX;  // workgroups of the grid-stride step k
 constexpr int kMaxParts = 4096;          // parts of one step split over launches
 constexpr int kArgReplicas = 256;        // replica pointers carried in the kernel arguments
 constexpr int64_t kEvenBlockQuads = 16;  // quads per block of an evenly split small launch
+// A bucket launch over a table of at most kChunkTableMax buckets that average at
+// least two chunks each cuts the buckets into chunks of kChunk elements.
+constexpr int64_t kChunk = (int64_t)kBlock * kVec;
+constexpr int64_t kChunkTableMax = 2048;
 
 // Bytes at the end of the workspace that a launch with n_rep replicas uses for
 // its device table of replica pointers (only beyond kArgReplicas replicas; 16
@@ -148,6 +152,7 @@ struct StepDesc {
 int rows_for(int32_t n_rep);
 int grid_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid = 0);
 int64_t even_blocks_for(int64_t S, int64_t n_buckets, int32_t n_rep, int max_grid = 0);
+bool bucket_chunks(int64_t S, int64_t n_buckets);
 hipError_t launch_step(const StepDesc& d, hipStream_t stream);
 hipError_t launch_cast_slot(const float* master, int64_t S, bool tiled, uint16_t* slot,
                             hipStream_t stream);
