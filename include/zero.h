@@ -395,8 +395,29 @@ typedef struct {
     uint32_t seq;                  /* steps folded into this record (committed or skipped) */
     uint32_t pending_n;            /* > 0: one more step has run and awaits folding in (its
                                       partial count); 0 after init, load and flush */
-    uint32_t reserved;
+    uint32_t error;                /* 0, or a ZERO_RECORD_E_* code: the record is frozen */
 } zero_device_state;
+
+/*
+ * Sticky error codes of a record (zero_device_state.error). The folding of a
+ * pending step waits, bounded by 2 s of the GPU's real-time counter, for two
+ * things: the pending step's partials (written by the previous launch, so
+ * present at once in a correct run) and the start marks of every workgroup of
+ * its own launch (which must all have read the record before it changes).
+ * Should either wait run out, which a correct launch never does, the folding
+ * workgroup leaves every other field of the record as it is and stores one of
+ * these codes instead; the stats read overflow = 1, bad_buckets = 0xFFFFFFFF,
+ * sumsq = NaN. From then on every step launch on the record returns at once
+ * without reading replicas or writing state, slot, partials or stats, the
+ * restore kernel leaves the slot alone and a flush only writes the error stats,
+ * so no update can land on state that a late workgroup may still be reading.
+ * The state set that the frozen record's pending step names (as the skip rule
+ * would apply it) is not written by the failed launch, but the caller should
+ * treat the run as failed and resume from a checkpoint: zero_device_state_load
+ * and zero_device_state_init clear the code. zero_device_state_load refuses a
+ * saved record that carries one.
+ */
+enum { ZERO_RECORD_OK = 0, ZERO_RECORD_E_COLLECT = 1, ZERO_RECORD_E_MARKS = 2 };
 
 /*
  * Enqueue the initialisation of a device state record (a small kernel, no
@@ -427,7 +448,8 @@ int zero_device_state_init(zero_device_state* state_dev, void* workspace_dev, si
  * double-buffered). The host record is read before return.
  * Errors: ZERO_E_INVAL (NULL, betas or loss scales as for zero_device_state_init,
  * t or n_skipped negative, cur or last_overflow not 0/1, beta powers outside
- * [0, 1] or not 1 at t = 0), ZERO_E_ALIGN, ZERO_E_HIP.
+ * [0, 1] or not 1 at t = 0, a pending step, a nonzero error code),
+ * ZERO_E_ALIGN, ZERO_E_HIP.
  */
 int zero_device_state_load(zero_device_state* state_dev, void* workspace_dev, size_t ws_bytes,
                            const zero_device_state* saved, void* stream);
@@ -437,7 +459,10 @@ int zero_device_state_load(zero_device_state* state_dev, void* workspace_dev, si
  * on `stream`): t, the loss scale, beta^t, the current set, n_skipped,
  * last_overflow and last_sumsq then describe every step enqueued before the
  * flush, and *stats_dev holds that last step's overflow flag, bucket count and
- * squared norm. No-op if nothing is pending. The workspace must be the record's.
+ * squared norm. No-op if nothing is pending. On a record frozen by a
+ * ZERO_RECORD_E_* code it changes nothing in the record and writes the error
+ * stats (overflow = 1, bad_buckets = 0xFFFFFFFF, sumsq = NaN); the caller finds
+ * the code in the record it copies back. The workspace must be the record's.
  * Errors: ZERO_E_INVAL (NULL, overlapping buffers), ZERO_E_ALIGN, ZERO_E_RANGE
  * (workspace too small for any step), ZERO_E_HIP.
  */
@@ -483,8 +508,9 @@ typedef struct {
  * partials in workgroup order and, once every workgroup of the launch has left
  * its start mark, folds that step into *state_dev; this step stays pending until
  * the next step or zero_device_state_flush. The waits are bounded (2 s); should
- * one run out, which a correct launch never does, the stats read overflow = 1,
- * bad_buckets = 0xFFFFFFFF. The workspace must be the one given to
+ * one run out, which a correct launch never does, the record is frozen with a
+ * ZERO_RECORD_E_* code and every later step on it does nothing (see
+ * zero_device_state.error). The workspace must be the one given to
  * zero_device_state_init, of at least zero_workspace_bytes(shard_S) bytes. With
  * a single slot the candidate bf16 values go straight into it and a second kernel
  * restores it from the committed master after an overflow;

@@ -302,6 +302,8 @@ def test_device_state_load_validation(Z):
     assert status(beta1_pow=float("nan")) == -1
     assert status(t=0) == -1                           # beta^0 must be 1
     assert status(pending_n=3) == -1                   # saved without a flush
+    assert status(error=Z.ZERO_RECORD_E_COLLECT) == -1 # frozen by a wait that ran out
+    assert status(error=Z.ZERO_RECORD_E_MARKS) == -1
 
 
 def test_device_state_flush_validation(Z):

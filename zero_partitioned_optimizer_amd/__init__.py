@@ -21,5 +21,6 @@ from ._binding import (  # noqa: F401
     zero_offload_step, zero_offload_args, zero_host_adam_args, zero_gather_tensors, GatherPlan,
     zero_train_args, zero_train_step, make_train_args, device_state_from_tensor,
     ZERO_STATE_SPLIT, ZERO_STATE_TILED, ZERO_STATE_TILE, zero_gather_slot_tiled,
-    zero_state_set_floats, zero_state_pack, zero_state_unpack, zero_device_state_flush)
+    zero_state_set_floats, zero_state_pack, zero_state_unpack, zero_device_state_flush,
+    ZeroRecordError, ZERO_RECORD_OK, ZERO_RECORD_E_COLLECT, ZERO_RECORD_E_MARKS)
 from .shard_step import DeviceShardStep, OffloadShardStep, ShardStep  # noqa: F401

@@ -26,6 +26,7 @@ ZERO_COMMIT, ZERO_SKIP = 1, 2
 ZERO_MAX_REPLICAS = 1024
 ZERO_STATE_SPLIT, ZERO_STATE_TILED = 0, 1
 ZERO_STATE_TILE = 8192
+ZERO_RECORD_OK, ZERO_RECORD_E_COLLECT, ZERO_RECORD_E_MARKS = 0, 1, 2
 
 _STATUS = {0: "ZERO_OK", -1: "ZERO_E_INVAL", -2: "ZERO_E_ALIGN", -3: "ZERO_E_RANGE",
            -4: "ZERO_E_NOMEM", -5: "ZERO_E_HIP", -6: "ZERO_E_UNSUPPORTED"}
@@ -35,6 +36,19 @@ class ZeroError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{_STATUS.get(status, status)}: {msg}")
         self.status = status
+
+
+class ZeroRecordError(RuntimeError):
+    """A device-committed record frozen by a ZERO_RECORD_E_* code: a bounded wait
+    inside a step ran out, and every later step on the record did nothing."""
+
+    _WHAT = {ZERO_RECORD_E_COLLECT: "the previous step's partial sums did not arrive",
+             ZERO_RECORD_E_MARKS: "a workgroup of the step did not read the record in time"}
+
+    def __init__(self, code: int):
+        super().__init__(f"device record frozen by error code {code} "
+                         f"({self._WHAT.get(code, 'unknown code')}); resume from a checkpoint")
+        self.code = code
 
 
 class zero_layout_info(ctypes.Structure):
@@ -76,7 +90,7 @@ class zero_device_state(ctypes.Structure):
     _fields_ = [("beta1", f64), ("beta2", f64), ("beta1_pow", f64), ("beta2_pow", f64),
                 ("loss_scale", f64), ("min_loss_scale", f64), ("last_sumsq", f64),
                 ("t", i64), ("n_skipped", i64), ("cur", u32), ("dynamic", u32),
-                ("last_overflow", u32), ("seq", u32), ("pending_n", u32), ("reserved", u32)]
+                ("last_overflow", u32), ("seq", u32), ("pending_n", u32), ("error", u32)]
 
 
 class zero_train_args(ctypes.Structure):

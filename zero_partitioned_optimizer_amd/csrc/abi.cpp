@@ -472,10 +472,14 @@ int zero_device_state_load(zero_device_state* state_dev, void* workspace_dev, si
                   r.pending_n);
         return ZERO_E_INVAL;
     }
+    if (r.error != 0u) {
+        set_error("%s: the saved record is frozen by error code %u (a bounded wait of a step ran "
+                  "out); resume from a record saved before it", fn, r.error);
+        return ZERO_E_INVAL;
+    }
     zero_device_state rec = r;
     rec.dynamic = r.dynamic ? 1u : 0u;
     rec.seq = 0u;                    // the cleared workspace holds no tag of an earlier step
-    rec.reserved = 0u;
     return hip_status(zk::launch_state_write(state_dev, rec, workspace_dev, ws_bytes,
                                              static_cast<hipStream_t>(stream)),
                       fn);

@@ -105,6 +105,7 @@ struct Res {
     uint32_t tag;                           // device-commit: number of this step
     uint64_t mark;                          // device-commit: start mark (tag, and a checksum of the
                                             // record words read, so it waits for all of them)
+    uint32_t err;                           // device-commit: the record's sticky error code
 };
 
 // ---------------------------------------------------------------------------
@@ -363,7 +364,7 @@ __device__ __forceinline__ uint64_t uni64(uint64_t x) {
 // workgroup derives it from the same words, so all agree; workgroup 0 writes it
 // back into the record later in the launch.
 struct RecView {
-    uint32_t seq, pend, cur, dynamic;
+    uint32_t seq, pend, cur, dynamic, err;
     uint64_t flag;                          // flag word of the pending step's parity
     double b1, b2, pow1, pow2, ls, min_ls;  // pow: beta^t of the committed t
     uint32_t sum;                           // checksum of every word read
@@ -380,6 +381,7 @@ __device__ __forceinline__ RecView read_record(const zero_device_state* c, const
     v.pend = uni32(c->pending_n);
     v.cur = uni32(c->cur);
     v.dynamic = uni32(c->dynamic);
+    v.err = uni32(c->error);
     const uint64_t b1 = uni64((uint64_t)__double_as_longlong(c->beta1));
     const uint64_t b2 = uni64((uint64_t)__double_as_longlong(c->beta2));
     const uint64_t p1 = uni64((uint64_t)__double_as_longlong(c->beta1_pow));
@@ -395,7 +397,7 @@ __device__ __forceinline__ RecView read_record(const zero_device_state* c, const
     v.pow2 = __longlong_as_double((long long)p2);
     v.ls = __longlong_as_double((long long)ls);
     v.min_ls = __longlong_as_double((long long)ml);
-    v.sum = v.seq ^ v.pend ^ v.cur ^ v.dynamic ^ fold32(b1) ^ fold32(b2) ^ fold32(p1) ^ fold32(p2) ^
+    v.sum = v.seq ^ v.pend ^ v.cur ^ v.dynamic ^ v.err ^ fold32(b1) ^ fold32(b2) ^ fold32(p1) ^ fold32(p2) ^
             fold32(ls) ^ fold32(ml) ^ fold32(v.flag);
     v.cur &= 1u;
     return v;
@@ -436,9 +438,11 @@ __device__ __forceinline__ Res resolve(const KParams& a) {
         r.slot = a.slot;
         r.tag = 0u;
         r.mark = 0u;
+        r.err = 0u;
     } else {
         RecView v = read_record(a.ctrl, a.ws_flags);
         const uint32_t tag = v.seq + (v.pend ? 2u : 1u);
+        r.err = v.err;
         r.tag = tag;
         r.mark = ((uint64_t)tag << 32) | v.sum;
         apply_pending(v);
@@ -653,9 +657,13 @@ __device__ __forceinline__ void block_reduce(double& sq, uint32_t& bad, uint32_t
 // read it, which each signals with a start mark. Nobody waits for the last
 // workgroup to finish, and nothing runs after it.
 //
-// Waits are bounded by kCollectTimeout ticks of the 100 MHz real-time counter;
-// if one runs out (which a correct launch never does) the stats carry the marker
-// bad_buckets = 0xFFFFFFFF.
+// Waits are bounded by kCollectTimeout ticks of the 100 MHz real-time counter.
+// If one runs out (which a correct launch never does) workgroup 0 freezes the
+// record instead of folding: it stores a ZERO_RECORD_E_* code in the record's
+// error word and touches nothing else there, and the stats carry the marker
+// bad_buckets = 0xFFFFFFFF. A workgroup that finds the code set returns at once,
+// in this launch and every later one, so no update lands on state that a late
+// workgroup may still be reading.
 constexpr uint64_t kCollectTimeout = 200000000ull;   // 2 s
 
 // OR of a per-thread flag over the workgroup, in every thread.
@@ -675,7 +683,8 @@ __device__ __forceinline__ uint32_t block_or(uint32_t x) {
 // Sum n partials tagged `tag` at `base` in slot order (thread t takes partials t,
 // t + kBlock, ..., kBatch at a time with their loads all in flight; then the
 // fixed tree of block_reduce, which leaves the totals in thread 0). Partials are
-// polled until they carry the tag.
+// polled until they carry the tag; a thread whose wait runs out sets
+// ZERO_RECORD_E_COLLECT in tmo.
 __device__ __forceinline__ void collect(const uint64_t* base, int n, uint32_t tag, uint64_t t0,
                                        double& sq, uint32_t& bad, uint32_t& badb, uint32_t& tmo) {
     constexpr int kBatch = 4;
@@ -717,13 +726,14 @@ __device__ __forceinline__ void collect(const uint64_t* base, int n, uint32_t ta
             badb += (uint32_t)(w[k][2] & 0xffffffffull) >> 1;
         }
     }
-    if (timed_out) tmo = 1u;
+    if (timed_out) tmo |= (uint32_t)ZERO_RECORD_E_COLLECT;
     block_reduce(sq, bad, badb);
 }
 
 // Wait until the n start marks at `marks` carry `tag`: every workgroup of this
 // launch has read the record. Thread t checks marks t, t + kBlock, ..., kBatch at
-// a time with their loads all in flight, re-polling the ones not yet in.
+// a time with their loads all in flight, re-polling the ones not yet in; a thread
+// whose wait runs out sets ZERO_RECORD_E_MARKS in tmo.
 __device__ __forceinline__ void wait_marks(const uint64_t* marks, int n, uint32_t tag, uint64_t t0,
                                           uint32_t& tmo) {
     constexpr int kBatch = 4;
@@ -742,7 +752,7 @@ __device__ __forceinline__ void wait_marks(const uint64_t* marks, int n, uint32_
                 if ((uint32_t)(w[k] >> 32) == tag) have |= (want >> k & 1u) << k;
             if (have == want) break;
             if (__builtin_amdgcn_s_memrealtime() - t0 > kCollectTimeout) {
-                tmo = 1u;
+                tmo |= (uint32_t)ZERO_RECORD_E_MARKS;
                 return;
             }
             __builtin_amdgcn_s_sleep(8);
@@ -750,24 +760,34 @@ __device__ __forceinline__ void wait_marks(const uint64_t* marks, int n, uint32_
     }
 }
 
+// The stats of a frozen record: overflow, every bucket counted bad, NaN norm.
+__device__ __forceinline__ void error_stats(zero_stats* stats) {
+    stats->overflow = 1u;
+    stats->bad_buckets = 0xffffffffu;
+    stats->sumsq = __longlong_as_double(0x7ff8000000000000ll);
+}
+
 // Thread 0: fold the pending step into the record (with the squared norm and
 // bucket count summed from its partials) and write its stats; the step that
-// just ran (new_pending partials; 0 for a flush) becomes the pending one.
+// just ran (new_pending partials; 0 for a flush) becomes the pending one. If a
+// wait ran out (tmo holds ZERO_RECORD_E_* bits), freeze the record instead: only
+// its error word changes, so every other field still describes the state before
+// this launch, whichever words a late reader of the record sees.
 __device__ __forceinline__ void fold_pending(zero_device_state* c, zero_stats* stats,
                                              const uint64_t* flags, double sq, uint32_t badb,
-                                             bool tmo, uint32_t new_pending) {
+                                             uint32_t tmo, uint32_t new_pending) {
+    if (tmo) {
+        error_stats(stats);
+        c->error = (tmo & (uint32_t)ZERO_RECORD_E_COLLECT) ? (uint32_t)ZERO_RECORD_E_COLLECT
+                                                          : (uint32_t)ZERO_RECORD_E_MARKS;
+        return;
+    }
     RecView v = read_record(c, flags);
     if (v.pend) {
         const bool overflow = pending_overflow(v);
-        if (tmo) {
-            stats->overflow = 1u;
-            stats->bad_buckets = 0xffffffffu;
-            stats->sumsq = __longlong_as_double(0x7ff8000000000000ll);
-        } else {
-            stats->overflow = overflow ? 1u : 0u;
-            stats->bad_buckets = badb;
-            stats->sumsq = sq;
-        }
+        stats->overflow = overflow ? 1u : 0u;
+        stats->bad_buckets = badb;
+        stats->sumsq = sq;
         c->last_overflow = overflow ? 1u : 0u;
         c->last_sumsq = sq;
         if (!overflow) c->t = c->t + 1;
@@ -778,10 +798,6 @@ __device__ __forceinline__ void fold_pending(zero_device_state* c, zero_stats* s
         c->beta2_pow = v.pow2;
         c->loss_scale = v.ls;
         c->seq = v.seq + 1u;
-    } else if (tmo) {
-        stats->overflow = 1u;
-        stats->bad_buckets = 0xffffffffu;
-        stats->sumsq = __longlong_as_double(0x7ff8000000000000ll);
     }
     c->pending_n = new_pending;
 }
@@ -797,7 +813,7 @@ __device__ __forceinline__ void finalize_launch(const KParams& a, uint32_t tag) 
     if (pend) collect(a.ws_half[(seq + 1u) & 1u], (int)pend, seq + 1u, t0, sq, bad, badb, tmo);
     wait_marks(a.ws_started + a.part_base, (int)gridDim.x, tag, t0, tmo);
     tmo = block_or(tmo);
-    if (threadIdx.x == 0) fold_pending(a.ctrl_rw, a.stats, a.ws_flags, sq, badb, tmo != 0u,
+    if (threadIdx.x == 0) fold_pending(a.ctrl_rw, a.stats, a.ws_flags, sq, badb, tmo,
                                        (uint32_t)a.collect_n);
 }
 
@@ -805,6 +821,8 @@ template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL, bool TI
 __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
     const Res rs = resolve<CTRL, TILED>(a);
     if constexpr (CTRL) {
+        // a frozen record (a wait of an earlier launch ran out): no work at all
+        if (rs.err) return;
         // this workgroup has read the record (the mark's value depends on every
         // word it read); workgroup 0 may rewrite it once all marks are in
         if (threadIdx.x == 0)
@@ -1000,6 +1018,8 @@ template <bool TILED>
 __global__ void __launch_bounds__(kBlock) k_restore(const zero_device_state* ctrl,
                                                    const uint64_t* flags, const float* set_p0,
                                                    const float* set_p1, uint16_t* slot, int64_t S) {
+    // a frozen record: the slot stays as it is
+    if (ctrl->error) return;
     // the step just run is pending in the record (or folded in by a flush)
     const uint32_t seq = ctrl->seq, pend = ctrl->pending_n;
     const bool overflow = pend ? flags[(seq + 1u) & 1u] == (uint64_t)(seq + 1u)
@@ -1013,6 +1033,11 @@ __global__ void __launch_bounds__(kBlock) k_restore(const zero_device_state* ctr
 __global__ void __launch_bounds__(kBlock) k_flush(zero_device_state* c, zero_stats* stats,
                                                  const uint64_t* half0, const uint64_t* half1,
                                                  const uint64_t* flags) {
+    if (rd32(&c->error)) {
+        // a frozen record: report it in the stats, change nothing
+        if (threadIdx.x == 0) error_stats(stats);
+        return;
+    }
     const uint32_t seq = rd32(&c->seq), pend = rd32(&c->pending_n);
     if (!pend) return;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -1020,7 +1045,7 @@ __global__ void __launch_bounds__(kBlock) k_flush(zero_device_state* c, zero_sta
     uint32_t bad = 0u, badb = 0u, tmo = 0u;
     collect(((seq + 1u) & 1u) ? half1 : half0, (int)pend, seq + 1u, t0, sq, bad, badb, tmo);
     tmo = block_or(tmo);
-    if (threadIdx.x == 0) fold_pending(c, stats, flags, sq, badb, tmo != 0u, 0u);
+    if (threadIdx.x == 0) fold_pending(c, stats, flags, sq, badb, tmo, 0u);
 }
 
 // Conversion between three split arrays p, m, v [S] and one tiled set buffer;

@@ -256,14 +256,20 @@ class DeviceShardStep:
         """Enqueue the folding of the last step into the record and the stats."""
         B.zero_device_state_flush(self.record, self.stats, self.ws, stream)
 
-    def state(self) -> B.zero_device_state:
-        """Flush, then copy the committed-state record back (synchronizes)."""
+    def state(self, check: bool = True) -> B.zero_device_state:
+        """Flush, then copy the committed-state record back (synchronizes). A record
+        frozen by a ZERO_RECORD_E_* code raises ZeroRecordError unless check is
+        False."""
         self.flush()
-        return B.device_state_from_tensor(self.record)
+        rec = B.device_state_from_tensor(self.record)
+        if check and rec.error:
+            raise B.ZeroRecordError(int(rec.error))
+        return rec
 
     def last_stats(self) -> B.zero_stats:
-        """Flush, then copy the last step's stats back (synchronizes)."""
-        self.flush()
+        """Flush, then copy the last step's stats back (synchronizes). Raises
+        ZeroRecordError on a frozen record."""
+        self.state()
         return B.stats_from_tensor(self.stats)
 
     def _cast_slot(self, k: int, slot: torch.Tensor) -> None:
