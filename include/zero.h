@@ -304,6 +304,31 @@ typedef struct {
 int zero_adam_step(const zero_adam_args* args, void* stream);
 
 /*
+ * zero_adam_step for callers that cannot allocate device memory: code under
+ * stream or graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, arithmetic and errors as zero_adam_step, and the
+ * same p, m, v and slot bit for bit (the squared norm equal within rounding: its
+ * per-workgroup partials are grouped differently), except:
+ *  - workspace_dev must be NULL and ws_bytes 0 (ZERO_E_INVAL otherwise);
+ *  - the per-workgroup partial sums and, for more than 256 replicas, the device
+ *    table of replica pointers go into a scratch array compiled into the
+ *    library: ZERO_NOALLOC_SCRATCH_BYTES bytes on each GPU the library runs on,
+ *    held until the process ends. A launch uses at most 65,536 workgroups
+ *    (shards beyond 64M elements stride over their 1,024-element trips), so
+ *    every shard size and replica count the other checks accept fits; a launch
+ *    that would need more scratch is refused with ZERO_E_RANGE;
+ *  - the first call on a device looks the scratch address up
+ *    (hipGetSymbolAddress, no allocation): make it outside any stream capture;
+ *  - calls on one GPU share its scratch, which keeps what the last call wrote:
+ *    calls that overlap in time (other streams, other threads) race, so order
+ *    them on one stream. Nothing in it needs to start at zero: a launch writes
+ *    every partial its finalize reads, and the pointer table before its use.
+ * No hipMalloc, hipFree or allocating library routine is called.
+ */
+#define ZERO_NOALLOC_SCRATCH_BYTES 1581072
+int zero_adam_step_noalloc(const zero_adam_args* args, void* stream);
+
+/*
  * slot[i] = bf16 round-to-nearest-even(master[i]) for i in [0, shard_S): the
  * local part of the all-gather of updated parameters ("[REQUEST] Direct
  * Correspondence ...", "Problem"), used to initialise the slot and to restore

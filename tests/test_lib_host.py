@@ -175,6 +175,33 @@ def test_adam_step_validation(Z, change, status):
     assert Z.zero_last_error()
 
 
+@pytest.mark.parametrize("change,status", [
+    (dict(), -1), (dict(grad_f32=FAKE + 40960, p_in=FAKE + 8), -2),
+    (dict(grad_f32=FAKE + 40960, step_t=0), -1), (dict(replicas=[FAKE + 45056] * 1025), -3),
+    (dict(replicas=[FAKE + 45056], p_out=FAKE), -1), (dict(grad_f32=FAKE + 40960, stats=0), -1),
+])
+def test_adam_step_noalloc_validation(Z, change, status):
+    """The allocation-free step checks its arguments like zero_adam_step, on the
+    host, before it looks up its scratch or touches the GPU."""
+    a = base_args(Z, **change)
+    a.workspace_dev, a.ws_bytes = None, 0
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_adam_step_noalloc(a, stream=0)
+    assert e.value.status == status, str(e.value)
+
+
+def test_adam_step_noalloc_refuses_a_workspace(Z):
+    a = base_args(Z, grad_f32=FAKE + 40960)
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_adam_step_noalloc(a, stream=0)
+    assert e.value.status == -1 and "takes no workspace" in Z.zero_last_error()
+    a.workspace_dev, a.ws_bytes = None, 64
+    with pytest.raises(Z.ZeroError) as e:
+        Z.zero_adam_step_noalloc(a, stream=0)
+    assert e.value.status == -1
+    assert Z.ZERO_NOALLOC_SCRATCH_BYTES == 65536 * 24 + 8 * 1024 + 16
+
+
 def test_adam_step_small_workspace_rejected(Z):
     a = base_args(Z, grad_f32=FAKE + 40960)
     a.ws_bytes = 8

@@ -22,5 +22,6 @@ from ._binding import (  # noqa: F401
     zero_train_args, zero_train_step, make_train_args, device_state_from_tensor,
     ZERO_STATE_SPLIT, ZERO_STATE_TILED, ZERO_STATE_TILE, zero_gather_slot_tiled,
     zero_state_set_floats, zero_state_pack, zero_state_unpack, zero_device_state_flush,
-    ZeroRecordError, ZERO_RECORD_OK, ZERO_RECORD_E_COLLECT, ZERO_RECORD_E_MARKS)
+    ZeroRecordError, ZERO_RECORD_OK, ZERO_RECORD_E_COLLECT, ZERO_RECORD_E_MARKS,
+    zero_adam_step_noalloc, ZERO_NOALLOC_SCRATCH_BYTES)
 from .shard_step import DeviceShardStep, OffloadShardStep, ShardStep  # noqa: F401

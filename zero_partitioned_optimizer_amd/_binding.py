@@ -26,6 +26,7 @@ ZERO_COMMIT, ZERO_SKIP = 1, 2
 ZERO_MAX_REPLICAS = 1024
 ZERO_STATE_SPLIT, ZERO_STATE_TILED = 0, 1
 ZERO_STATE_TILE = 8192
+ZERO_NOALLOC_SCRATCH_BYTES = 1581072
 ZERO_RECORD_OK, ZERO_RECORD_E_COLLECT, ZERO_RECORD_E_MARKS = 0, 1, 2
 
 _STATUS = {0: "ZERO_OK", -1: "ZERO_E_INVAL", -2: "ZERO_E_ALIGN", -3: "ZERO_E_RANGE",
@@ -148,6 +149,7 @@ def lib() -> ctypes.CDLL:
     L.zero_workspace_bytes.restype = sz
     L.zero_reduce_shard.argtypes = [P(vp), i32, i32, i64, vp, i64, f64, vp, vp, vp, sz, vp]
     L.zero_adam_step.argtypes = [P(zero_adam_args), vp]
+    L.zero_adam_step_noalloc.argtypes = [P(zero_adam_args), vp]
     L.zero_gather_slot.argtypes = [vp, i64, vp, vp]
     L.zero_gather_slot_tiled.argtypes = [vp, i64, vp, vp]
     L.zero_state_set_floats.argtypes = [i64, i32]
@@ -169,7 +171,7 @@ def lib() -> ctypes.CDLL:
     L.zero_version.restype = ctypes.c_char_p
     for name in ("zero_layout_build", "zero_layout_info_get", "zero_layout_offsets",
                  "zero_layout_segments", "zero_layout_buckets", "zero_layout_mem_values",
-                 "zero_layout_mem_bytes", "zero_reduce_shard", "zero_adam_step",
+                 "zero_layout_mem_bytes", "zero_reduce_shard", "zero_adam_step", "zero_adam_step_noalloc",
                  "zero_gather_slot", "zero_gather_slot_tiled", "zero_state_pack",
                  "zero_state_unpack", "zero_commit_rule", "zero_device_state_init",
                  "zero_device_state_load", "zero_device_state_flush", "zero_train_step", "zero_train_step_part",
@@ -339,6 +341,12 @@ def _event(ev):
 
 def zero_adam_step(args: zero_adam_args, stream=None) -> None:
     _check(lib().zero_adam_step(ctypes.byref(args), _stream(stream)))
+
+
+def zero_adam_step_noalloc(args: zero_adam_args, stream=None) -> None:
+    """zero_adam_step with the library's own scratch: args carry no workspace
+    (make_adam_args(..., workspace=None))."""
+    _check(lib().zero_adam_step_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 def zero_gather_slot(master, shard_S: int, slot, stream=None) -> None:

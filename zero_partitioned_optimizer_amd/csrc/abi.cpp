@@ -143,8 +143,11 @@ int check_replicas(const char* fn, const void* const* replicas, int32_t n, zero_
     return ZERO_OK;
 }
 
+// lib_ws: the workspace is the library's own scratch (the allocation-free entry
+// point): only its size is checked, against the launch capped at max_grid.
 int check_common(const char* fn, int64_t S, const zero_bucket* buckets, int64_t n_buckets,
-                 const zero_stats* stats, const void* ws, size_t ws_bytes, int32_t n_rep) {
+                 const zero_stats* stats, const void* ws, size_t ws_bytes, int32_t n_rep,
+                 bool lib_ws = false, int max_grid = 0) {
     if (S < 0) {
         set_error("%s: shard_S=%lld is negative", fn, (long long)S);
         return ZERO_E_RANGE;
@@ -161,7 +164,7 @@ int check_common(const char* fn, int64_t S, const zero_bucket* buckets, int64_t 
         set_error("%s: bucket table %p is not 8-byte aligned", fn, (const void*)buckets);
         return ZERO_E_ALIGN;
     }
-    if (!stats || !ws) {
+    if (!stats || (!ws && !lib_ws)) {
         set_error("%s: stats_dev or workspace_dev is NULL", fn);
         return ZERO_E_INVAL;
     }
@@ -169,10 +172,14 @@ int check_common(const char* fn, int64_t S, const zero_bucket* buckets, int64_t 
         set_error("%s: stats_dev or workspace_dev is not 16-byte aligned", fn);
         return ZERO_E_ALIGN;
     }
-    const size_t need = (size_t)zk::grid_for(S, n_buckets, n_rep) * zk::kPartialBytes +
+    const size_t need = (size_t)zk::grid_for(S, n_buckets, n_rep, max_grid) * zk::kPartialBytes +
                         zk::rep_table_bytes(n_rep);
     if (ws_bytes < need) {
-        set_error("%s: workspace of %zu bytes < %zu needed", fn, ws_bytes, need);
+        if (lib_ws)
+            set_error("%s: the launch needs %zu bytes of scratch, more than the %zu this entry "
+                      "point holds", fn, need, ws_bytes);
+        else
+            set_error("%s: workspace of %zu bytes < %zu needed", fn, ws_bytes, need);
         return ZERO_E_RANGE;
     }
     return ZERO_OK;
@@ -271,8 +278,13 @@ int zero_reduce_shard(const void* const* replicas, int32_t n_replicas, zero_dtyp
     return hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
 }
 
-int zero_adam_step(const zero_adam_args* args, void* stream) {
-    static const char* fn = "zero_adam_step";
+}  // extern "C"
+
+// zero_adam_step, with the workspace either the caller's (a.workspace_dev,
+// a.ws_bytes) or, for noalloc, the library's scratch: then the checks see no
+// workspace buffer, the launch's grid is capped at kNoallocGrid, and the scratch
+// address is looked up only once every argument has passed.
+static int adam_step(const char* fn, const zero_adam_args* args, bool noalloc, void* stream) {
     if (!args) {
         set_error("%s: args is NULL", fn);
         return ZERO_E_INVAL;
@@ -283,9 +295,15 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
         set_error("%s: exactly one of replicas and grad_f32 must be given", fn);
         return ZERO_E_INVAL;
     }
+    if (noalloc && (a.workspace_dev || a.ws_bytes)) {
+        set_error("%s: takes no workspace (workspace_dev must be NULL and ws_bytes 0)", fn);
+        return ZERO_E_INVAL;
+    }
+    const int max_grid = noalloc ? zk::kNoallocGrid : 0;
     const int64_t S = a.shard_S;
-    int rc = check_common(fn, S, a.buckets_dev, a.n_buckets, a.stats_dev, a.workspace_dev, a.ws_bytes,
-                          fused ? a.n_replicas : 1);
+    int rc = check_common(fn, S, a.buckets_dev, a.n_buckets, a.stats_dev, a.workspace_dev,
+                          noalloc ? zk::kNoallocBytes : a.ws_bytes, fused ? a.n_replicas : 1,
+                          noalloc, max_grid);
     if (rc) return rc;
     if (fused) {
         rc = check_replicas(fn, a.replicas, a.n_replicas, a.grad_dtype, S);
@@ -366,11 +384,18 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
             return ZERO_E_INVAL;
         }
     }
+    void* ws = a.workspace_dev;
+    size_t ws_bytes = a.ws_bytes;
+    if (noalloc) {
+        rc = hip_status(zk::noalloc_scratch(&ws), fn);
+        if (rc) return rc;
+        ws_bytes = zk::kNoallocBytes;
+    }
     const void* one_rep[1] = {a.grad_f32};
     zk::StepDesc d{};
     d.replicas = fused ? a.replicas : one_rep;
     d.n_rep = fused ? a.n_replicas : 1;
-    d.rep_table = zk::rep_table_at(a.workspace_dev, a.ws_bytes, d.n_rep);
+    d.rep_table = zk::rep_table_at(ws, ws_bytes, d.n_rep);
     d.dtype = fused ? a.grad_dtype : ZERO_F32;
     d.S = S;
     d.buckets = a.n_buckets > 0 ? a.buckets_dev : nullptr;
@@ -388,10 +413,21 @@ int zero_adam_step(const zero_adam_args* args, void* stream) {
     // the unfused source is already averaged and unscaled: inv = 1 (x * 1 == x)
     d.sc = adam_scalars(a, fused ? a.n_replicas : 1, fused ? a.loss_scale : 1.0);
     d.stats = a.stats_dev;
-    d.partials = static_cast<zk::Partial*>(a.workspace_dev);
+    d.partials = static_cast<zk::Partial*>(ws);
     d.ev_begin = static_cast<hipEvent_t>(a.event_begin);
     d.ev_end = static_cast<hipEvent_t>(a.event_end);
+    d.max_grid = max_grid;
     return hip_status(zk::launch_step(d, static_cast<hipStream_t>(stream)), fn);
+}
+
+extern "C" {
+
+int zero_adam_step(const zero_adam_args* args, void* stream) {
+    return adam_step("zero_adam_step", args, false, stream);
+}
+
+int zero_adam_step_noalloc(const zero_adam_args* args, void* stream) {
+    return adam_step("zero_adam_step_noalloc", args, true, stream);
 }
 
 static int check_record_buffers(const char* fn, const zero_device_state* state_dev,

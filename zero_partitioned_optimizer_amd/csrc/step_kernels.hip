@@ -37,6 +37,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "zero_internal.h"
 
 #ifndef ZERO_NT
@@ -1354,6 +1357,40 @@ hipError_t launch_state_write(zero_device_state* s, const zero_device_state& rec
     hipLaunchKernelGGL(k_state_write, dim3((unsigned)grid), dim3(kBlock), 0, st, s, rec,
                        static_cast<uint64_t*>(ws), words);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// scratch of the allocation-free entry point
+// ---------------------------------------------------------------------------
+
+// zero_adam_step_noalloc takes its workspace -- the per-workgroup partials of the
+// flag and the squared norm, and the device table of replica pointers beyond
+// the kernel arguments -- from this array instead of a caller's buffer. Every
+// GPU the library runs on holds its own copy until the process ends. In host
+// code the name stands for the symbol, not for device memory: kernels get the
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kNoallocBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+    static std::atomic<void*> addr[kNoallocMaxDevices];
+    static std::mutex mu;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kNoallocMaxDevices) return hipErrorInvalidDevice;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 }  // namespace zk

@@ -98,6 +98,15 @@ static_assert(sizeof(Partial) == 16, "partials are 16 bytes");
 // tagged 64-bit words (device commit).
 constexpr size_t kPartialBytes = 24;
 
+// The allocation-free entry point's scratch (a file-scope device array in
+// step_kernels.hip, one copy per GPU): the partials of at most kNoallocGrid
+// workgroups and the replica pointer table at its end. Its launches cap their
+// grid at kNoallocGrid, so longer shards stride over their trips.
+constexpr int kNoallocGrid = 65536;
+constexpr size_t kNoallocBytes = (size_t)kNoallocGrid * kPartialBytes + kRepTableMax;
+constexpr int kNoallocMaxDevices = 64;
+static_assert(kNoallocBytes == ZERO_NOALLOC_SCRATCH_BYTES, "the scratch size of the ABI");
+
 // fp32 scalars of one update, each rounded once from double on the host.
 struct Scalars {
     float inv;                      // 1 / (N * loss_scale)
@@ -176,6 +185,9 @@ hipError_t launch_flush(zero_device_state* ctrl, zero_stats* stats, const Commit
 // Write rec to *s and clear the workspace (ws_bytes / 8 words), on st.
 hipError_t launch_state_write(zero_device_state* s, const zero_device_state& rec, void* ws,
                               size_t ws_bytes, hipStream_t st);
+// Device address of the allocation-free scratch on the current device
+// (kNoallocBytes bytes), looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace zk
 
