@@ -5,16 +5,20 @@ A step is one pass of the whole path over one rank's shard: fold the N resident
 gradient replicas in ring (slot) order, average and unscale, flag overflow and
 form the squared norm, Adam/AdamW on fp32 master / m / v, bf16 write into this
 rank's slot of the gathered parameter buffer, then the 16-byte stats read-back
-and the commit rule. The default workload is the GPT-2-small shard (rank 0 of
-N=8, 15,554,976 elements, bf16 replicas, AdamW); inputs are synthetic, seeded,
-and resident in HBM before the timed region starts.
+and the commit rule. The default workload is the Llama-70B-shaped shard, the
+largest configuration one GPU holds (rank 0 of N=32, 2,155,520,256 elements,
+32 bf16 replicas, AdamW; about 200 GB of HBM); inputs are synthetic, seeded,
+and resident in HBM before the timed region starts. The GPT-2-small, Llama-7B,
+ragged and tiny shards run with --config (GPT-2 and ragged with --flush-mall,
+since their working sets fit or partly fit the 256 MB Infinity Cache).
 
 Prints one JSON line. ``roofline`` is for the dominant kernel (the fused step
 kernel): algorithmic bytes per launch, S * (N * 2 + 26), over its mean duration
 measured with HIP events that the kernel's own launch carries on its stream
-(hipExtLaunchKernel: they take the kernel's start and end), on every tenth timed
-step by default (timed launches cost the stream a few microseconds each).
-``cpu_baseline`` is the CPU oracle timed on this host on the same shard.
+(hipExtLaunchKernel: they take the kernel's start and end), on every timed step
+by default. ``wall_gbps`` and ``wall_frac`` give the same bytes over the wall
+time per step (``ms_per_step``). ``cpu_baseline`` is the CPU oracle timed on
+this host on a sample of the same shard.
 """
 from __future__ import annotations
 
@@ -471,9 +475,9 @@ def unfused_bench(args, Z, w, S, reps, p0, gdt) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="gpt2s",
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama70b",
                     choices=["tiny", "gpt2s", "llama7b", "ragged", "llama70b"])
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--seed", type=int, default=None,
@@ -491,16 +495,13 @@ def main() -> int:
     ap.add_argument("--single-slot", action="store_true",
                     help="device commit with one slot buffer (restore kernel after an overflow) "
                          "instead of a double-buffered slot")
-    ap.add_argument("--event-every", type=int, default=10,
+    ap.add_argument("--event-every", type=int, default=1,
                     help="time the step kernel of every k-th timed step with HIP events its "
-                         "launch carries (a timed launch costs the stream a few us)")
+                         "launch carries (a timed launch costs the stream a few us, which "
+                         "shows on shards whose step takes ~100 us)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain device copy of 1 GiB three times "
                          "(the known-size reference for HBM byte counters under rocprofv3)")
-    ap.add_argument("--hbm-probe", action="store_true",
-                    help="also run the plain-stream HBM probe (read, write, copy, 2:1 and 5:1 "
-                         "read:write mixes, and a stream of the step's own shape at this shard's "
-                         "size) and report it beside the roofline")
     ap.add_argument("--fold", default="f32", choices=["f32", "bf16-wire"],
                     help="f32: the fold keeps its running sum in fp32; bf16-wire: rounded to "
                          "bf16 after every add, as a ring with bf16 buffers (bf16 replicas only)")
@@ -658,6 +659,11 @@ def main() -> int:
     bpe = w.N * w.grad_bytes + 26
     kernel_s = statistics.mean(kms) / 1e3
     achieved = S * bpe / kernel_s / 1e9
+    wall_gbps = S * bpe / (elapsed / K) / 1e9
+    # a working set that fits the 256 MB Infinity Cache (plus the replicas reused
+    # step after step) is partly served from it: FETCH_SIZE then counts L2 fills,
+    # not HBM reads
+    fits_mall = S * bpe < 256e6
     # the committed counter runs cover the default launch of each workload: device
     # commit, whole shard, fp32 fold; other launches report no traffic
     default_launch = not wire and args.commit == "device" and not args.bucket_elems
@@ -682,38 +688,22 @@ def main() -> int:
                    "mall_flushed": bool(args.flush_mall),
                    "slot": "single" if (args.single_slot or args.commit == "host") else "double",
                    "seed": w.seed},
-        "step_gbps": S * bpe / (elapsed / K) / 1e9,
-        # measured HBM bytes (the committed counter runs) over the same mean kernel time
+        "step_gbps": wall_gbps,
+        "wall_gbps": wall_gbps,
+        "wall_frac": wall_gbps / HBM_PEAK_GBS,
+        # measured bytes (the committed counter runs) over the same mean kernel time
         "physical_gbps": traffic / kernel_s / 1e9 if traffic else None,
         "kernel_us_mean": kernel_s * 1e6,
         "kernel_us_median": statistics.median(kms) * 1e3,
         "kernel_us_min": min(kms) * 1e3,
         "kernel_samples": len(kms),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_kind": ("L2 fill bytes (FETCH_SIZE, MALL hits included) + written bytes"
+                                      if fits_mall else "HBM bytes read + written")},
         "cpu_baseline": None,
         "skipped_steps": skipped,
     }
-    if args.hbm_probe:
-        import subprocess
-        probe = os.path.join(ROOT, "zero_partitioned_optimizer_amd", "hbm_probe")
-        log("hbm probe ...")
-        cmd = [probe]
-        # the step-shaped stream at this shard's size, where a second copy of the
-        # step's buffers fits beside the bench's own
-        if w.grad_dtype == "bf16" and S % 4 == 0 and S * bpe <= 80e9:
-            cmd += ["1024", str(S), str(w.N)]
-        res = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
-        if res.returncode != 0:
-            raise RuntimeError("hbm_probe failed: " + res.stderr)
-        hp = json.loads(res.stdout.strip().splitlines()[-1])
-        mix = "mix_2to1" if bpe - 26 <= 2 * 14 else "mix_5to1"
-        hp["step_kernel_vs_" + mix] = achieved / hp[mix]
-        key = "step_shape_tiled" if state == "tiled" else "step_shape"
-        if key in hp:
-            hp["step_kernel_vs_step_shape"] = achieved / hp[key]["gbps"]
-            hp["step_shape_layout"] = state
-        out["hbm_probe"] = hp
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

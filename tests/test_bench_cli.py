@@ -30,7 +30,7 @@ def test_world_size_above_one_is_refused():
 def test_help_lists_the_modes():
     r = run("--help")
     assert r.returncode == 0
-    for flag in ("--config", "--commit", "--hbm-probe", "--fold", "--overlap", "--offload",
+    for flag in ("--config", "--commit", "--fold", "--overlap", "--offload",
                  "--gather", "--flush-mall", "--cpu-seconds", "--calibrate-copy", "--graph",
                  "--unfused"):
         assert flag in r.stdout

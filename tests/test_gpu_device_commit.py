@@ -102,6 +102,43 @@ def test_gpt2_tiled_device_commit(Z, rank):
     run_device_protocol(Z, W.get("gpt2s"), rank, double_slot=True, tiled=True, steps=3)
 
 
+def test_gpt2_bench_launch_all_steps(Z):
+    """The bench's own launch and inputs -- GPT-2-small shard, rank 0, replicas and
+    master filled on the device by the bench's generators, device commit, tiled
+    state, two slots -- against the oracle for all 10 of the workload's steps,
+    every element."""
+    w = W.get("gpt2s")
+    rank = 0
+    lay, covered = layout_of(w, rank)
+    S = lay.S
+    p0 = torch.empty(S, dtype=torch.float32, device="cuda")
+    W.device_fill_params(p0, w, covered, rank)
+    ph = to_host(p0)
+    step = Z.DeviceShardStep(S, w.N, Z.ZERO_BF16, p0, lr=w.lr, beta1=w.beta1, beta2=w.beta2,
+                             eps=w.eps, weight_decay=w.wd, loss_scale=w.loss_scale,
+                             dynamic=w.dynamic_loss_scale, double_slot=True,
+                             state_layout=Z.ZERO_STATE_TILED)
+    tr = oracle.Trainer(ph.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
+                        oracle.f32_to_bf16(ph), loss_scale=w.loss_scale,
+                        dynamic=w.dynamic_loss_scale, nthreads=NTHREADS, **w.hyper())
+    reps = [torch.empty(S, dtype=torch.bfloat16, device="cuda") for _ in range(w.N)]
+    assert w.steps == 10
+    for s in range(w.steps):
+        say(f"gpt2s bench launch step {s}")
+        for j, r in enumerate(reps):
+            W.device_fill_replica(r, w, covered, rank, s, j)
+        dreps = [r.view(torch.int16) for r in reps]
+        step.step(dreps)
+        flag, sumsq = tr.step([to_host(r) for r in dreps])
+        rec = step.state()
+        st = step.last_stats()
+        assert flag == 0 and st.overflow == 0 and rec.t == tr.t == s + 1
+        assert sumsq_close(st.sumsq, sumsq), (st.sumsq, sumsq)
+        P, M, V = step.committed()
+        check_state(f"gpt2s bench launch s{s}", to_host(P), to_host(M), to_host(V),
+                    to_host(step.current_slot()), tr.p, tr.m, tr.v, tr.slot)
+
+
 def test_gpt2_device_equals_host_commit(Z):
     w = W.get("gpt2s")
     lay, covered = layout_of(w, 0)

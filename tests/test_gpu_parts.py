@@ -132,3 +132,41 @@ def test_parts_ragged_against_oracle(Z, rank):
         check_state(f"parts ragged r{rank} s{s}", to_host(P), to_host(M), to_host(V),
                     to_host(step.current_slot()), tr.p, tr.m, tr.v, tr.slot)
     assert sum(flags) == 1
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_parts_multi_trip_grid_stride(Z, tiled):
+    """4,096 parts cap each part's grid at 4,194,304 / 4,096 = 1,024 workgroups.
+    The last part, 1,537,037 elements (1,501 trips of 1,024 elements, then 3
+    quads and 1 element), runs on 751 workgroups that stride over two trips
+    each; the one with a single trip (1,501 mod 751 = 750) also takes the quads
+    after the last trip and the S % 4 tail. 4,094 empty parts come first, then an
+    8,192-element part. Against the whole-shard step and the oracle, two steps."""
+    first = 8192
+    SS = first + 1501 * 1024 + 13
+    ends = [0] * 4094 + [first, SS]
+    n = 8
+    rng = np.random.default_rng(99)
+    p0h = (rng.standard_normal(SS) * 0.02).astype(np.float32)
+    kw = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, loss_scale=1.0,
+              double_slot=True, state_layout=Z.ZERO_STATE_TILED if tiled else Z.ZERO_STATE_SPLIT)
+    parts = Z.DeviceShardStep(SS, n, Z.ZERO_BF16, to_dev(p0h), **kw)
+    whole = Z.DeviceShardStep(SS, n, Z.ZERO_BF16, to_dev(p0h), **kw)
+    tr = oracle.Trainer(p0h.copy(), np.zeros(SS, np.float32), np.zeros(SS, np.float32),
+                        oracle.f32_to_bf16(p0h), loss_scale=1.0, dynamic=False, nthreads=NTHREADS,
+                        lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.01)
+    for s in range(2):
+        say(f"parts multi-trip tiled={tiled} step {s}")
+        hreps = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(SS) * 1e-3))
+                 for _ in range(n)]
+        dreps = [to_dev(r) for r in hreps]
+        parts.step_parts(dreps, ends)
+        whole.step(dreps)
+        flag, sumsq = tr.step(hreps)
+        assert flag == 0
+        same(whole, parts, ("multi-trip", tiled, s))
+        rec = parts.state()
+        assert rec.t == s + 1 and sumsq_close(rec.last_sumsq, sumsq)
+        P, M, V = parts.committed()
+        check_state(f"parts multi-trip tiled={tiled} s{s}", to_host(P), to_host(M), to_host(V),
+                    to_host(parts.current_slot()), tr.p, tr.m, tr.v, tr.slot)

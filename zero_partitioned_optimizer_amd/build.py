@@ -29,17 +29,14 @@ def hipcc() -> str:
     return "hipcc"
 
 
-PROBE = os.path.join(PKG, "hbm_probe")
-
-
 def _run(cmd):
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + proc.stdout + proc.stderr)
 
 
-def build(out: str = LIB, extra=(), probe: bool = True) -> str:
-    """Compile every source into ``out`` (always recompiles), and the HBM probe."""
+def build(out: str = LIB, extra=()) -> str:
+    """Compile every source into ``out`` (always recompiles)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     objs = []
@@ -53,10 +50,6 @@ def build(out: str = LIB, extra=(), probe: bool = True) -> str:
     for obj in objs:
         os.remove(obj)
     os.replace(out + ".tmp", out)
-    if probe:
-        flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
-        _run([hipcc(), *flags, os.path.join(CSRC, "hbm_probe.hip"), "-o", PROBE + ".tmp"])
-        os.replace(PROBE + ".tmp", PROBE)
     return out
 
 
