@@ -19,9 +19,9 @@ from gpu_util import NTHREADS, check_state, say, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-def test_collect_timeout_freezes_record(Z):
-    S, N = 20_011, 4
-    rng = np.random.default_rng(7)
+@pytest.mark.parametrize("S,N", [(20_011, 4), ((1 << 22) + 517, 16)])
+def test_collect_timeout_freezes_record(Z, S, N):
+    rng = np.random.default_rng(7 + N)
     p0 = (rng.standard_normal(S) * 0.02).astype(np.float32)
     reps = [[np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * 1e-3)) for _ in range(N)]
             for _ in range(3)]

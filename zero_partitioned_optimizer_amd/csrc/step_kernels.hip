@@ -360,6 +360,17 @@ __device__ __forceinline__ uint64_t uni64(uint64_t x) {
     return ((uint64_t)uni32((uint32_t)(x >> 32)) << 32) | uni32((uint32_t)x);
 }
 
+// Workgroup barrier for LDS traffic: every wave's LDS operations before it are
+// done and visible to every wave after it. Unlike __syncthreads, whose workgroup
+// fence also waits for each wave's outstanding global loads and stores, it lets
+// the state and slot stores of a finished tile drain while the workgroup
+// reduces its partial and ends.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // The committed state as a launch sees it: the record (state after its `seq`
 // finalized steps) with the pending step -- the one that ran after them, if
 // pending_n > 0 -- folded in by the skip rule: a clean pending step advances the
@@ -629,7 +640,7 @@ __device__ __forceinline__ void block_reduce(double& sq, uint32_t& bad, uint32_t
         s_bad[w] = bad;
         s_badb[w] = badb;
     }
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x == 0) {
         double t = s_sq[0];
         uint32_t b = s_bad[0], bb = s_badb[0];
@@ -674,9 +685,9 @@ __device__ __forceinline__ uint32_t block_or(uint32_t x) {
     __shared__ uint32_t s_or[kBlock / 64];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x |= __shfl_xor(x, off, 64);
-    __syncthreads();
+    lds_barrier();
     if ((threadIdx.x & 63) == 0) s_or[threadIdx.x >> 6] = x;
-    __syncthreads();
+    lds_barrier();
     uint32_t r = 0u;
 #pragma unroll
     for (int w = 0; w < kBlock / 64; ++w) r |= s_or[w];
@@ -820,17 +831,34 @@ __device__ __forceinline__ void finalize_launch(const KParams& a, uint32_t tag) 
                                        (uint32_t)a.collect_n);
 }
 
+// Device commit: post this workgroup's start mark once every one of its waves
+// has read the record. Each wave's checksum of the words it read goes through
+// LDS (its write waits for those reads), and thread 0 stores the step's number
+// with the XOR of all of them, so the mark cannot become visible before any
+// wave's reads are done; workgroup 0 rewrites the record only once every mark of
+// the launch is in. (A mark posted by wave 0 alone would not cover a sibling wave
+// whose record loads were still in flight.)
+__device__ __forceinline__ void post_mark(const KParams& a, const Res& rs) {
+    constexpr int kWaves = kBlock / 64;
+    __shared__ uint32_t s_mark[kWaves];
+    if ((threadIdx.x & 63) == 0) s_mark[threadIdx.x >> 6] = (uint32_t)rs.mark;
+    lds_barrier();
+    if (threadIdx.x == 0) {
+        uint32_t x = 0u;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) x ^= s_mark[k];
+        __hip_atomic_store(a.ws_started + ((int64_t)a.part_base + blockIdx.x),
+                           ((uint64_t)rs.tag << 32) | x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL, bool TILED, int ROWS>
 __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
     const Res rs = resolve<CTRL, TILED>(a);
     if constexpr (CTRL) {
         // a frozen record (a wait of an earlier launch ran out): no work at all
         if (rs.err) return;
-        // this workgroup has read the record (the mark's value depends on every
-        // word it read); workgroup 0 may rewrite it once all marks are in
-        if (threadIdx.x == 0)
-            __hip_atomic_store(a.ws_started + ((int64_t)a.part_base + blockIdx.x), rs.mark,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        post_mark(a, rs);
     }
     double sq = 0.0;
     uint32_t bad = 0u, badb = 0u;
@@ -895,7 +923,7 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
             if (lane >= off) incl += y;
         }
         if (lane == 63) wave_sum[wv] = incl;
-        __syncthreads();
+        lds_barrier();
         int64_t run = incl - mine;
         for (int w = 0; w < wv; ++w) run += wave_sum[w];
         if (threadIdx.x == kBlock - 1) first[nbk] = run + mine;
@@ -906,7 +934,7 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
             first[b] = run;
             run += c;
         }
-        __syncthreads();
+        lds_barrier();
         const int64_t total = first[nbk];
         for (int64_t j = blockIdx.x; j < total; j += gridDim.x) {
             // the bucket holding chunk j: first[lb] <= j < first[lb + 1]
