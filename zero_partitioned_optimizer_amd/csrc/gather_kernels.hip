@@ -11,7 +11,9 @@
 // tasks of kGatherChunk output elements, so a launch has about one task per
 // 16 KB of bf16 output whatever the tensor sizes; pieces whose source and
 // destination share their 16-byte alignment move as 16-byte vectors, others
-// element by element (still coalesced).
+// element by element (still coalesced). Up to kGatherTensors tensors go into one
+// launch (as many as the kernel argument block holds), so a model's fetch takes
+// few launches, each with its own tail.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,7 +21,7 @@
 
 namespace zk {
 
-constexpr int kGatherTensors = 32;                      // tensors per launch
+constexpr int kGatherTensors = 48;                      // tensors per launch
 constexpr int64_t kGatherChunk = 8192;                  // output elements per task
 constexpr int64_t kGatherMaxTasks = int64_t(1) << 20;   // workgroups per gather launch
 
@@ -36,6 +38,7 @@ struct GatherParams {
     int64_t first_task[kGatherTensors + 1];   // prefix sums of the tensors' task counts
     int64_t task_base;                        // task of workgroup 0 of this launch
 };
+static_assert(sizeof(GatherParams) <= 4096, "the gather arguments fit the kernel argument block");
 
 // len elements from src to dst by the whole workgroup. Each lane issues up to
 // four 16-byte loads before its stores, so a full task (16 KB of bf16) is one
