@@ -1,0 +1,149 @@
+"""GPU parity at bucket edges that cut quads (4-element groups).
+
+A bucket-table launch updates exactly the elements inside its buckets ("ZeRO
+Optimizer", Communication Optimization: gradients are reduced and applied in
+buckets). The kernel takes a quad cut by a bucket edge with the same vector
+loads as a whole one and keeps only the bucket's elements, so these tests put
+the edges everywhere a quad can be cut:
+- buckets of 1, 2 and 3 elements, both edges inside one quad;
+- neighbouring buckets sharing a quad (two workgroups writing one quad);
+- a bucket that ends at S with S % 4 != 0 (the shard's last partial quad);
+- an empty bucket.
+NaN and inf sit in the excluded elements of cut quads (in every replica slot the
+case draws); they must neither raise the overflow flag nor reach the norm.
+Elements outside the buckets keep their sentinel. The short table runs one
+workgroup per bucket; the long-bucket table is cut into chunks over the grid.
+Checked: the fused step (p, m, v, slot bit for bit), the reduce-only launch (g
+bit for bit), the device-commit step in the tiled layout (committed state inside
+the buckets). Inputs from numpy's seeded generator; expected values from oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import NTHREADS, assert_bitexact, say, sumsq_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+# (offset, length) tables; S % 4 == 3 in both
+SHORT_S = 4003
+SHORT = [(1, 1), (2, 2), (5, 2), (8, 4), (13, 10), (30, 900), (50 + 900, 0), (1000, 3),
+         (3990, 9), (3999, 1), (4000, 3)]
+SHORT_BAD = [0, 4, 7, 12, 23, 1003]                       # outside, in cut quads
+LONG_S = 300_003
+LONG = [(3, 100_000), (100_005, 150_001), (250_007, 49_993), (300_000, 3)]
+LONG_BAD = [0, 2, 100_003, 100_004, 250_006]
+
+CASES = [("short", "bf16", 5), ("short", "f32", 3), ("short", "bf16", 20), ("short", "wire", 9),
+         ("long", "bf16", 5), ("long", "bf16", 20), ("long", "f32", 3)]
+
+
+def _case(Z, table_kind, kind, N):
+    S, table, bad = ((SHORT_S, SHORT, SHORT_BAD) if table_kind == "short"
+                     else (LONG_S, LONG, LONG_BAD))
+    rng = np.random.default_rng(4000 + N + len(kind) + S)
+    sample = [rng.standard_normal(S) * 4e-3 for _ in range(N)]
+    for i, e in enumerate(bad):
+        sample[(3 * i) % N][e] = (np.nan, np.inf, -np.inf)[i % 3]
+    if kind == "f32":
+        reps = [x.astype(np.float32) for x in sample]
+    else:
+        reps = [np.asarray(W._bf16_bits_from_f32(x)) for x in sample]
+    inside = np.zeros(S, bool)
+    for o, ln in table:
+        inside[o:o + ln] = True
+    assert not inside[bad].any()
+    raw = np.array([(o, ln, 0) for o, ln in table],
+                   dtype=np.dtype([("off", "<i8"), ("len", "<i4"), ("t", "<i4")]))
+    buckets = torch.from_numpy(raw.view(np.uint8).copy()).to("cuda")
+    gdt = {"bf16": Z.ZERO_BF16, "f32": Z.ZERO_F32, "wire": Z.ZERO_BF16_WIRE}[kind]
+    g, _, _ = oracle.reduce(reps, wire=(kind == "wire"))
+    return S, table, rng, reps, inside, buckets, gdt, g
+
+
+def _stats(Z, t):
+    torch.cuda.synchronize()
+    return Z.stats_from_tensor(t)
+
+
+@pytest.mark.parametrize("table_kind,kind,N", CASES)
+def test_bucket_edges_fused_and_reduce(Z, table_kind, kind, N):
+    S, table, rng, reps, inside, buckets, gdt, g = _case(Z, table_kind, kind, N)
+    say(f"bucket edges {table_kind} {kind} N={N} S={S} buckets={len(table)}")
+    want_sumsq = float(np.sum(g[inside].astype(np.float64) ** 2))
+    assert np.isfinite(g[inside]).all()
+    p = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(S) * 1e-4).astype(np.float32)
+    v = ((rng.standard_normal(S) * 1e-4) ** 2).astype(np.float32)
+    hy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    po, mo, vo, so = oracle.adam(g, p, m, v, t=3, wd=0.01, **hy)
+    dreps = [to_dev(r) for r in reps]
+    sent = np.full(S, 0x7FBADBAD, np.uint32).view(np.float32)
+    P_out, M_out, V_out = (to_dev(sent.copy()) for _ in range(3))
+    slot = to_dev(np.full(S, 0x5A5A, np.uint16))
+    stats = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(Z.zero_workspace_bytes(S), dtype=torch.uint8, device="cuda")
+    a = Z.make_adam_args(replicas=dreps, grad_dtype=gdt, p_in=to_dev(p), m_in=to_dev(m),
+                         v_in=to_dev(v), p_out=P_out, m_out=M_out, v_out=V_out, slot=slot,
+                         shard_S=S, buckets=buckets, n_buckets=len(table), loss_scale=1.0,
+                         step_t=3, weight_decay=0.01, stats=stats, workspace=ws, **hy)
+    Z.zero_adam_step(a)
+    st = _stats(Z, stats)
+    assert st.overflow == 0 and st.bad_buckets == 0
+    assert sumsq_close(st.sumsq, want_sumsq, rel=1e-12), (st.sumsq, want_sumsq)
+    for name, got, want in (("p", P_out, po), ("m", M_out, mo), ("v", V_out, vo), ("slot", slot, so)):
+        h = to_host(got)
+        assert_bitexact(f"{table_kind} {kind} N={N} {name}", h[inside], want[inside])
+        if name == "slot":
+            assert np.all(h[~inside] == 0x5A5A)
+        else:
+            assert np.all(h[~inside].view(np.uint32) == 0x7FBADBAD), name
+    # reduce-only launch over the same table: g inside, sentinel outside
+    G = to_dev(sent.copy())
+    stats.zero_()
+    Z.zero_reduce_shard(dreps, gdt, S, stats, ws, buckets=buckets, n_buckets=len(table), grad_out=G)
+    st = _stats(Z, stats)
+    assert st.overflow == 0 and st.bad_buckets == 0
+    assert sumsq_close(st.sumsq, want_sumsq, rel=1e-12)
+    gh = to_host(G)
+    assert_bitexact(f"{table_kind} {kind} N={N} g", gh[inside], g[inside])
+    assert np.all(gh[~inside].view(np.uint32) == 0x7FBADBAD)
+
+
+@pytest.mark.parametrize("table_kind", ["short", "long"])
+def test_bucket_edges_device_commit_tiled(Z, table_kind):
+    """Two device-commit steps over the table in the tiled layout; the second step's
+    replicas carry an inf inside a bucket, so it is skipped."""
+    N = 6
+    S, table, rng, reps, inside, buckets, gdt, g = _case(Z, table_kind, "bf16", N)
+    say(f"bucket edges device commit tiled {table_kind} S={S}")
+    p0 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    zhy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    st = Z.DeviceShardStep(S, N, gdt, to_dev(p0), loss_scale=1.0, double_slot=True,
+                           state_layout=Z.ZERO_STATE_TILED, buckets=buckets, n_buckets=len(table),
+                           **zhy)
+    hy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.01)
+    tr = oracle.Trainer(p0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32),
+                        oracle.f32_to_bf16(p0), loss_scale=1.0, nthreads=NTHREADS, **hy)
+    first_inside = int(np.flatnonzero(inside)[17])
+    for s in range(3):
+        if s == 0:
+            rs = reps
+        else:
+            rs = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * 4e-3)) for _ in range(N)]
+        if s == 1:
+            rs[N - 1][first_inside] = np.asarray(W._bf16_bits_from_f32(np.array([np.inf])))[0]
+        # the oracle sees only the buckets' elements: outside them the step reads nothing
+        masked = [np.where(inside, r, np.uint16(0)) for r in rs]
+        flag, sumsq = tr.step(masked)
+        assert flag == (1 if s == 1 else 0)
+        st.step([to_dev(r) for r in rs])
+        rec = st.state()
+        assert rec.last_overflow == flag and rec.t == tr.t
+        if not flag:
+            assert sumsq_close(rec.last_sumsq, sumsq), (rec.last_sumsq, sumsq)
+        got = (*st.committed(), st.current_slot())
+        for name, gv, want in zip(("p", "m", "v", "slot"), got, (tr.p, tr.m, tr.v, tr.slot)):
+            assert_bitexact(f"{table_kind} step {s} {name}", to_host(gv)[inside], want[inside])

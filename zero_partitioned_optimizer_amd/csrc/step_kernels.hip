@@ -498,11 +498,15 @@ struct Outs {
 
 // ROWS quads at q0, q0 + qs, ...: fold, average, flag, g^2 and (with ADAM) the
 // update of 4*ROWS elements of this lane. Reduce-only launches store g here;
-// the update is returned in `o` for quads_store.
-template <typename RT, bool ADAM, bool WRITE_G, bool TILED, int ROWS>
+// the update is returned in `o` for quads_store. MASKED (one row): only the
+// elements whose bits are set in `mask` (bit c: element 4*q0 + c) count towards
+// the flag and g^2 and are stored; the others are loaded and computed, since the
+// quad lies inside the shard's buffers, and dropped.
+template <typename RT, bool ADAM, bool WRITE_G, bool TILED, int ROWS, bool MASKED = false>
 __device__ __forceinline__ void quads_compute(const KParams& a, const Res& rs, int64_t q0,
                                               int64_t qs, double& sq, uint32_t& bad,
-                                              Outs<ROWS>& o) {
+                                              Outs<ROWS>& o, uint32_t mask = 0xFu) {
+    static_assert(!MASKED || ROWS == 1, "masked quads come one at a time");
     f32x4 p[ROWS], m[ROWS], v[ROWS];
     if constexpr (ADAM) {
 #pragma unroll
@@ -521,11 +525,20 @@ __device__ __forceinline__ void quads_compute(const KParams& a, const Res& rs, i
         f32x4 g = acc[r] * rs.sc.inv;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            bad |= nonfinite(g[c]) ? 1u : 0u;
+            const bool in = !MASKED || ((mask >> c) & 1u);
+            bad |= (in && nonfinite(g[c])) ? 1u : 0u;
             const double gd = (double)g[c];
-            sq += gd * gd;
+            sq += in ? gd * gd : 0.0;
         }
-        if constexpr (WRITE_G) st(reinterpret_cast<f32x4*>(a.g_out) + q, g);
+        if constexpr (WRITE_G) {
+            if (!MASKED || mask == 0xFu) {
+                st(reinterpret_cast<f32x4*>(a.g_out) + q, g);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if ((mask >> c) & 1u) a.g_out[q * 4 + c] = g[c];
+            }
+        }
         if constexpr (ADAM) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -539,9 +552,24 @@ __device__ __forceinline__ void quads_compute(const KParams& a, const Res& rs, i
     }
 }
 
-template <bool TILED, int ROWS>
+template <bool TILED, int ROWS, bool MASKED = false>
 __device__ __forceinline__ void quads_store(const Res& rs, int64_t q0, int64_t qs,
-                                            const Outs<ROWS>& o) {
+                                            const Outs<ROWS>& o, uint32_t mask = 0xFu) {
+    if constexpr (MASKED) {
+        if (mask != 0xFu) {
+            // a quad cut by a bucket edge: its own elements one by one
+            const int64_t qt = state_q<TILED>(q0);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (!((mask >> c) & 1u)) continue;
+                rs.p_out[qt * 4 + c] = o.pn[0][c];
+                rs.m_out[qt * 4 + c] = o.m1[0][c];
+                rs.v_out[qt * 4 + c] = o.v1[0][c];
+                if (rs.slot) rs.slot[q0 * 4 + c] = (uint16_t)f2bf(o.pn[0][c]);
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
         const int64_t q = q0 + r * qs;
@@ -559,12 +587,12 @@ __device__ __forceinline__ void quads_store(const Res& rs, int64_t q0, int64_t q
 }
 
 // The whole step for ROWS quads of this lane.
-template <typename RT, bool ADAM, bool WRITE_G, bool TILED, int ROWS>
+template <typename RT, bool ADAM, bool WRITE_G, bool TILED, int ROWS, bool MASKED = false>
 __device__ __forceinline__ void quads(const KParams& a, const Res& rs, int64_t q0, int64_t qs,
-                                      double& sq, uint32_t& bad) {
+                                      double& sq, uint32_t& bad, uint32_t mask = 0xFu) {
     Outs<ROWS> o;
-    quads_compute<RT, ADAM, WRITE_G, TILED, ROWS>(a, rs, q0, qs, sq, bad, o);
-    if constexpr (ADAM) quads_store<TILED, ROWS>(rs, q0, qs, o);
+    quads_compute<RT, ADAM, WRITE_G, TILED, ROWS, MASKED>(a, rs, q0, qs, sq, bad, o, mask);
+    if constexpr (ADAM) quads_store<TILED, ROWS, MASKED>(rs, q0, qs, o, mask);
 }
 
 // One element, for bucket edges and the shard tail.
@@ -603,23 +631,29 @@ __device__ __forceinline__ void one_elem(const KParams& a, const Res& rs, int64_
     }
 }
 
-// All elements of [lo, hi) by the threads of one workgroup.
-template <typename RT, bool ADAM, bool WRITE_G, bool TILED, int ROWS>
+// All elements of [lo, hi) by the threads of one workgroup, one quad per lane
+// per round. A quad cut by an edge of the range goes through the same loads as
+// the others, masked to the range's elements, so the lanes on the edges make the
+// same memory round trips as the rest; only the shard's last partial quad (when
+// S % 4 != 0), which the buffers do not hold whole, goes element by element.
+template <typename RT, bool ADAM, bool WRITE_G, bool TILED>
 __device__ __forceinline__ void range(const KParams& a, const Res& rs, int64_t lo, int64_t hi,
                                       double& sq, uint32_t& bad) {
+    if (lo >= hi) return;
     const int tid = threadIdx.x;
-    const int64_t qa = (lo + 3) >> 2;       // first whole quad
-    const int64_t qb = hi >> 2;             // one past the last whole quad
-    if (qa >= qb) {
-        for (int64_t e = lo + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
-        return;
+    const int64_t qw = a.S >> 2;            // the shard's whole quads
+    int64_t qhi = (hi + 3) >> 2;            // one past the quad holding element hi - 1
+    if (qhi > qw) qhi = qw;
+    for (int64_t q = (lo >> 2) + tid; q < qhi; q += kBlock) {
+        const int64_t e = q << 2;
+        uint32_t mask = 0xFu;
+        if (e < lo) mask &= 0xFu << (uint32_t)(lo - e);
+        if (e + 4 > hi) mask &= 0xFu >> (uint32_t)(e + 4 - hi);
+        quads<RT, ADAM, WRITE_G, TILED, 1, true>(a, rs, q, 0, sq, bad, mask);
     }
-    for (int64_t e = lo + tid; e < qa * 4; e += kBlock) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
-    int64_t q = qa + tid;
-    for (; q + (ROWS - 1) * kBlock < qb; q += ROWS * kBlock)
-        quads<RT, ADAM, WRITE_G, TILED, ROWS>(a, rs, q, kBlock, sq, bad);
-    for (; q < qb; q += kBlock) quads<RT, ADAM, WRITE_G, TILED, 1>(a, rs, q, 0, sq, bad);
-    for (int64_t e = qb * 4 + tid; e < hi; e += kBlock) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
+    const int64_t et = qw << 2;
+    for (int64_t e = (lo > et ? lo : et) + tid; e < hi; e += kBlock)
+        one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
 }
 
 // Wave64 shuffles, then LDS across the workgroup's waves, in a fixed order.
@@ -951,7 +985,7 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
             int64_t hi = k == last ? bhi : ((blo + (k + 1) * kChunk) & ~int64_t(63));
             if (lo < blo) lo = blo;
             if (hi < blo) hi = blo;
-            range<RT, ADAM, WRITE_G, TILED, ROWS>(a, rs, lo, hi, sq, bad);
+            range<RT, ADAM, WRITE_G, TILED>(a, rs, lo, hi, sq, bad);
         }
     } else {
         for (int64_t b = blockIdx.x; b < a.n_buckets; b += gridDim.x) {
@@ -961,7 +995,7 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
                 if (threadIdx.x == 0) badb += 1u;
                 continue;
             }
-            range<RT, ADAM, WRITE_G, TILED, ROWS>(a, rs, lo, lo + len, sq, bad);
+            range<RT, ADAM, WRITE_G, TILED>(a, rs, lo, lo + len, sq, bad);
         }
     }
     block_reduce(sq, bad, badb);
