@@ -230,8 +230,11 @@ size_t zero_workspace_bytes(int64_t shard_S);
  *   the workspace with a small kernel on `stream`, and the step reads them
  *   there (the workspace must then hold that table after its partials).
  * buckets_dev, n_buckets: device bucket table; only elements inside buckets are
- *   read and written (NULL, 0 = the whole shard). Buckets must not overlap;
- *   one that leaves [0, shard_S) is skipped and counted in stats->bad_buckets.
+ *   written and count towards the flag and the norm (NULL, 0 = the whole
+ *   shard). A group of four elements (4k .. 4k+3) cut by a bucket edge is read
+ *   whole, so up to three elements beyond each edge, inside the shard, are read
+ *   and never written. Buckets must not overlap; one that leaves [0, shard_S)
+ *   is skipped and counted in stats->bad_buckets.
  * grad_out_dev: fp32 [shard_S] output of g, or NULL.
  * stats_dev: device zero_stats. workspace_dev/ws_bytes: >= zero_workspace_bytes.
  * The outputs (grad_out, stats, workspace) must not overlap one another, a

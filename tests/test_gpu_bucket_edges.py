@@ -11,8 +11,13 @@ the edges everywhere a quad can be cut:
 - an empty bucket.
 NaN and inf sit in the excluded elements of cut quads (in every replica slot the
 case draws); they must neither raise the overflow flag nor reach the norm.
-Elements outside the buckets keep their sentinel. The short table runs one
-workgroup per bucket; the long-bucket table is cut into chunks over the grid.
+Elements outside the buckets keep their sentinel.
+
+The short table (11 buckets over 4,003 elements) runs one workgroup per bucket.
+Tables of a few long buckets are cut into chunks dealt over the grid: the long
+table (and the same table in reverse order), the mid table over 3,000,003
+elements, and a 70,000,003-element shard through the allocation-free entry
+point, whose grid cap makes every workgroup take several chunks.
 Checked: the fused step (p, m, v, slot bit for bit), the reduce-only launch (g
 bit for bit), the device-commit step in the tiled layout (committed state inside
 the buckets). Inputs from numpy's seeded generator; expected values from oracle.
@@ -27,7 +32,7 @@ from gpu_util import NTHREADS, assert_bitexact, say, sumsq_close, to_dev, to_hos
 
 pytestmark = pytest.mark.gpu
 
-# (offset, length) tables; S % 4 == 3 in both
+# (offset, length) tables; S % 4 == 3 in all of them
 SHORT_S = 4003
 SHORT = [(1, 1), (2, 2), (5, 2), (8, 4), (13, 10), (30, 900), (50 + 900, 0), (1000, 3),
          (3990, 9), (3999, 1), (4000, 3)]
@@ -35,14 +40,19 @@ SHORT_BAD = [0, 4, 7, 12, 23, 1003]                       # outside, in cut quad
 LONG_S = 300_003
 LONG = [(3, 100_000), (100_005, 150_001), (250_007, 49_993), (300_000, 3)]
 LONG_BAD = [0, 2, 100_003, 100_004, 250_006]
+MID_S = 3_000_003
+MID = [(2, 1_000_000), (1_000_006, 999_990), (2_000_064, 999_936), (3_000_000, 3)]
+MID_BAD = [0, 1, 1_000_002, 1_000_005, 1_999_996, 2_000_000, 2_000_063]
+TABLES = {"short": (SHORT_S, SHORT, SHORT_BAD), "long": (LONG_S, LONG, LONG_BAD),
+          "long_rev": (LONG_S, LONG[::-1], LONG_BAD), "mid": (MID_S, MID, MID_BAD)}
 
 CASES = [("short", "bf16", 5), ("short", "f32", 3), ("short", "bf16", 20), ("short", "wire", 9),
-         ("long", "bf16", 5), ("long", "bf16", 20), ("long", "f32", 3)]
+         ("long", "bf16", 5), ("long", "bf16", 20), ("long", "f32", 3), ("long_rev", "bf16", 5),
+         ("mid", "bf16", 5), ("mid", "wire", 9), ("mid", "f32", 3), ("mid", "bf16", 33)]
 
 
 def _case(Z, table_kind, kind, N):
-    S, table, bad = ((SHORT_S, SHORT, SHORT_BAD) if table_kind == "short"
-                     else (LONG_S, LONG, LONG_BAD))
+    S, table, bad = TABLES[table_kind]
     rng = np.random.default_rng(4000 + N + len(kind) + S)
     sample = [rng.standard_normal(S) * 4e-3 for _ in range(N)]
     for i, e in enumerate(bad):
@@ -112,7 +122,7 @@ def test_bucket_edges_fused_and_reduce(Z, table_kind, kind, N):
     assert np.all(gh[~inside].view(np.uint32) == 0x7FBADBAD)
 
 
-@pytest.mark.parametrize("table_kind", ["short", "long"])
+@pytest.mark.parametrize("table_kind", ["short", "long", "mid"])
 def test_bucket_edges_device_commit_tiled(Z, table_kind):
     """Two device-commit steps over the table in the tiled layout; the second step's
     replicas carry an inf inside a bucket, so it is skipped."""
@@ -147,3 +157,55 @@ def test_bucket_edges_device_commit_tiled(Z, table_kind):
         got = (*st.committed(), st.current_slot())
         for name, gv, want in zip(("p", "m", "v", "slot"), got, (tr.p, tr.m, tr.v, tr.slot)):
             assert_bitexact(f"{table_kind} step {s} {name}", to_host(gv)[inside], want[inside])
+
+
+def test_chunks_over_a_capped_grid_noalloc(Z):
+    """The allocation-free entry point caps the grid at 65,536 workgroups, so the
+    68,361 chunks of a 70,000,003-element shard's four buckets are dealt over it
+    more than once. Bucket edges cut quads, a NaN sits in a 64-element gap
+    between buckets, the last bucket ends at S (S % 4 == 3)."""
+    S, N = 70_000_003, 2
+    table = [(0, 10_000_001), (10_000_005, 30_000_000), (40_000_069, 29_999_931), (70_000_000, 3)]
+    bad = [10_000_002, 10_000_004, 40_000_040, 40_000_068]
+    rng = np.random.default_rng(4242)
+    say(f"chunks over a capped grid: S={S} N={N} buckets={len(table)}")
+    sample = [rng.standard_normal(S, dtype=np.float32) * np.float32(4e-3) for _ in range(N)]
+    for i, e in enumerate(bad):
+        sample[i % N][e] = np.nan
+    reps = [np.asarray(W._bf16_bits_from_f32(x)) for x in sample]
+    del sample
+    inside = np.zeros(S, bool)
+    for o, ln in table:
+        inside[o:o + ln] = True
+    assert not inside[bad].any()
+    raw = np.array([(o, ln, 0) for o, ln in table],
+                   dtype=np.dtype([("off", "<i8"), ("len", "<i4"), ("t", "<i4")]))
+    buckets = torch.from_numpy(raw.view(np.uint8).copy()).to("cuda")
+    p = rng.standard_normal(S, dtype=np.float32) * np.float32(0.02)
+    z = np.zeros(S, np.float32)
+    g, _, _ = oracle.reduce(reps, nthreads=NTHREADS)
+    want_sumsq = float(np.sum(g[inside].astype(np.float64) ** 2))
+    po, mo, vo, so = oracle.adam(g, p, z, z, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.01,
+                                 t=1, nthreads=NTHREADS)
+    del g
+    sent = torch.full((S,), 0x7FBADBAD, dtype=torch.int32, device="cuda")
+    P, M, V = (sent.clone().view(torch.float32) for _ in range(3))
+    slot = torch.full((S,), 0x5A5A, dtype=torch.int16, device="cuda")
+    stats = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    zd = torch.zeros(S, dtype=torch.float32, device="cuda")
+    a = Z.make_adam_args(replicas=[to_dev(r) for r in reps], grad_dtype=Z.ZERO_BF16,
+                         p_in=to_dev(p), m_in=zd, v_in=zd, p_out=P, m_out=M, v_out=V, slot=slot,
+                         shard_S=S, buckets=buckets, n_buckets=len(table), loss_scale=1.0, step_t=1,
+                         lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, stats=stats,
+                         workspace=None)
+    Z.zero_adam_step_noalloc(a)
+    st = _stats(Z, stats)
+    assert st.overflow == 0 and st.bad_buckets == 0
+    assert sumsq_close(st.sumsq, want_sumsq), (st.sumsq, want_sumsq)
+    for name, got, want in (("p", P, po), ("m", M, mo), ("v", V, vo), ("slot", slot, so)):
+        h = to_host(got)
+        assert_bitexact(f"capped grid {name}", h[inside], want[inside])
+        if name == "slot":
+            assert np.all(h[~inside] == 0x5A5A)
+        else:
+            assert np.all(h[~inside].view(np.uint32) == 0x7FBADBAD), name
