@@ -25,6 +25,10 @@
 //    strides over the shard with the same number of trips per workgroup; small
 //    shards are instead split evenly over a multiple of 256 workgroups;
 //  - fp32 state as three arrays or in tiles of p | m | v (state_q, state_e);
+//  - a bucket table confines the step to its buckets: one workgroup per bucket,
+//    or, for a short table of long buckets, chunks of 1,024 elements dealt over
+//    the grid; a quad cut by a bucket edge is loaded whole like the others and
+//    masked to the bucket's elements;
 //  - the flag and the fp64 squared norm are reduced with wave shuffles, then
 //    LDS, then one partial per workgroup, summed in workgroup order (by a
 //    one-workgroup finalize kernel, or, with the device commit, by workgroup 0
@@ -595,13 +599,14 @@ __device__ __forceinline__ void quads(const KParams& a, const Res& rs, int64_t q
     if constexpr (ADAM) quads_store<TILED, ROWS, MASKED>(rs, q0, qs, o, mask);
 }
 
-// One element, for bucket edges and the shard tail.
+// One element, for the shard's last S % 4 elements (the buffers do not hold them
+// as a whole quad).
 template <typename RT, bool ADAM, bool WRITE_G, bool TILED>
 __device__ __forceinline__ void one_elem(const KParams& a, const Res& rs, int64_t e, double& sq,
                                          uint32_t& bad) {
     // replica loads in batches of 8, all in flight before their adds (a spare load
-    // repeats the batch's first slot and is dropped): a lane on a bucket edge
-    // makes N / 8 memory round trips, not N
+    // repeats the batch's first slot and is dropped): a lane on the tail makes
+    // N / 8 memory round trips, not N
     const int n = a.n_rep;
     float acc = Quad<RT>::one(Reps<RT>::at(a, 0), e);
     for (int j = 1; j < n; j += 8) {
