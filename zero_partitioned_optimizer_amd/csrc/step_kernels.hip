@@ -348,7 +348,9 @@ __device__ __forceinline__ void fold(const KParams& a, int64_t q0, int64_t qs, f
 // a permutation of the first 8 * floor(G / 8) trips (the last partial run
 // shrinks K; the rest of the grid keeps its index). Each XCD then walks runs of
 // K consecutive trips (K = 64: 128 KB of each bf16 replica) instead of every
-// eighth trip: Llama-7B 1.6-2.5% faster, Llama-70B 0.3-0.4%, GPT-2 0-2%.
+// eighth trip: Llama-7B 1.6-2.9% faster, Llama-70B 0.3-0.4%, GPT-2 0-2%. The
+// evenly split small launches permute their shares and the chunked bucket
+// launches their chunks the same way.
 constexpr int64_t kXcdRun = 64;
 __device__ __forceinline__ int64_t xcd_trip(int64_t bx, int64_t G) {
     const int64_t L = G >> 3;
@@ -920,8 +922,10 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
     if constexpr (!BUCKETS) {
         if (a.even_blocks > 0) {
             // blocks [b*NB/G, (b+1)*NB/G) of the shard's quads, and the last S % 4
-            // elements with the last workgroup
-            const int64_t nq = a.S >> 2, nb = a.even_blocks, g = gridDim.x, b = blockIdx.x;
+            // elements with the one that takes the last blocks (b: the workgroup's
+            // share, permuted over the XCDs like the trips of a larger launch)
+            const int64_t nq = a.S >> 2, nb = a.even_blocks, g = gridDim.x;
+            const int64_t b = xcd_trip(blockIdx.x, gridDim.x);
             const int64_t qlo = (b * nb / g) * kEvenBlockQuads;
             int64_t qhi = ((b + 1) * nb / g) * kEvenBlockQuads;
             if (qhi > nq) qhi = nq;
@@ -991,7 +995,7 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
         }
         lds_barrier();
         const int64_t total = first[nbk];
-        for (int64_t j = blockIdx.x; j < total; j += gridDim.x) {
+        for (int64_t j = xcd_trip(blockIdx.x, gridDim.x); j < total; j += gridDim.x) {
             // the bucket holding chunk j: first[lb] <= j < first[lb + 1]
             int64_t lb = 0, ub = nbk;
             while (ub - lb > 1) {
