@@ -285,28 +285,68 @@ def gather_bench(args, Z, W, w, S) -> int:
     layer = list(range(first, first + per_layer))
     outs_all = [torch.empty(n, dtype=torch.int16, device=dev) for n in numels]
 
-    def timed(idx, reps):
-        nums = [numels[t] for t in idx]
-        plan = Z.GatherPlan(shards, S, [offsets[t] for t in idx], nums, [outs_all[t] for t in idx])
+    def plan_of(idx):
+        return Z.GatherPlan(shards, S, [offsets[t] for t in idx], [numels[t] for t in idx],
+                            [outs_all[t] for t in idx])
+
+    def timed(plans, reps):
         for _ in range(args.warmup):
-            plan()
+            for plan in plans:
+                plan()
         # back to back, one event pair around all calls: the host's call overhead
         # overlaps the copies of the calls before it
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
         for _ in range(reps):
-            plan()
+            for plan in plans:
+                plan()
         e1.record()
         e1.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / reps, sum(nums)
+        return e0.elapsed_time(e1) * 1e-3 / (reps * len(plans))
 
-    t_layer, n_layer = timed(layer, args.steps)
-    t_all, n_all = timed(list(range(len(numels))), max(5, args.steps // 10))
+    def graphed(plans, reps):
+        # the same calls captured once in a HIP graph and replayed: the GPU's time
+        # per call with no host work per launch
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            for plan in plans:
+                plan()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                for plan in plans:
+                    plan()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / (reps * len(plans))
+
+    n_layer = sum(numels[t] for t in layer)
+    t_layer = timed([plan_of(layer)], args.steps)
+    # every layer in turn: no layer's tensors are still cached when it comes round
+    n_layers = (len(numels) - first) // per_layer
+    layers = [list(range(first + k * per_layer, first + (k + 1) * per_layer)) for k in range(n_layers)]
+    turn_plans = [plan_of(ix) for ix in layers]
+    n_turn = sum(numels[t] for ix in layers for t in ix) / n_layers
+    t_turn = timed(turn_plans, max(1, args.steps // n_layers))
+    t_turn_g = graphed(turn_plans, max(2, args.steps // n_layers))
+    n_all = sum(numels)
+    t_all = timed([plan_of(list(range(len(numels))))], max(5, args.steps // 10))
     gbs_all = 4 * n_all / t_all / 1e9
     log(f"gather: layer ({per_layer} tensors, {n_layer} elements) {t_layer * 1e6:.1f} us "
-        f"= {4 * n_layer / t_layer / 1e9:.0f} GB/s; model ({len(numels)} tensors) "
-        f"{t_all * 1e3:.3f} ms = {gbs_all:.0f} GB/s")
+        f"= {4 * n_layer / t_layer / 1e9:.0f} GB/s; the {n_layers} layers in turn "
+        f"{t_turn * 1e6:.1f} us = {4 * n_turn / t_turn / 1e9:.0f} GB/s per layer "
+        f"({t_turn_g * 1e6:.1f} us = {4 * n_turn / t_turn_g / 1e9:.0f} GB/s replayed from a graph); "
+        f"model ({len(numels)} tensors) {t_all * 1e3:.3f} ms = {gbs_all:.0f} GB/s")
     out = {
         "metric": "stage-3 fetch: achieved HBM GB/s (bf16 tensors out of the rank shards)",
         "value": gbs_all, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -315,7 +355,10 @@ def gather_bench(args, Z, W, w, S) -> int:
         "config": {"workload": f"{w.name} parameters, N={w.N} shards of S={S}",
                    "n_tensors": len(numels), "elements": n_all},
         "layer": {"tensors": per_layer, "elements": n_layer, "us": t_layer * 1e6,
-                  "gbs": 4 * n_layer / t_layer / 1e9},
+                  "gbs": 4 * n_layer / t_layer / 1e9, "repeated": "the same layer back to back"},
+        "layers_in_turn": {"layers": n_layers, "elements_per_layer": n_turn, "us": t_turn * 1e6,
+                           "gbs": 4 * n_turn / t_turn / 1e9, "graph_us": t_turn_g * 1e6,
+                           "graph_gbs": 4 * n_turn / t_turn_g / 1e9},
         "roofline": {"bound": "hbm", "achieved": gbs_all, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs_all / HBM_PEAK_GBS, "traffic": None},
         "cpu_baseline": None,
