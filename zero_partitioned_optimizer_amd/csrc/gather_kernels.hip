@@ -30,6 +30,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 struct GatherParams {
     const void* shard[kGatherMaxShards];
     int64_t S;
+    double inv_S;                             // 1 / S, rounded once
     int32_t n_tensors;
     int32_t reserved;
     int64_t offset[kGatherTensors];
@@ -76,14 +77,24 @@ __device__ __forceinline__ void copy_piece(const E* __restrict__ src, E* __restr
 template <typename E>
 __global__ void __launch_bounds__(kBlock) k_gather(const GatherParams g) {
     const int64_t task = g.task_base + blockIdx.x;
-    int t = 0;
-    while (t + 1 < g.n_tensors && g.first_task[t + 1] <= task) ++t;
+    // the task's tensor: the last t with first_task[t] <= task (first_task does
+    // not decrease). Lane i of every wave reads entry i, and the number of entries
+    // at or below the task, over the wave, is t + 1: one round of loads whatever
+    // the tensor's position, where a scan of the entries takes up to 47 in a row.
+    static_assert(kGatherTensors <= 64, "one entry per lane");
+    const int lane = threadIdx.x & 63;
+    const int64_t ft = lane < g.n_tensors ? g.first_task[lane] : INT64_MAX;
+    const int t = __popcll(__ballot(ft <= task)) - 1;
     const int64_t n = g.numel[t];
     const int64_t e0 = (task - g.first_task[t]) * kGatherChunk;
     const int64_t e1 = e0 + kGatherChunk < n ? e0 + kGatherChunk : n;
     E* out = static_cast<E*>(g.out[t]);
     const int64_t f = g.offset[t] + e0;
-    int64_t r = f / g.S;
+    // rank r = floor(f / S) from the reciprocal (within one of it for any f below
+    // 2^51), then corrected: no 64-bit division
+    int64_t r = (int64_t)((double)f * g.inv_S);
+    if (r * g.S > f) --r;
+    else if ((r + 1) * g.S <= f) ++r;
     int64_t off = f - r * g.S;
     for (int64_t e = e0; e < e1; ++r, off = 0) {
         const int64_t rest = g.S - off;
@@ -99,6 +110,7 @@ hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S,
     GatherParams g{};
     for (int r = 0; r < kGatherMaxShards; ++r) g.shard[r] = r < n_shards ? shards[r] : nullptr;
     g.S = S;
+    g.inv_S = S > 0 ? 1.0 / (double)S : 0.0;
     for (int32_t base = 0; base < n_tensors; base += kGatherTensors) {
         const int32_t k = n_tensors - base < kGatherTensors ? n_tensors - base : kGatherTensors;
         g.n_tensors = k;
