@@ -349,8 +349,8 @@ __device__ __forceinline__ void fold(const KParams& a, int64_t q0, int64_t qs, f
 // shrinks K; the rest of the grid keeps its index). Each XCD then walks runs of
 // K consecutive trips (K = 64: 128 KB of each bf16 replica) instead of every
 // eighth trip: Llama-7B 1.6-2.9% faster, Llama-70B 0.3-0.4%, GPT-2 0-2%. The
-// evenly split small launches permute their shares and the chunked bucket
-// launches their chunks the same way.
+// evenly split small launches permute their shares, and bucket launches their
+// chunks or buckets, the same way.
 constexpr int64_t kXcdRun = 64;
 __device__ __forceinline__ int64_t xcd_trip(int64_t bx, int64_t G) {
     const int64_t L = G >> 3;
@@ -1013,7 +1013,7 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
             range<RT, ADAM, WRITE_G, TILED>(a, rs, lo, hi, sq, bad);
         }
     } else {
-        for (int64_t b = blockIdx.x; b < a.n_buckets; b += gridDim.x) {
+        for (int64_t b = xcd_trip(blockIdx.x, gridDim.x); b < a.n_buckets; b += gridDim.x) {
             const zero_bucket bk = a.buckets[b];
             const int64_t lo = bk.shard_off, len = bk.len;
             if (lo < 0 || len < 0 || lo > a.S || len > a.S - lo) {
