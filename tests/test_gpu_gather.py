@@ -57,6 +57,20 @@ def test_unaligned_layouts(Z, seed):
     check_layout(Z, numels, int(rng.integers(2, 12)), 1, seed=seed)
 
 
+@pytest.mark.parametrize("N,count", [(8, 141), (8, 142), (8, 143), (8, 285), (64, 125), (64, 126),
+                                     (64, 127), (200, 70), (200, 71), (200, 72), (200, 143)])
+def test_tensor_counts_around_one_launch(Z, N, count):
+    """Calls whose tensor counts sit just below, at and just above what one launch's
+    argument block holds for their shard count (and twice that), so that the
+    split into launches and the tensor lookup at the ends of a group are both
+    exercised: every tensor bit-exact against the oracle."""
+    rng = np.random.default_rng(1000 + N + count)
+    numels = [int(x) for x in rng.integers(1, 3000, size=count)]
+    numels[count // 2] = 40_000          # one tensor of several tasks
+    say(f"gather N={N} count={count}")
+    check_layout(Z, numels, N, 1, seed=N + count)
+
+
 def test_fp32_and_spanning_tensor(Z):
     say("gather fp32 + a tensor over every shard")
     check_layout(Z, [3, 5000, 1, 7], 64, 1, dtype=np.float32, seed=6)

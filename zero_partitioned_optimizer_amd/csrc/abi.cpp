@@ -7,7 +7,9 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
+#include <vector>
 
 #include "zero.h"
 #include "zero_internal.h"
@@ -814,16 +816,28 @@ int zero_gather_tensors(const void* const* shards, int32_t n_shards, int64_t sha
             return ZERO_E_ALIGN;
         }
         const Span sk = span("out", outs[k], n * elem_bytes);
-        for (int32_t r = 0; r < n_shards; ++r)
+        for (int32_t r = 0; r < n_shards && n > 0; ++r)
             if (overlap(sk, span("shard", shards[r], shard_S * elem_bytes))) {
                 set_error("%s: outs[%d] overlaps shards[%d]", fn, (int)k, (int)r);
                 return ZERO_E_INVAL;
             }
-        for (int32_t j = 0; j < k; ++j)
-            if (overlap(sk, span("out", outs[j], numels[j] * elem_bytes))) {
-                set_error("%s: outs[%d] overlaps outs[%d]", fn, (int)k, (int)j);
-                return ZERO_E_INVAL;
-            }
+    }
+    // outputs pairwise disjoint: sorted by start, two non-empty outputs overlap
+    // exactly when some output starts before its predecessor in that order ends
+    std::vector<int32_t> order;
+    order.reserve((size_t)n_tensors);
+    for (int32_t k = 0; k < n_tensors; ++k)
+        if (numels[k] > 0) order.push_back(k);
+    std::sort(order.begin(), order.end(), [outs](int32_t x, int32_t y) {
+        return reinterpret_cast<uintptr_t>(outs[x]) < reinterpret_cast<uintptr_t>(outs[y]);
+    });
+    for (size_t i = 1; i < order.size(); ++i) {
+        const int32_t j = order[i - 1], k = order[i];
+        if (overlap(span("out", outs[j], numels[j] * elem_bytes),
+                    span("out", outs[k], numels[k] * elem_bytes))) {
+            set_error("%s: outs[%d] overlaps outs[%d]", fn, (int)(j > k ? j : k), (int)(j < k ? j : k));
+            return ZERO_E_INVAL;
+        }
     }
     return hip_status(zk::launch_gather(shards, n_shards, shard_S, elem_bytes, offsets, numels, outs,
                                         n_tensors, static_cast<hipStream_t>(stream)),

@@ -11,9 +11,11 @@
 // tasks of kGatherChunk output elements, so a launch has about one task per
 // 16 KB of bf16 output whatever the tensor sizes; pieces whose source and
 // destination share their 16-byte alignment move as 16-byte vectors, others
-// element by element (still coalesced). Up to kGatherTensors tensors go into one
-// launch (as many as the kernel argument block holds), so a model's fetch takes
-// few launches, each with its own tail.
+// element by element (still coalesced). The tensor table travels in the kernel
+// argument block, sized to the call's shard count (a table of 8, 64 or 256
+// shard pointers, then as many tensors as the rest of the 4 KB block holds:
+// 142, 126 or 71), so a model's fetch takes few launches, each with its own
+// fill and tail.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -21,25 +23,35 @@
 
 namespace zk {
 
-constexpr int kGatherTensors = 48;                      // tensors per launch
 constexpr int64_t kGatherChunk = 8192;                  // output elements per task
 constexpr int64_t kGatherMaxTasks = int64_t(1) << 20;   // workgroups per gather launch
+constexpr int kArgBytes = 4096;                         // the kernel argument block
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-struct GatherParams {
-    const void* shard[kGatherMaxShards];
+// One launch's arguments for calls over at most NSH shards: the header and the
+// shard table, then per tensor its flat offset, length, output and first task
+// (the prefix sum of the task counts, relative to the launch's group; the
+// entries from n_tensors to kTensors all hold the group's total).
+template <int NSH>
+struct GatherArgs {
+    static constexpr int kHead = 8 * NSH + 32;
+    static constexpr int kTensors = (kArgBytes - kHead - 4) / 28;
+    const void* shard[NSH];
     int64_t S;
     double inv_S;                             // 1 / S, rounded once
+    int64_t task_base;                        // task of workgroup 0 of this launch
     int32_t n_tensors;
     int32_t reserved;
-    int64_t offset[kGatherTensors];
-    int64_t numel[kGatherTensors];
-    void* out[kGatherTensors];
-    int64_t first_task[kGatherTensors + 1];   // prefix sums of the tensors' task counts
-    int64_t task_base;                        // task of workgroup 0 of this launch
+    int64_t offset[kTensors];
+    int64_t numel[kTensors];
+    void* out[kTensors];
+    int32_t first_task[kTensors + 1];
 };
-static_assert(sizeof(GatherParams) <= 4096, "the gather arguments fit the kernel argument block");
+static_assert(sizeof(GatherArgs<8>) <= kArgBytes && sizeof(GatherArgs<64>) <= kArgBytes &&
+                  sizeof(GatherArgs<kGatherMaxShards>) <= kArgBytes,
+              "the gather arguments fit the kernel argument block");
+static_assert(GatherArgs<kGatherMaxShards>::kTensors >= 64, "at least one lane's worth of tensors");
 
 // len elements from src to dst by the whole workgroup. Each lane issues up to
 // four 16-byte loads before its stores, so a full task (16 KB of bf16) is one
@@ -74,17 +86,26 @@ __device__ __forceinline__ void copy_piece(const E* __restrict__ src, E* __restr
     for (int64_t k = done + threadIdx.x; k < len; k += kBlock) dst[k] = src[k];
 }
 
-template <typename E>
-__global__ void __launch_bounds__(kBlock) k_gather(const GatherParams g) {
+template <typename E, int NSH>
+__global__ void __launch_bounds__(kBlock) k_gather(const GatherArgs<NSH> g) {
+    constexpr int KT = GatherArgs<NSH>::kTensors;
     const int64_t task = g.task_base + blockIdx.x;
     // the task's tensor: the last t with first_task[t] <= task (first_task does
-    // not decrease). Lane i of every wave reads entry i, and the number of entries
-    // at or below the task, over the wave, is t + 1: one round of loads whatever
-    // the tensor's position, where a scan of the entries takes up to 47 in a row.
-    static_assert(kGatherTensors <= 64, "one entry per lane");
+    // not decrease). Lane i of every wave reads entries i, i + 64, ..., and the
+    // number of entries at or below the task, over the wave, is t + 1: one round
+    // of loads whatever the tensor's position. The entries past the group hold
+    // its total, which exceeds every task of the launch; the loads depend on
+    // nothing but the lane, so that they are all in flight together.
     const int lane = threadIdx.x & 63;
-    const int64_t ft = lane < g.n_tensors ? g.first_task[lane] : INT64_MAX;
-    const int t = __popcll(__ballot(ft <= task)) - 1;
+    int32_t ft[(KT + 63) / 64];
+#pragma unroll
+    for (int i = 0; i < (KT + 63) / 64; ++i) {
+        const int j = 64 * i + lane;
+        ft[i] = g.first_task[j < KT ? j : KT];
+    }
+    int t = -1;
+#pragma unroll
+    for (int i = 0; i < (KT + 63) / 64; ++i) t += __popcll(__ballot((int64_t)ft[i] <= task));
     const int64_t n = g.numel[t];
     const int64_t e0 = (task - g.first_task[t]) * kGatherChunk;
     const int64_t e1 = e0 + kGatherChunk < n ? e0 + kGatherChunk : n;
@@ -104,38 +125,54 @@ __global__ void __launch_bounds__(kBlock) k_gather(const GatherParams g) {
     }
 }
 
-hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S, int32_t elem_bytes,
-                         const int64_t* offsets, const int64_t* numels, void* const* outs,
-                         int32_t n_tensors, hipStream_t st) {
-    GatherParams g{};
-    for (int r = 0; r < kGatherMaxShards; ++r) g.shard[r] = r < n_shards ? shards[r] : nullptr;
+template <int NSH>
+static hipError_t gather_groups(const void* const* shards, int32_t n_shards, int64_t S,
+                                int32_t elem_bytes, const int64_t* offsets, const int64_t* numels,
+                                void* const* outs, int32_t n_tensors, hipStream_t st) {
+    constexpr int KT = GatherArgs<NSH>::kTensors;
+    GatherArgs<NSH> g{};
+    for (int r = 0; r < NSH; ++r) g.shard[r] = r < n_shards ? shards[r] : nullptr;
     g.S = S;
-    g.inv_S = S > 0 ? 1.0 / (double)S : 0.0;
-    for (int32_t base = 0; base < n_tensors; base += kGatherTensors) {
-        const int32_t k = n_tensors - base < kGatherTensors ? n_tensors - base : kGatherTensors;
+    g.inv_S = 1.0 / (double)S;
+    for (int32_t base = 0; base < n_tensors; base += KT) {
+        const int32_t k = n_tensors - base < KT ? n_tensors - base : KT;
         g.n_tensors = k;
-        g.first_task[0] = 0;
+        int64_t tasks = 0;
         for (int32_t i = 0; i < k; ++i) {
             g.offset[i] = offsets[base + i];
             g.numel[i] = numels[base + i];
             g.out[i] = outs[base + i];
-            g.first_task[i + 1] = g.first_task[i] + (g.numel[i] + kGatherChunk - 1) / kGatherChunk;
+            g.first_task[i] = (int32_t)tasks;
+            tasks += (g.numel[i] + kGatherChunk - 1) / kGatherChunk;
+            // a group's tasks are counted in 32 bits (2^31 tasks: 16T elements)
+            if (tasks > INT32_MAX) return hipErrorInvalidValue;
         }
-        const int64_t tasks = g.first_task[k];
+        for (int32_t i = k; i <= KT; ++i) g.first_task[i] = (int32_t)tasks;
         // at most kGatherMaxTasks workgroups (8G elements) per launch; a group
         // with more tasks takes several launches over consecutive task ranges
         for (int64_t t0 = 0; t0 < tasks; t0 += kGatherMaxTasks) {
             const int64_t n = tasks - t0 < kGatherMaxTasks ? tasks - t0 : kGatherMaxTasks;
             g.task_base = t0;
             if (elem_bytes == 2)
-                hipLaunchKernelGGL(k_gather<uint16_t>, dim3((unsigned)n), dim3(kBlock), 0, st, g);
+                hipLaunchKernelGGL((k_gather<uint16_t, NSH>), dim3((unsigned)n), dim3(kBlock), 0, st, g);
             else
-                hipLaunchKernelGGL(k_gather<uint32_t>, dim3((unsigned)n), dim3(kBlock), 0, st, g);
+                hipLaunchKernelGGL((k_gather<uint32_t, NSH>), dim3((unsigned)n), dim3(kBlock), 0, st, g);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
     }
     return hipSuccess;
+}
+
+hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S, int32_t elem_bytes,
+                         const int64_t* offsets, const int64_t* numels, void* const* outs,
+                         int32_t n_tensors, hipStream_t st) {
+    if (n_shards <= 8)
+        return gather_groups<8>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
+    if (n_shards <= 64)
+        return gather_groups<64>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
+    return gather_groups<kGatherMaxShards>(shards, n_shards, S, elem_bytes, offsets, numels, outs,
+                                           n_tensors, st);
 }
 
 }  // namespace zk
