@@ -649,10 +649,13 @@ __device__ __forceinline__ void quads_store(const Res& rs, int64_t q0, int64_t q
 }
 
 // The whole step for ROWS quads of this lane.
-// quads() for one quad whose first replica batch is already loaded.
-template <typename RT, bool ADAM, bool WRITE_G, bool TILED>
+// quads() for one quad whose first replica batch is already loaded (MASKED: as
+// in quads_compute, only the elements whose bits are set in `mask` count and are
+// stored).
+template <typename RT, bool ADAM, bool WRITE_G, bool TILED, bool MASKED = false>
 __device__ __forceinline__ void quad_pre(const KParams& a, const Res& rs, int64_t q0,
-                                         const Head<RT>& h, double& sq, uint32_t& bad) {
+                                         const Head<RT>& h, double& sq, uint32_t& bad,
+                                         uint32_t mask = 0xFu) {
     f32x4 p[1], m[1], v[1];
     if constexpr (ADAM) {
         const int64_t q = state_q<TILED>(q0);
@@ -677,12 +680,21 @@ __device__ __forceinline__ void quad_pre(const KParams& a, const Res& rs, int64_
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        bad |= nonfinite(g[0][c]) ? 1u : 0u;
+        const bool in = !MASKED || ((mask >> c) & 1u);
+        bad |= (in && nonfinite(g[0][c])) ? 1u : 0u;
         const double gd = (double)g[0][c];
-        sq += gd * gd;
+        sq += in ? gd * gd : 0.0;
     }
-    if constexpr (WRITE_G) st(reinterpret_cast<f32x4*>(a.g_out) + q0, g[0]);
-    if constexpr (ADAM) quads_store<TILED, 1>(rs, q0, 0, o);
+    if constexpr (WRITE_G) {
+        if (!MASKED || mask == 0xFu) {
+            st(reinterpret_cast<f32x4*>(a.g_out) + q0, g[0]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if ((mask >> c) & 1u) a.g_out[q0 * 4 + c] = g[0][c];
+        }
+    }
+    if constexpr (ADAM) quads_store<TILED, 1, MASKED>(rs, q0, 0, o, mask);
 }
 
 template <typename RT, bool ADAM, bool WRITE_G, bool TILED, int ROWS, bool MASKED = false>
@@ -735,21 +747,36 @@ __device__ __forceinline__ void one_elem(const KParams& a, const Res& rs, int64_
 // the others, masked to the range's elements, so the lanes on the edges make the
 // same memory round trips as the rest; only the shard's last partial quad (when
 // S % 4 != 0), which the buffers do not hold whole, goes element by element.
-template <typename RT, bool ADAM, bool WRITE_G, bool TILED>
+// HEAD: the lane's first quad of the range, (lo >> 2) + threadIdx.x, has its first
+// replica batch in `h` already (range_first_quad, when it is below range_qend).
+__device__ __forceinline__ int64_t range_qend(const KParams& a, int64_t hi) {
+    const int64_t qw = a.S >> 2;            // the shard's whole quads
+    const int64_t qhi = (hi + 3) >> 2;      // one past the quad holding element hi - 1
+    return qhi < qw ? qhi : qw;
+}
+
+__device__ __forceinline__ uint32_t edge_mask(int64_t q, int64_t lo, int64_t hi) {
+    const int64_t e = q << 2;
+    uint32_t mask = 0xFu;
+    if (e < lo) mask &= 0xFu << (uint32_t)(lo - e);
+    if (e + 4 > hi) mask &= 0xFu >> (uint32_t)(e + 4 - hi);
+    return mask;
+}
+
+template <typename RT, bool ADAM, bool WRITE_G, bool TILED, bool HEAD = false>
 __device__ __forceinline__ void range(const KParams& a, const Res& rs, int64_t lo, int64_t hi,
-                                      double& sq, uint32_t& bad) {
+                                      double& sq, uint32_t& bad, const Head<RT>* h = nullptr) {
     if (lo >= hi) return;
     const int tid = threadIdx.x;
-    const int64_t qw = a.S >> 2;            // the shard's whole quads
-    int64_t qhi = (hi + 3) >> 2;            // one past the quad holding element hi - 1
-    if (qhi > qw) qhi = qw;
-    for (int64_t q = (lo >> 2) + tid; q < qhi; q += kBlock) {
-        const int64_t e = q << 2;
-        uint32_t mask = 0xFu;
-        if (e < lo) mask &= 0xFu << (uint32_t)(lo - e);
-        if (e + 4 > hi) mask &= 0xFu >> (uint32_t)(e + 4 - hi);
-        quads<RT, ADAM, WRITE_G, TILED, 1, true>(a, rs, q, 0, sq, bad, mask);
+    const int64_t qw = a.S >> 2;
+    const int64_t qhi = range_qend(a, hi);
+    int64_t q = (lo >> 2) + tid;
+    if constexpr (HEAD) {
+        if (q < qhi) quad_pre<RT, ADAM, WRITE_G, TILED, true>(a, rs, q, *h, sq, bad, edge_mask(q, lo, hi));
+        q += kBlock;
     }
+    for (; q < qhi; q += kBlock)
+        quads<RT, ADAM, WRITE_G, TILED, 1, true>(a, rs, q, 0, sq, bad, edge_mask(q, lo, hi));
     const int64_t et = qw << 2;
     for (int64_t e = (lo > et ? lo : et) + tid; e < hi; e += kBlock)
         one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
@@ -985,16 +1012,28 @@ __device__ __forceinline__ void post_mark(const KParams& a, const Res& rs) {
     }
 }
 
-// PRE (device commit, whole shard, one row; launches of at most kPreGrid
-// workgroups): each lane's first quad and its first replica batch are taken
-// before the committed-state record is read, so that with a cold cache the
-// record's round trip overlaps those loads.
+// PRE (device commit, one row, launches of at most kPreGrid workgroups over the
+// whole shard or over a table of short buckets): each lane's first quad and its
+// first replica batch are taken before the committed-state record is read, so
+// that with a cold cache the record's round trip overlaps those loads.
 template <typename RT, bool BUCKETS, bool ADAM, bool WRITE_G, bool CTRL, bool TILED, int ROWS,
           bool PRE = false>
 __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
-    static_assert(!PRE || (CTRL && !BUCKETS && ROWS == 1), "the prefetch serves one-row device-commit launches");
+    static_assert(!PRE || (CTRL && ROWS == 1), "the prefetch serves one-row device-commit launches");
     Head<RT> head;
-    if constexpr (PRE) {
+    if constexpr (PRE && BUCKETS) {
+        // a table of short buckets, one per workgroup in turn (never the chunked
+        // table): the first bucket's descriptor, then the lane's first quad in it
+        const int64_t b = xcd_trip(blockIdx.x, gridDim.x);
+        if (b < a.n_buckets) {
+            const zero_bucket bk = a.buckets[b];
+            const int64_t lo = bk.shard_off, len = bk.len;
+            if (lo >= 0 && len > 0 && lo <= a.S && len <= a.S - lo) {
+                const int64_t q = (lo >> 2) + threadIdx.x;
+                if (q < range_qend(a, lo + len)) head_load<RT>(a, q, head);
+            }
+        }
+    } else if constexpr (PRE) {
         const int64_t nq = a.S >> 2, g = gridDim.x;
         const int64_t b = xcd_trip(blockIdx.x, gridDim.x);
         int64_t q = -1;
@@ -1058,7 +1097,7 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
                 if (e < a.S) one_elem<RT, ADAM, WRITE_G, TILED>(a, rs, e, sq, bad);
             }
         }
-    } else if (a.even_blocks > 0) {
+    } else if (!PRE && a.even_blocks > 0) {
         // A short table of long buckets: every bucket is cut into chunks of kChunk
         // elements (boundaries on 64-element lines) and the chunks are dealt over
         // the grid. Each workgroup reads the table and prefix-sums the chunk counts
@@ -1122,7 +1161,21 @@ __global__ void ZERO_STEP_BOUNDS k_step(const KParams a) {
             range<RT, ADAM, WRITE_G, TILED>(a, rs, lo, hi, sq, bad);
         }
     } else {
-        for (int64_t b = xcd_trip(blockIdx.x, gridDim.x); b < a.n_buckets; b += gridDim.x) {
+        int64_t b = xcd_trip(blockIdx.x, gridDim.x);
+        if constexpr (PRE) {
+            // the first bucket, its first quad per lane loaded in the prologue
+            if (b < a.n_buckets) {
+                const zero_bucket bk = a.buckets[b];
+                const int64_t lo = bk.shard_off, len = bk.len;
+                if (lo < 0 || len < 0 || lo > a.S || len > a.S - lo) {
+                    if (threadIdx.x == 0) badb += 1u;
+                } else {
+                    range<RT, ADAM, WRITE_G, TILED, true>(a, rs, lo, lo + len, sq, bad, &head);
+                }
+            }
+            b += gridDim.x;
+        }
+        for (; b < a.n_buckets; b += gridDim.x) {
             const zero_bucket bk = a.buckets[b];
             const int64_t lo = bk.shard_off, len = bk.len;
             if (lo < 0 || len < 0 || lo > a.S || len > a.S - lo) {
@@ -1383,18 +1436,19 @@ static void launch_one(const StepDesc& d, const KParams& k, int grid, hipStream_
                            dim3(kBlock), 0, st, k);
 }
 
-// Device-commit whole-shard launches of at most this many workgroups take their
-// first replica batch before the record (k_step's PRE): GPT-2-sized and smaller
-// shards gain 1-3%; on the Llama shards it changes nothing or costs 0.1%.
+// Device-commit launches of at most this many workgroups, over the whole shard or
+// a table of short buckets, take their first replica batch before the record
+// (k_step's PRE): GPT-2-sized and smaller shards gain 1-3%; on the Llama shards it
+// changes nothing or costs 0.1%.
 constexpr int kPreGrid = 65536;
 
 template <typename RT, bool BUCKETS, int ROWS>
 static void launch_rows(const StepDesc& d, const KParams& k, int grid, hipStream_t st) {
     if (d.ctrl) {
-        if constexpr (!BUCKETS && ROWS == 1) {
-            if (grid <= kPreGrid) {
-                if (d.tiled) launch_one<RT, false, true, false, true, true, 1, true>(d, k, grid, st);
-                else launch_one<RT, false, true, false, true, false, 1, true>(d, k, grid, st);
+        if constexpr (ROWS == 1) {
+            if (grid <= kPreGrid && (!BUCKETS || k.even_blocks == 0)) {
+                if (d.tiled) launch_one<RT, BUCKETS, true, false, true, true, 1, true>(d, k, grid, st);
+                else launch_one<RT, BUCKETS, true, false, true, false, 1, true>(d, k, grid, st);
                 return;
             }
         }
