@@ -13,7 +13,11 @@ NaN and inf sit in the excluded elements of cut quads (in every replica slot the
 case draws); they must neither raise the overflow flag nor reach the norm.
 Elements outside the buckets keep their sentinel.
 
-The short table (11 buckets over 4,003 elements) runs one workgroup per bucket.
+The short table (11 buckets over 4,003 elements) runs one workgroup per bucket;
+a generated table of about 10,000 buckets of 1-5 elements has more buckets than
+workgroups, and one of about 70,000 buckets of 950 elements a grid above the
+65,536 workgroups up to which device-commit launches load their first replica
+batch before the committed-state record.
 Tables of a few long buckets are cut into chunks dealt over the grid: the long
 table (and the same table in reverse order), the mid table over 3,000,003
 elements, and a 70,000,003-element shard through the allocation-free entry
@@ -43,10 +47,41 @@ LONG_BAD = [0, 2, 100_003, 100_004, 250_006]
 MID_S = 3_000_003
 MID = [(2, 1_000_000), (1_000_006, 999_990), (2_000_064, 999_936), (3_000_000, 3)]
 MID_BAD = [0, 1, 1_000_002, 1_000_005, 1_999_996, 2_000_000, 2_000_063]
+
+
+def _generated(S, seed, first, sizes, gaps):
+    """A table of buckets from `first` on, lengths and gaps drawn from the given
+    ranges (a gap of 0 puts two buckets in one quad), the last bucket the shard's
+    last 3 elements; the bad positions are gap elements spread over the shard."""
+    rng = np.random.default_rng(seed)
+    table, pos, gap_at = [], first, []
+    while True:
+        ln = int(rng.integers(*sizes))
+        if pos + ln > S - 4:
+            break
+        table.append((pos, ln))
+        pos += ln
+        gp = int(rng.integers(*gaps))
+        gap_at.extend(range(pos, pos + gp))
+        pos += gp
+    gap_at.extend(range(pos, S - 3))
+    table.append((S - 3, 3))
+    pick = np.linspace(0, len(gap_at) - 1, 7).astype(np.int64)
+    return S, table, [gap_at[i] for i in pick]
+
+
 TABLES = {"short": (SHORT_S, SHORT, SHORT_BAD), "long": (LONG_S, LONG, LONG_BAD),
-          "long_rev": (LONG_S, LONG[::-1], LONG_BAD), "mid": (MID_S, MID, MID_BAD)}
+          "long_rev": (LONG_S, LONG[::-1], LONG_BAD), "mid": (MID_S, MID, MID_BAD),
+          # about 10,000 buckets of 1-5 elements over 40,003: more buckets than the
+          # grid's 4,136 workgroups, so a workgroup takes two or three in turn
+          "many": _generated(40_003, 71, 1, (1, 6), (0, 3)),
+          # about 70,000 buckets of 950 elements over 67,000,003: a grid of 69,526
+          # workgroups, past the 65,536 up to which the first replica batch is
+          # loaded before the committed-state record
+          "wide": _generated(67_000_003, 72, 2, (950, 951), (0, 3))}
 
 CASES = [("short", "bf16", 5), ("short", "f32", 3), ("short", "bf16", 20), ("short", "wire", 9),
+         ("many", "bf16", 5),
          ("long", "bf16", 5), ("long", "bf16", 20), ("long", "f32", 3), ("long_rev", "bf16", 5),
          ("mid", "bf16", 5), ("mid", "wire", 9), ("mid", "f32", 3), ("mid", "bf16", 33)]
 
@@ -122,11 +157,13 @@ def test_bucket_edges_fused_and_reduce(Z, table_kind, kind, N):
     assert np.all(gh[~inside].view(np.uint32) == 0x7FBADBAD)
 
 
-@pytest.mark.parametrize("table_kind", ["short", "long", "mid"])
+@pytest.mark.parametrize("table_kind", ["short", "long", "mid", "many", "wide"])
 def test_bucket_edges_device_commit_tiled(Z, table_kind):
-    """Two device-commit steps over the table in the tiled layout; the second step's
-    replicas carry an inf inside a bucket, so it is skipped."""
-    N = 6
+    """Three device-commit steps over the table in the tiled layout; the second
+    step's replicas carry an inf inside a bucket, so it is skipped. Tables of short
+    buckets (short, many) load each workgroup's first replica batch before the
+    committed-state record; the wide table's grid is past that bound."""
+    N = 2 if table_kind == "wide" else 6
     S, table, rng, reps, inside, buckets, gdt, g = _case(Z, table_kind, "bf16", N)
     say(f"bucket edges device commit tiled {table_kind} S={S}")
     p0 = (rng.standard_normal(S) * 0.02).astype(np.float32)

@@ -57,8 +57,8 @@ def test_unaligned_layouts(Z, seed):
     check_layout(Z, numels, int(rng.integers(2, 12)), 1, seed=seed)
 
 
-@pytest.mark.parametrize("N,count", [(8, 141), (8, 142), (8, 143), (8, 285), (64, 125), (64, 126),
-                                     (64, 127), (200, 70), (200, 71), (200, 72), (200, 143)])
+@pytest.mark.parametrize("N,count", [(8, 142), (8, 143), (8, 144), (8, 287), (64, 126), (64, 127),
+                                     (64, 128), (200, 71), (200, 72), (200, 73), (200, 145)])
 def test_tensor_counts_around_one_launch(Z, N, count):
     """Calls whose tensor counts sit just below, at and just above what one launch's
     argument block holds for their shard count (and twice that), so that the

@@ -14,7 +14,7 @@
 // element by element (still coalesced). The tensor table travels in the kernel
 // argument block, sized to the call's shard count (a table of 8, 64 or 256
 // shard pointers, then as many tensors as the rest of the 4 KB block holds:
-// 142, 126 or 71), so a model's fetch takes few launches, each with its own
+// 143, 127 or 72), so a model's fetch takes few launches, each with its own
 // fill and tail.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -32,17 +32,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // One launch's arguments for calls over at most NSH shards: the header and the
 // shard table, then per tensor its flat offset, length, output and first task
 // (the prefix sum of the task counts, relative to the launch's group; the
-// entries from n_tensors to kTensors all hold the group's total).
+// entries past the group's last tensor, up to kTensors, all hold its total).
 template <int NSH>
 struct GatherArgs {
-    static constexpr int kHead = 8 * NSH + 32;
+    static constexpr int kHead = 8 * NSH + 24;
     static constexpr int kTensors = (kArgBytes - kHead - 4) / 28;
     const void* shard[NSH];
     int64_t S;
     double inv_S;                             // 1 / S, rounded once
     int64_t task_base;                        // task of workgroup 0 of this launch
-    int32_t n_tensors;
-    int32_t reserved;
     int64_t offset[kTensors];
     int64_t numel[kTensors];
     void* out[kTensors];
@@ -136,7 +134,6 @@ static hipError_t gather_groups(const void* const* shards, int32_t n_shards, int
     g.inv_S = 1.0 / (double)S;
     for (int32_t base = 0; base < n_tensors; base += KT) {
         const int32_t k = n_tensors - base < KT ? n_tensors - base : KT;
-        g.n_tensors = k;
         int64_t tasks = 0;
         for (int32_t i = 0; i < k; ++i) {
             g.offset[i] = offsets[base + i];
