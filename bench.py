@@ -508,7 +508,7 @@ def unfused_bench(args, Z, w, S, reps, p0, gdt) -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "note": "S * (2N + 34) bytes over the two kernels' times"},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
         "skipped_steps": skipped,
     }
     print(json.dumps(out), flush=True)
@@ -624,10 +624,33 @@ def main() -> int:
         return gather_bench(args, Z, W, w, S)
 
     tdt = torch.int16 if w.grad_dtype == "bf16" else torch.float32
+    fdt = torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32
+    cpu = None
+    if not (args.no_cpu_baseline or args.overlap or args.offload or args.unfused or args.graph):
+        # The oracle's timing runs first, on the first CPU_SAMPLE_ELEMS elements of
+        # the same inputs (drawn alone, without the whole shard; elements/s does
+        # not depend on the shard length), and only then is the shard allocated.
+        # A process that allocates the Llama-70B shard's ~200 GB within a few
+        # seconds of another process freeing as much streams it about 5% slower
+        # (33.0 against 31.6 ms per step); ten seconds between the two are enough,
+        # and the oracle's timing takes longer than that.
+        n_cpu = min(S, CPU_SAMPLE_ELEMS)
+        log(f"cpu baseline (oracle) on {n_cpu} of {S} elements ...")
+        host_reps = []
+        for j in range(w.N):
+            x = W.device_prefix(W.device_fill_replica, S, n_cpu, fdt, dev, w, covered, args.rank, 0, j)
+            x = x.view(tdt).cpu().numpy()
+            host_reps.append(x.view(np.uint16) if w.grad_dtype == "bf16" else x)
+        p_host = W.device_prefix(W.device_fill_params, S, n_cpu, torch.float32, dev, w, covered,
+                                 args.rank).cpu().numpy()
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(w, host_reps, p_host, n_cpu, args.cpu_seconds, wire)
+        if n_cpu < S:
+            cpu["sample"] += f" (the first {n_cpu} of the shard's {S} elements)"
+        del host_reps, p_host
     reps = []
     for j in range(w.N):
-        buf = torch.empty(S, dtype=torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32,
-                          device=dev)
+        buf = torch.empty(S, dtype=fdt, device=dev)
         W.device_fill_replica(buf, w, covered, args.rank, 0, j)
         reps.append(buf.view(tdt))
     p0 = torch.empty(S, dtype=torch.float32, device=dev)
@@ -744,7 +767,7 @@ def main() -> int:
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_kind": ("L2 fill bytes (FETCH_SIZE, MALL hits included) + written bytes"
                                       if fits_mall else "HBM bytes read + written")},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
         "skipped_steps": skipped,
     }
     if args.calibrate_copy:
@@ -756,19 +779,6 @@ def main() -> int:
         out["calibration_copy_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4,
                                          "launches": 3}
         del src, dst
-    if not args.no_cpu_baseline:
-        # shards above CPU_SAMPLE_ELEMS are sampled: the oracle runs on their first
-        # CPU_SAMPLE_ELEMS elements (elements/s does not depend on the shard length)
-        n_cpu = min(S, CPU_SAMPLE_ELEMS)
-        log(f"cpu baseline (oracle) on {n_cpu} of {S} elements ...")
-        host_reps = []
-        for r in reps:
-            x = r[:n_cpu].cpu()
-            host_reps.append(x.numpy().view(np.uint16) if w.grad_dtype == "bf16" else x.numpy())
-        out["cpu_baseline"] = cpu_baseline(w, host_reps, p0[:n_cpu].cpu().numpy(), n_cpu,
-                                           args.cpu_seconds, wire)
-        if n_cpu < S:
-            out["cpu_baseline"]["sample"] += f" (the first {n_cpu} of the shard's {S} elements)"
     print(json.dumps(out), flush=True)
     return 0
 

@@ -255,6 +255,22 @@ def device_fill_replica(buf, w: Workload, covered, rank: int, step: int, slot: i
     _zero_outside(buf, covered)
 
 
+def device_prefix(fill, S: int, n: int, dtype, device, *args):
+    """The first n elements of what ``fill`` (device_fill_replica or
+    device_fill_params, with ``args`` after the buffer) writes into a buffer of
+    S elements, without allocating S: the fills draw chunk by chunk, so the first
+    min(S, 2^27) elements come from the first chunk's draw alone."""
+    import torch
+    L = min(S, _CHUNK)
+    if not 0 < n <= L:
+        raise ValueError(f"a prefix of {n} elements of a {S}-element fill (at most {L})")
+    buf = torch.empty(L, dtype=dtype, device=device)
+    fill(buf, *args)
+    out = buf[:n].clone()
+    del buf
+    return out
+
+
 def device_fill_params(buf, w: Workload, covered, rank: int) -> None:
     import torch
     S = buf.numel()
