@@ -15,9 +15,10 @@ Elements outside the buckets keep their sentinel.
 
 The short table (11 buckets over 4,003 elements) runs one workgroup per bucket;
 a generated table of about 10,000 buckets of 1-5 elements has more buckets than
-workgroups, and one of about 70,000 buckets of 950 elements a grid above the
+workgroups, one of about 70,000 buckets of 950 elements a grid above the
 65,536 workgroups up to which device-commit launches load their first replica
-batch before the committed-state record.
+batch before the committed-state record, and one of short buckets runs under
+300 replicas, whose pointers the kernel reads from the workspace.
 Tables of a few long buckets are cut into chunks dealt over the grid: the long
 table (and the same table in reverse order), the mid table over 3,000,003
 elements, and a 70,000,003-element shard through the allocation-free entry
@@ -78,10 +79,13 @@ TABLES = {"short": (SHORT_S, SHORT, SHORT_BAD), "long": (LONG_S, LONG, LONG_BAD)
           # about 70,000 buckets of 950 elements over 67,000,003: a grid of 69,526
           # workgroups, past the 65,536 up to which the first replica batch is
           # loaded before the committed-state record
-          "wide": _generated(67_000_003, 72, 2, (950, 951), (0, 3))}
+          "wide": _generated(67_000_003, 72, 2, (950, 951), (0, 3)),
+          # short buckets under 300 replicas: the replica pointers come from the
+          # workspace table instead of the kernel arguments
+          "ptr": _generated(9001, 73, 3, (5, 40), (0, 4))}
 
 CASES = [("short", "bf16", 5), ("short", "f32", 3), ("short", "bf16", 20), ("short", "wire", 9),
-         ("many", "bf16", 5),
+         ("many", "bf16", 5), ("ptr", "bf16", 300),
          ("long", "bf16", 5), ("long", "bf16", 20), ("long", "f32", 3), ("long_rev", "bf16", 5),
          ("mid", "bf16", 5), ("mid", "wire", 9), ("mid", "f32", 3), ("mid", "bf16", 33)]
 
@@ -157,13 +161,13 @@ def test_bucket_edges_fused_and_reduce(Z, table_kind, kind, N):
     assert np.all(gh[~inside].view(np.uint32) == 0x7FBADBAD)
 
 
-@pytest.mark.parametrize("table_kind", ["short", "long", "mid", "many", "wide"])
+@pytest.mark.parametrize("table_kind", ["short", "long", "mid", "many", "wide", "ptr"])
 def test_bucket_edges_device_commit_tiled(Z, table_kind):
     """Three device-commit steps over the table in the tiled layout; the second
     step's replicas carry an inf inside a bucket, so it is skipped. Tables of short
     buckets (short, many) load each workgroup's first replica batch before the
     committed-state record; the wide table's grid is past that bound."""
-    N = 2 if table_kind == "wide" else 6
+    N = {"wide": 2, "ptr": 300}.get(table_kind, 6)
     S, table, rng, reps, inside, buckets, gdt, g = _case(Z, table_kind, "bf16", N)
     say(f"bucket edges device commit tiled {table_kind} S={S}")
     p0 = (rng.standard_normal(S) * 0.02).astype(np.float32)
