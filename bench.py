@@ -508,7 +508,7 @@ def unfused_bench(args, Z, w, S, reps, p0, gdt) -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "note": "S * (2N + 34) bytes over the two kernels' times"},
-        "cpu_baseline": cpu,
+        "cpu_baseline": None,
         "skipped_steps": skipped,
     }
     print(json.dumps(out), flush=True)
