@@ -5,7 +5,8 @@ temporary and compared bit for bit with the oracle's gather_tensor: the GPT-2
 small tensor list (148 tensors, more than one launch), the ragged workload (256-
 element alignment), unaligned layouts (alignment 1, odd sizes) where source and
 destination differ in their 16-byte alignment, a tensor spanning every shard
-with a tiny shard, fp32 elements, and guard bands around the outputs.
+with a tiny shard, fp32 elements, guard bands around the outputs, and a call
+whose outputs exceed the Infinity Cache (stored past the caches).
 """
 import numpy as np
 import pytest
@@ -69,6 +70,16 @@ def test_tensor_counts_around_one_launch(Z, N, count):
     numels[count // 2] = 40_000          # one tensor of several tasks
     say(f"gather N={N} count={count}")
     check_layout(Z, numels, N, 1, seed=N + count)
+
+
+def test_outputs_past_the_cache(Z):
+    """A call whose outputs exceed the 256 MB Infinity Cache stores them with
+    nontemporal stores: large tensors with odd sizes and offsets (pieces whose
+    source and destination differ in their 16-byte alignment) among small ones,
+    every tensor bit-exact against the oracle."""
+    numels = [3, 45_000_001, 7, 50_000_000, 1_001, 44_999_999, 2]
+    say("gather past the cache: 140M elements over 3 shards")
+    check_layout(Z, numels, 3, 1, seed=12)
 
 
 def test_fp32_and_spanning_tensor(Z):

@@ -11,11 +11,12 @@
 // tasks of kGatherChunk output elements, so a launch has about one task per
 // 16 KB of bf16 output whatever the tensor sizes; pieces whose source and
 // destination share their 16-byte alignment move as 16-byte vectors, others
-// element by element (still coalesced). The tensor table travels in the kernel
-// argument block, sized to the call's shard count (a table of 8, 64 or 256
-// shard pointers, then as many tensors as the rest of the 4 KB block holds:
-// 143, 127 or 72), so a model's fetch takes few launches, each with its own
-// fill and tail.
+// element by element (still coalesced); outputs go through the caches when the
+// call's outputs fit in the Infinity Cache and past them otherwise. The tensor
+// table travels in the kernel argument block, sized to the call's shard count
+// (a table of 8, 64 or 256 shard pointers, then as many tensors as the rest of
+// the 4 KB block holds: 143, 127 or 72), so a model's fetch takes few launches,
+// each with its own fill and tail.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,10 +52,17 @@ static_assert(sizeof(GatherArgs<8>) <= kArgBytes && sizeof(GatherArgs<64>) <= kA
               "the gather arguments fit the kernel argument block");
 static_assert(GatherArgs<kGatherMaxShards>::kTensors >= 64, "at least one lane's worth of tensors");
 
+// 16-byte store: nontemporal (NTS, past the caches) or plain (allocating in them).
+template <bool NTS>
+__device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
+    if constexpr (NTS) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 // len elements from src to dst by the whole workgroup. Each lane issues up to
 // four 16-byte loads before its stores, so a full task (16 KB of bf16) is one
 // round of loads in flight per lane.
-template <typename E>
+template <typename E, bool NTS>
 __device__ __forceinline__ void copy_piece(const E* __restrict__ src, E* __restrict__ dst,
                                            int64_t len) {
     constexpr int64_t V = 16 / sizeof(E);
@@ -73,18 +81,18 @@ __device__ __forceinline__ void copy_piece(const E* __restrict__ src, E* __restr
             const u32x4 b = __builtin_nontemporal_load(s4 + k + kBlock);
             const u32x4 c = __builtin_nontemporal_load(s4 + k + 2 * kBlock);
             const u32x4 d = __builtin_nontemporal_load(s4 + k + 3 * kBlock);
-            d4[k] = a;
-            d4[k + kBlock] = b;
-            d4[k + 2 * kBlock] = c;
-            d4[k + 3 * kBlock] = d;
+            st16<NTS>(d4 + k, a);
+            st16<NTS>(d4 + k + kBlock, b);
+            st16<NTS>(d4 + k + 2 * kBlock, c);
+            st16<NTS>(d4 + k + 3 * kBlock, d);
         }
-        for (; k < nv; k += kBlock) d4[k] = __builtin_nontemporal_load(s4 + k);
+        for (; k < nv; k += kBlock) st16<NTS>(d4 + k, __builtin_nontemporal_load(s4 + k));
         done = h + nv * V;
     }
     for (int64_t k = done + threadIdx.x; k < len; k += kBlock) dst[k] = src[k];
 }
 
-template <typename E, int NSH>
+template <typename E, int NSH, bool NTS>
 __global__ void __launch_bounds__(kBlock) k_gather(const GatherArgs<NSH> g) {
     constexpr int KT = GatherArgs<NSH>::kTensors;
     const int64_t task = g.task_base + blockIdx.x;
@@ -118,12 +126,12 @@ __global__ void __launch_bounds__(kBlock) k_gather(const GatherArgs<NSH> g) {
     for (int64_t e = e0; e < e1; ++r, off = 0) {
         const int64_t rest = g.S - off;
         const int64_t len = e1 - e < rest ? e1 - e : rest;
-        copy_piece<E>(static_cast<const E*>(g.shard[r]) + off, out + e, len);
+        copy_piece<E, NTS>(static_cast<const E*>(g.shard[r]) + off, out + e, len);
         e += len;
     }
 }
 
-template <int NSH>
+template <int NSH, bool NTS>
 static hipError_t gather_groups(const void* const* shards, int32_t n_shards, int64_t S,
                                 int32_t elem_bytes, const int64_t* offsets, const int64_t* numels,
                                 void* const* outs, int32_t n_tensors, hipStream_t st) {
@@ -151,9 +159,9 @@ static hipError_t gather_groups(const void* const* shards, int32_t n_shards, int
             const int64_t n = tasks - t0 < kGatherMaxTasks ? tasks - t0 : kGatherMaxTasks;
             g.task_base = t0;
             if (elem_bytes == 2)
-                hipLaunchKernelGGL((k_gather<uint16_t, NSH>), dim3((unsigned)n), dim3(kBlock), 0, st, g);
+                hipLaunchKernelGGL((k_gather<uint16_t, NSH, NTS>), dim3((unsigned)n), dim3(kBlock), 0, st, g);
             else
-                hipLaunchKernelGGL((k_gather<uint32_t, NSH>), dim3((unsigned)n), dim3(kBlock), 0, st, g);
+                hipLaunchKernelGGL((k_gather<uint32_t, NSH, NTS>), dim3((unsigned)n), dim3(kBlock), 0, st, g);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -161,15 +169,34 @@ static hipError_t gather_groups(const void* const* shards, int32_t n_shards, int
     return hipSuccess;
 }
 
+template <bool NTS>
+static hipError_t gather_by_shards(const void* const* shards, int32_t n_shards, int64_t S,
+                                   int32_t elem_bytes, const int64_t* offsets, const int64_t* numels,
+                                   void* const* outs, int32_t n_tensors, hipStream_t st) {
+    if (n_shards <= 8)
+        return gather_groups<8, NTS>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
+    if (n_shards <= 64)
+        return gather_groups<64, NTS>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
+    return gather_groups<kGatherMaxShards, NTS>(shards, n_shards, S, elem_bytes, offsets, numels, outs,
+                                                n_tensors, st);
+}
+
+// A call whose outputs fit in the 256 MB Infinity Cache stores them through the
+// caches, where the layer that reads them right after finds them; a larger one
+// could not keep them there and streams them past the caches, which leaves the
+// cache to the other traffic (Llama-7B layer 139 -> 127 us, model 4.72 -> 4.56
+// ms; a GPT-2 layer or model keeps the cached stores).
+constexpr int64_t kCachedOutBytes = int64_t(256) << 20;
+
 hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S, int32_t elem_bytes,
                          const int64_t* offsets, const int64_t* numels, void* const* outs,
                          int32_t n_tensors, hipStream_t st) {
-    if (n_shards <= 8)
-        return gather_groups<8>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
-    if (n_shards <= 64)
-        return gather_groups<64>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
-    return gather_groups<kGatherMaxShards>(shards, n_shards, S, elem_bytes, offsets, numels, outs,
-                                           n_tensors, st);
+    int64_t out_bytes = 0;
+    for (int32_t k = 0; k < n_tensors && out_bytes <= kCachedOutBytes; ++k)
+        out_bytes += numels[k] * elem_bytes;
+    if (out_bytes > kCachedOutBytes)
+        return gather_by_shards<true>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
+    return gather_by_shards<false>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
 }
 
 }  // namespace zk
