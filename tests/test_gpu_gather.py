@@ -72,14 +72,16 @@ def test_tensor_counts_around_one_launch(Z, N, count):
     check_layout(Z, numels, N, 1, seed=N + count)
 
 
-def test_outputs_past_the_cache(Z):
+@pytest.mark.parametrize("dtype,N", [(np.uint16, 3), (np.float32, 16), (np.uint16, 100)])
+def test_outputs_past_the_cache(Z, dtype, N):
     """A call whose outputs exceed the 256 MB Infinity Cache stores them with
     nontemporal stores: large tensors with odd sizes and offsets (pieces whose
     source and destination differ in their 16-byte alignment) among small ones,
-    every tensor bit-exact against the oracle."""
+    2- and 4-byte elements, 8-, 64- and 256-entry shard tables; every tensor
+    bit-exact against the oracle."""
     numels = [3, 45_000_001, 7, 50_000_000, 1_001, 44_999_999, 2]
-    say("gather past the cache: 140M elements over 3 shards")
-    check_layout(Z, numels, 3, 1, seed=12)
+    say(f"gather past the cache: 140M elements over {N} shards ({np.dtype(dtype).name})")
+    check_layout(Z, numels, N, 1, dtype=dtype, seed=12 + N)
 
 
 def test_fp32_and_spanning_tensor(Z):
