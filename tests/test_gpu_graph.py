@@ -115,3 +115,61 @@ def test_graph_of_two_steps_replayed_back_to_back(Z, tiled):
     for a, b in zip(sg.committed(), se.committed()):
         assert torch.equal(a, b)
     assert torch.equal(sg.current_slot(), se.current_slot())
+
+
+@pytest.mark.parametrize("bucket_len", [1000, 70_000])
+def test_graph_over_a_bucket_table(Z, bucket_len):
+    """Steps over a bucket table under graph capture: short buckets (one workgroup
+    each, the first replica batch loaded before the record) and long ones (cut
+    into chunks). A graph of two steps replayed three times, an injected +inf
+    inside a bucket on the second replay, against eager steps over the same
+    table; the committed state must be equal everywhere (outside the buckets both
+    keep the initial values)."""
+    S, N = 300_007, 4
+    rng = np.random.default_rng(43)
+    reps_h = [np.asarray(W._bf16_bits_from_f32(rng.standard_normal(S) * 1e-3 * 64.0))
+              for _ in range(N)]
+    p0 = to_dev((rng.standard_normal(S) * 0.02).astype(np.float32))
+    offs = np.arange(3, S - bucket_len, bucket_len + 5, dtype=np.int64)
+    raw = np.zeros(len(offs), dtype=np.dtype([("off", "<i8"), ("len", "<i4"), ("t", "<i4")]))
+    raw["off"] = offs
+    raw["len"] = bucket_len
+    buckets = torch.from_numpy(raw.view(np.uint8).copy()).to("cuda")
+    hy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, loss_scale=64.0,
+              dynamic=True, state_layout=Z.ZERO_STATE_TILED, double_slot=True, buckets=buckets,
+              n_buckets=len(offs))
+    reps_g = [to_dev(r) for r in reps_h]
+    reps_e = [to_dev(r) for r in reps_h]
+    sg = Z.DeviceShardStep(S, N, Z.ZERO_BF16, p0, **hy)
+    se = Z.DeviceShardStep(S, N, Z.ZERO_BF16, p0, **hy)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        sg._args_for(reps_g)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            sg.step(reps_g)
+            sg.step(reps_g)
+    torch.cuda.synchronize()
+    inside = int(offs[len(offs) // 2]) + 7
+    good = int(reps_h[2][inside].view(np.int16))
+    for r in range(3):
+        say(f"graph over buckets of {bucket_len}: replay {r}")
+        if r == 1:
+            reps_g[2][inside] = 0x7F80
+            reps_e[2][inside] = 0x7F80
+        graph.replay()
+        se.step(reps_e)
+        se.step(reps_e)
+        torch.cuda.synchronize()
+        if r == 1:
+            reps_g[2][inside] = good
+            reps_e[2][inside] = good
+    rg, re = sg.state(), se.state()
+    assert (rg.t, rg.n_skipped, rg.seq, rg.loss_scale) == (re.t, re.n_skipped, re.seq, re.loss_scale)
+    assert (rg.t, rg.n_skipped) == (4, 2)
+    for a, b in zip(sg.committed(), se.committed()):
+        assert torch.equal(a, b)
+    assert torch.equal(sg.current_slot(), se.current_slot())
