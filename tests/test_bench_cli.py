@@ -1,6 +1,6 @@
 """bench.py's command line on a machine without a GPU: more than one GPU is refused
-with a message before anything touches a device, and the help text lists the
-measurement modes."""
+with a message before anything touches a device, the help text lists the
+measurement modes, and the committed byte counters belong to the current kernel."""
 import os
 import subprocess
 import sys
@@ -40,3 +40,18 @@ def test_graph_mode_needs_the_device_commit():
     r = run("--graph", "4", "--commit", "host")
     assert r.returncode == 2
     assert "--graph" in r.stderr
+
+
+def test_committed_counters_match_the_kernel():
+    """The byte counters in profiles/traffic.json were taken on the step kernel as
+    it is now (their code hash matches), for every workload's default launch, so
+    the bench line carries measured traffic; each profile summary names the same
+    hash."""
+    sys.path.insert(0, ROOT)
+    import bench
+    h = bench.kernel_source_hash()
+    for name in ("llama70b", "llama7b", "gpt2s", "ragged"):
+        t = bench.measured_traffic(name, "tiled")
+        assert t is not None, f"{name}: counters taken on another kernel (hash {h})"
+        with open(os.path.join(ROOT, "profiles", f"fused_step_{name}.md")) as f:
+            assert h in f.read(), name
