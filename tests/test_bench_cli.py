@@ -55,3 +55,18 @@ def test_committed_counters_match_the_kernel():
         assert t is not None, f"{name}: counters taken on another kernel (hash {h})"
         with open(os.path.join(ROOT, "profiles", f"fused_step_{name}.md")) as f:
             assert h in f.read(), name
+
+
+def test_fetch_profile_matches_the_kernel():
+    """profiles/gather_gpt2s.md was taken on the stage-3 fetch kernel as it is now:
+    it names the sha256[:16] of gather_kernels.hip with comments and whitespace
+    removed."""
+    import hashlib
+    import re
+    with open(os.path.join(ROOT, "zero_partitioned_optimizer_amd", "csrc", "gather_kernels.hip")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    h = hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+    with open(os.path.join(ROOT, "profiles", "gather_gpt2s.md")) as f:
+        assert h in f.read()
