@@ -1,7 +1,8 @@
 """zero_adam_step_noalloc -- the step with the library's own scratch, for callers
 that cannot allocate -- against zero_adam_step with a caller workspace, on the
-same inputs, through the C ABI: p, m, v and the slot bit for bit, the overflow
-flag exactly, the squared norm within 1e-9 relative (its partials are grouped by
+same inputs, through the C ABI: p, m, v and the slot bit for bit (outputs
+filled with sentinels first; a bucket launch must leave those outside its
+buckets), the overflow flag exactly, the squared norm within 1e-9 relative (its partials are grouped by
 another grid). Three calls in a row on one stream, each on a smaller input than
 the one before, so the second and third find the scratch holding what the call
 before wrote:
@@ -33,14 +34,22 @@ def bf16_replicas(gen, S, N, scale):
     return out
 
 
-def run_pair(Z, name, reps, S, p, m, v, *, loss_scale, t, wd, buckets=None, n_buckets=0):
+SENT32, SENT16 = 0x7FBADBAD, 0x5A5A
+
+
+def run_pair(Z, name, reps, S, p, m, v, *, loss_scale, t, wd, buckets=None, n_buckets=0,
+             inside=None):
     """One zero_adam_step (with a workspace) and one zero_adam_step_noalloc on the
-    same inputs into separate outputs; compare."""
+    same inputs into separate outputs, both filled with the same sentinels first
+    (a bucket launch writes only the elements inside its buckets); compare, and
+    check that the elements outside the buckets (``inside``: a boolean device
+    mask, or None for the whole shard) kept their sentinels."""
     hy = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wd)
     outs = {}
     for mode in ("workspace", "noalloc"):
-        P, M, V = (torch.empty(S, dtype=torch.float32, device="cuda") for _ in range(3))
-        slot = torch.empty(S, dtype=torch.int16, device="cuda")
+        P, M, V = (torch.full((S,), SENT32, dtype=torch.int32, device="cuda").view(torch.float32)
+                   for _ in range(3))
+        slot = torch.full((S,), SENT16, dtype=torch.int16, device="cuda")
         stats = torch.zeros(16, dtype=torch.uint8, device="cuda")
         ws = (torch.empty(Z.zero_workspace_bytes(S), dtype=torch.uint8, device="cuda")
               if mode == "workspace" else None)
@@ -58,6 +67,9 @@ def run_pair(Z, name, reps, S, p, m, v, *, loss_scale, t, wd, buckets=None, n_bu
         xb = x.view(torch.int32) if x.dtype == torch.float32 else x
         yb = y.view(torch.int32) if y.dtype == torch.float32 else y
         assert torch.equal(xb, yb), f"{name}: {what} differs between the two entry points"
+        if inside is not None:
+            sent = SENT32 if x.dtype == torch.float32 else SENT16
+            assert bool(torch.all(xb[~inside] == sent)), f"{name}: {what} written outside the buckets"
     assert st1.overflow == st0.overflow and st1.bad_buckets == st0.bad_buckets == 0
     assert sumsq_close(st1.sumsq, st0.sumsq, 1e-9), (st1.sumsq, st0.sumsq)
     return st0
@@ -94,8 +106,12 @@ def test_noalloc_equals_workspace_entry_point(Z):
     reps[5][off + ln // 2] = 0x7F80                         # +inf in bf16, inside a bucket
     p = torch.randn(S, generator=gen, device="cuda").mul_(0.02)
     z = torch.zeros(S, dtype=torch.float32, device="cuda")
+    inside = torch.zeros(S, dtype=torch.bool)
+    for o, ln in np.frombuffer(bytes(raw)[: 16 * nb], dtype=np.dtype(
+            [("off", "<i8"), ("len", "<i4"), ("t", "<i4")]))[["off", "len"]].tolist():
+        inside[o:o + ln] = True
     st = run_pair(Z, "ragged buckets", reps, S, p, z, z, loss_scale=65536.0, t=1, wd=0.0,
-                  buckets=bt, n_buckets=nb)
+                  buckets=bt, n_buckets=nb, inside=inside.to("cuda"))
     assert st.overflow == 1
     # 3: 300 replicas, the pointer table in the scratch
     S = 5003
