@@ -8,8 +8,9 @@
 // resident buffers (in a multi-GPU build: the peers' shards mapped over xGMI).
 //
 // Pure copy, HBM-bound (2 x element bytes per element): workgroups take fixed
-// tasks of kGatherChunk output elements, so a launch has about one task per
-// 16 KB of bf16 output whatever the tensor sizes; pieces whose source and
+// tasks of kGatherChunk output elements (kSmallChunk in calls too small to fill
+// the chip), so a launch has about one task per 16 KB of bf16 output whatever
+// the tensor sizes; pieces whose source and
 // destination share their 16-byte alignment move as 16-byte vectors, others
 // element by element (still coalesced); outputs go through the caches when the
 // call's outputs fit in the Infinity Cache and past them otherwise. The tensor
@@ -25,6 +26,9 @@
 namespace zk {
 
 constexpr int64_t kGatherChunk = 8192;                  // output elements per task
+constexpr int64_t kSmallChunk = 4096;                   // ... in calls too small to fill the chip
+constexpr int64_t kSmallCallTasks = 2048;               // tasks of kGatherChunk below which a
+                                                        // call takes tasks of kSmallChunk
 constexpr int64_t kGatherMaxTasks = int64_t(1) << 20;   // workgroups per gather launch
 constexpr int kArgBytes = 4096;                         // the kernel argument block
 
@@ -92,7 +96,7 @@ __device__ __forceinline__ void copy_piece(const E* __restrict__ src, E* __restr
     for (int64_t k = done + threadIdx.x; k < len; k += kBlock) dst[k] = src[k];
 }
 
-template <typename E, int NSH, bool NTS>
+template <typename E, int NSH, bool NTS, int64_t CHUNK>
 __global__ void __launch_bounds__(kBlock) k_gather(const GatherArgs<NSH> g) {
     constexpr int KT = GatherArgs<NSH>::kTensors;
     const int64_t task = g.task_base + blockIdx.x;
@@ -113,8 +117,8 @@ __global__ void __launch_bounds__(kBlock) k_gather(const GatherArgs<NSH> g) {
 #pragma unroll
     for (int i = 0; i < (KT + 63) / 64; ++i) t += __popcll(__ballot((int64_t)ft[i] <= task));
     const int64_t n = g.numel[t];
-    const int64_t e0 = (task - g.first_task[t]) * kGatherChunk;
-    const int64_t e1 = e0 + kGatherChunk < n ? e0 + kGatherChunk : n;
+    const int64_t e0 = (task - g.first_task[t]) * CHUNK;
+    const int64_t e1 = e0 + CHUNK < n ? e0 + CHUNK : n;
     E* out = static_cast<E*>(g.out[t]);
     const int64_t f = g.offset[t] + e0;
     // rank r = floor(f / S) from the reciprocal (within one of it for any f below
@@ -131,7 +135,7 @@ __global__ void __launch_bounds__(kBlock) k_gather(const GatherArgs<NSH> g) {
     }
 }
 
-template <int NSH, bool NTS>
+template <int NSH, bool NTS, int64_t CHUNK>
 static hipError_t gather_groups(const void* const* shards, int32_t n_shards, int64_t S,
                                 int32_t elem_bytes, const int64_t* offsets, const int64_t* numels,
                                 void* const* outs, int32_t n_tensors, hipStream_t st) {
@@ -148,7 +152,7 @@ static hipError_t gather_groups(const void* const* shards, int32_t n_shards, int
             g.numel[i] = numels[base + i];
             g.out[i] = outs[base + i];
             g.first_task[i] = (int32_t)tasks;
-            tasks += (g.numel[i] + kGatherChunk - 1) / kGatherChunk;
+            tasks += (g.numel[i] + CHUNK - 1) / CHUNK;
             // a group's tasks are counted in 32 bits (2^31 tasks: 16T elements)
             if (tasks > INT32_MAX) return hipErrorInvalidValue;
         }
@@ -159,9 +163,11 @@ static hipError_t gather_groups(const void* const* shards, int32_t n_shards, int
             const int64_t n = tasks - t0 < kGatherMaxTasks ? tasks - t0 : kGatherMaxTasks;
             g.task_base = t0;
             if (elem_bytes == 2)
-                hipLaunchKernelGGL((k_gather<uint16_t, NSH, NTS>), dim3((unsigned)n), dim3(kBlock), 0, st, g);
+                hipLaunchKernelGGL((k_gather<uint16_t, NSH, NTS, CHUNK>), dim3((unsigned)n), dim3(kBlock), 0,
+                                   st, g);
             else
-                hipLaunchKernelGGL((k_gather<uint32_t, NSH, NTS>), dim3((unsigned)n), dim3(kBlock), 0, st, g);
+                hipLaunchKernelGGL((k_gather<uint32_t, NSH, NTS, CHUNK>), dim3((unsigned)n), dim3(kBlock), 0,
+                                   st, g);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -169,16 +175,18 @@ static hipError_t gather_groups(const void* const* shards, int32_t n_shards, int
     return hipSuccess;
 }
 
-template <bool NTS>
+template <bool NTS, int64_t CHUNK>
 static hipError_t gather_by_shards(const void* const* shards, int32_t n_shards, int64_t S,
                                    int32_t elem_bytes, const int64_t* offsets, const int64_t* numels,
                                    void* const* outs, int32_t n_tensors, hipStream_t st) {
     if (n_shards <= 8)
-        return gather_groups<8, NTS>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
+        return gather_groups<8, NTS, CHUNK>(shards, n_shards, S, elem_bytes, offsets, numels, outs,
+                                            n_tensors, st);
     if (n_shards <= 64)
-        return gather_groups<64, NTS>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
-    return gather_groups<kGatherMaxShards, NTS>(shards, n_shards, S, elem_bytes, offsets, numels, outs,
-                                                n_tensors, st);
+        return gather_groups<64, NTS, CHUNK>(shards, n_shards, S, elem_bytes, offsets, numels, outs,
+                                             n_tensors, st);
+    return gather_groups<kGatherMaxShards, NTS, CHUNK>(shards, n_shards, S, elem_bytes, offsets, numels,
+                                                       outs, n_tensors, st);
 }
 
 // A call whose outputs fit in the 256 MB Infinity Cache stores them through the
@@ -188,15 +196,27 @@ static hipError_t gather_by_shards(const void* const* shards, int32_t n_shards, 
 // ms; a GPT-2 layer or model keeps the cached stores).
 constexpr int64_t kCachedOutBytes = int64_t(256) << 20;
 
+// A call of fewer than kSmallCallTasks tasks (a layer of a small model: GPT-2
+// small's 865) leaves most of the 256 compute units' slots empty; tasks of half
+// the size double its workgroups (GPT-2 layers in turn 8.6 -> 8.1 us). Larger
+// calls keep the full tasks, with which they run faster (GPT-2 model 78 against
+// 82 us with half tasks, Llama-7B layer 127 against 129 us).
 hipError_t launch_gather(const void* const* shards, int32_t n_shards, int64_t S, int32_t elem_bytes,
                          const int64_t* offsets, const int64_t* numels, void* const* outs,
                          int32_t n_tensors, hipStream_t st) {
-    int64_t out_bytes = 0;
-    for (int32_t k = 0; k < n_tensors && out_bytes <= kCachedOutBytes; ++k)
+    int64_t out_bytes = 0, tasks = 0;
+    for (int32_t k = 0; k < n_tensors && out_bytes <= kCachedOutBytes; ++k) {
         out_bytes += numels[k] * elem_bytes;
+        tasks += (numels[k] + kGatherChunk - 1) / kGatherChunk;
+    }
     if (out_bytes > kCachedOutBytes)
-        return gather_by_shards<true>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
-    return gather_by_shards<false>(shards, n_shards, S, elem_bytes, offsets, numels, outs, n_tensors, st);
+        return gather_by_shards<true, kGatherChunk>(shards, n_shards, S, elem_bytes, offsets, numels, outs,
+                                                    n_tensors, st);
+    if (tasks < kSmallCallTasks)
+        return gather_by_shards<false, kSmallChunk>(shards, n_shards, S, elem_bytes, offsets, numels, outs,
+                                                    n_tensors, st);
+    return gather_by_shards<false, kGatherChunk>(shards, n_shards, S, elem_bytes, offsets, numels, outs,
+                                                 n_tensors, st);
 }
 
 }  // namespace zk
